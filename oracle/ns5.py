@@ -1,0 +1,75 @@
+"""Quintic Newton-Schulz orthogonalization, five iterations (test infrastructure only).
+
+Follows "Muon under AutoTP orthogonalizes each shard, so the update depends on
+the TP degree", section "Why it happens": the input is divided by its matrix
+(Frobenius) norm and the iteration then works on the Gram matrix X X^T.  The
+iteration itself is the one whose two symmetric products are named in
+"core.optimizer.layer_sharded_muon", LayerShardedMuon, parameter use_syrk:
+A = X X^T and B = b A + c A^2, after which X <- a X + B X.  The coefficients
+(a, b, c) = (3.4445, -4.7750, 2.0315) are the quintic ones of the workload
+definition and are used unchanged in all five iterations.
+
+Readings where the pages are silent:
+* eps is added to the norm: X0 = G / (||G||_F + eps).
+* A matrix with more rows than columns is transposed first and transposed back
+  at the end, so the Gram matrix is min(rows, cols) square.  p(X X^T) X equals
+  X p(X^T X), so this only changes rounding.
+"""
+import numpy as np
+
+QUINTIC = (3.4445, -4.7750, 2.0315)
+
+
+def frobenius_normalize(g, eps=1e-7):
+    g = np.array(g, dtype=np.float64, copy=True, order="C")
+    return g / (np.sqrt(np.sum(g * g)) + eps)
+
+
+def newton_schulz5(g, steps=5, coeffs=QUINTIC, eps=1e-7):
+    """Orthogonalize one matrix.  float64 in, float64 out, same shape."""
+    g = np.asarray(g, dtype=np.float64)
+    if g.ndim != 2:
+        raise ValueError("newton_schulz5 takes one 2-D matrix")
+    a, b, c = (float(t) for t in coeffs)
+    x = frobenius_normalize(g, eps)
+    tall = x.shape[0] > x.shape[1]
+    if tall:
+        x = np.ascontiguousarray(x.T)
+    for _ in range(int(steps)):
+        gram = x @ x.T                       # A = X X^T
+        poly = b * gram + c * (gram @ gram)  # B = b A + c A^2
+        x = a * x + poly @ x                 # X <- a X + B X
+    if tall:
+        x = x.T
+    return np.ascontiguousarray(x)
+
+
+def ns5_megabatch(stack, **kw):
+    """A megabatch [N, out, F] is N independent problems: one call per slice.
+
+    "Fix convolution flattening in megabatches and NorMuon normalization",
+    "Problem and fix": the megabatch axis is kept, never folded into columns.
+    """
+    stack = np.asarray(stack, dtype=np.float64)
+    if stack.ndim != 3:
+        raise ValueError("megabatch must be [N, out, F]")
+    return np.stack([newton_schulz5(np.array(s, copy=True, order="C"), **kw)
+                     for s in stack]) if len(stack) else np.zeros_like(stack)
+
+
+def ns5_per_head(p, heads, **kw):
+    """Per-head Newton-Schulz: row block h = rows [h*out/H, (h+1)*out/H).
+
+    "Muon under AutoTP orthogonalizes each shard...", "What could be done",
+    option 3: per-head NS batches over the head (row-block) axis.
+    """
+    p = np.asarray(p, dtype=np.float64)
+    out = p.shape[0]
+    if heads < 1 or out % heads:
+        raise ValueError("rows must divide evenly into heads")
+    hb = out // heads
+    res = np.empty_like(p)
+    for h in range(heads):
+        res[h * hb:(h + 1) * hb] = newton_schulz5(
+            np.array(p[h * hb:(h + 1) * hb], copy=True, order="C"), **kw)
+    return res

@@ -1,0 +1,129 @@
+"""Seeded synthetic input generators.
+
+Every draw comes from ``numpy.random.Generator(PCG64(SeedSequence(key)))`` with
+``key = (workload, layer, matrix, step, role)``, is made in float64 and is then
+rounded to the storage dtype the workload names.  Rounding to bfloat16 goes
+float64 -> float32 (round to nearest even) -> bfloat16 (round to nearest even);
+both sides receive the exact stored bits, so neither side depends on that choice.
+
+Roles (the last component of the key):
+
+=====  =====================================================
+0      gradient, i.i.d. N(0, 1)
+1      initial master weight, N(0, 0.02^2)
+2      Haar factor U of a power-law gradient
+3      Haar factor V of a power-law gradient
+4      noise term of a power-law gradient
+=====  =====================================================
+
+Power-law gradients follow the workload description of one Llama-3-8B-shaped
+layer: ``G = U diag(s) V^T + 0.1 N(0,1)`` with Haar-random U (r x k) and V (c x k),
+``k = min(r, c)`` and ``s_i = i^-0.7``.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "ROLE_GRAD", "ROLE_WEIGHT", "ROLE_U", "ROLE_V", "ROLE_NOISE",
+    "generator", "f64_to_bf16_bits", "bf16_bits_to_f64", "bf16_bits_to_f32",
+    "store", "gaussian", "haar", "power_law",
+    "LLAMA3_8B_LAYER", "conv_megabatches",
+]
+
+ROLE_GRAD, ROLE_WEIGHT, ROLE_U, ROLE_V, ROLE_NOISE = 0, 1, 2, 3, 4
+
+# One Llama-3-8B decoder layer's projection shapes, [out, in].
+LLAMA3_8B_LAYER = (
+    ("q", (4096, 4096)),
+    ("k", (1024, 4096)),
+    ("v", (1024, 4096)),
+    ("o", (4096, 4096)),
+    ("gate", (14336, 4096)),
+    ("up", (14336, 4096)),
+    ("down", (4096, 14336)),
+)
+
+
+def conv_megabatches():
+    """The convolution megabatch workload: (name, N, param shape)."""
+    return (("conv2d", 64, (256, 128, 3, 3)), ("conv1d", 32, (512, 512, 5)))
+
+
+def generator(*key: int) -> np.random.Generator:
+    """A PCG64 generator seeded by the integer key tuple."""
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(k) for k in key])))
+
+
+def f64_to_bf16_bits(x) -> np.ndarray:
+    """Round float64 values to bfloat16 (via float32, both steps nearest-even).
+
+    Returns the raw 16-bit patterns as uint16.
+    """
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    nan = np.isnan(f)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    if nan.any():
+        r = np.where(nan, np.uint16(0x7FC0), r)
+    return r
+
+
+def bf16_bits_to_f32(bits) -> np.ndarray:
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float64."""
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def store(x64: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float64 draws to the storage dtype.
+
+    ``"f32"`` returns a float32 array; ``"bf16"`` returns uint16 bit patterns.
+    """
+    if dtype == "f32":
+        return np.asarray(x64, dtype=np.float64).astype(np.float32)
+    if dtype == "bf16":
+        return f64_to_bf16_bits(x64)
+    raise ValueError(f"unknown storage dtype {dtype!r}")
+
+
+def gaussian(shape, key, dtype: str = "f32", std: float = 1.0) -> np.ndarray:
+    """``std * N(0,1)`` draws of the given shape, rounded to ``dtype``."""
+    g = generator(*key)
+    return store(std * g.standard_normal(size=tuple(shape)), dtype)
+
+
+def haar(n: int, k: int, key) -> np.ndarray:
+    """An n x k matrix with orthonormal columns, Haar distributed (float64).
+
+    Q factor of a Gaussian matrix with the signs of diag(R) moved into Q.
+    """
+    g = generator(*key)
+    z = g.standard_normal(size=(n, k))
+    q, r = np.linalg.qr(z, mode="reduced")
+    d = np.sign(np.diag(r))
+    d[d == 0] = 1.0
+    return q * d[None, :]
+
+
+def power_law(shape, key_uv, key_noise, dtype: str = "bf16", alpha: float = 0.7,
+              noise: float = 0.1) -> np.ndarray:
+    """``U diag(i^-alpha) V^T + noise * N(0,1)`` rounded to ``dtype``.
+
+    ``key_uv`` seeds U (role 2) and V (role 3); ``key_noise`` seeds the noise.
+    Keys are tuples without the role component.
+    """
+    r, c = int(shape[0]), int(shape[1])
+    k = min(r, c)
+    u = haar(r, k, tuple(key_uv) + (ROLE_U,))
+    v = haar(c, k, tuple(key_uv) + (ROLE_V,))
+    s = np.arange(1, k + 1, dtype=np.float64) ** (-alpha)
+    gnoise = generator(*(tuple(key_noise) + (ROLE_NOISE,)))
+    g = (u * s[None, :]) @ v.T
+    g += noise * gnoise.standard_normal(size=(r, c))
+    return store(g, dtype)
