@@ -1,0 +1,260 @@
+"""Benchmark: one Muon / NorMuon optimizer step over one Llama-3-8B-shaped layer
+on one MI355X, through the C ABI (muon_step_group per shape group).
+
+A step is the whole hot path for the layer's seven matrices: Nesterov
+momentum, Frobenius normalization, five quintic Newton-Schulz iterations
+(bf16 MFMA, fp32 accumulation), NorMuon and the spectrally scaled fp32 weight
+update with its bf16 model copy.  Groups: {q, o} 4096x4096, {k, v} 1024x4096,
+{gate, up} 14336x4096, {down} 4096x14336.  Gradients are the seeded power-law
+matrices of the workload definition (U diag(i^-0.7) V^T + 0.1 N(0,1)), bf16;
+master weights fp32 N(0, 0.02^2); momentum bf16; all resident in HBM before
+timing starts.
+
+Prints one JSON line.  `value` is Newton-Schulz orthogonalizations per second
+(7 per step).  `roofline` covers the dominant kernel (the X <- a X + B X
+update GEMM) from HIP events recorded around each of its launches inside the
+timed region; `cpu_baseline` times the float64 oracle on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+METRIC = "NS5 orthogonalizations/sec + TFLOP/s (% bf16 MFMA peak) at Llama-8B shapes"
+LAYER = (("q", (4096, 4096)), ("k", (1024, 4096)), ("v", (1024, 4096)), ("o", (4096, 4096)),
+         ("gate", (14336, 4096)), ("up", (14336, 4096)), ("down", (4096, 14336)))
+WORKLOAD_ID = 2
+
+
+def ns_flops(rows, cols, steps=5):
+    """(L, E) FLOPs of `steps` iterations: L = 4 m^2 n + m^3, E = 3 m^2 n + m^3 per iteration."""
+    m, n = min(rows, cols), max(rows, cols)
+    return steps * (4 * m * m * n + m ** 3), steps * (3 * m * m * n + m ** 3)
+
+
+def make_layer_inputs():
+    """Seeded inputs of the layer.  U, V and s of the power-law gradients are
+    drawn once per shape (key: workload, layer, index of the first matrix of
+    that shape); each matrix has its own noise (key: workload, layer, index,
+    step 1)."""
+    import synth
+    grads, weights = {}, {}
+    index = {name: i for i, (name, _) in enumerate(LAYER)}
+    for shape, names in groups_of_layer():
+        t = time.perf_counter()
+        first = index[names[0]]
+        gs = synth.power_law_many(shape, (WORKLOAD_ID, 0, first),
+                                  [(WORKLOAD_ID, 0, index[n], 1) for n in names], "bf16")
+        for n, g in zip(names, gs):
+            grads[n] = g
+            weights[n] = synth.gaussian(shape, (WORKLOAD_ID, 0, index[n], 0, synth.ROLE_WEIGHT), "f32", std=0.02)
+        print(f"[bench] generated {'+'.join(names)} {shape} in {time.perf_counter() - t:.1f} s",
+              file=sys.stderr, flush=True)
+    return grads, weights
+
+
+def groups_of_layer():
+    order = []
+    by_shape = {}
+    for name, shape in LAYER:
+        if shape not in by_shape:
+            by_shape[shape] = []
+            order.append(shape)
+        by_shape[shape].append(name)
+    return [(shape, by_shape[shape]) for shape in order]
+
+
+def cpu_baseline(grads, weights, target_seconds=20.0):
+    """The oracle as it stands, on q, k and v of the layer (3 of 7 matrices),
+    scaled by dense float64 NS FLOPs to the whole layer."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    hp = oracle.MuonHParams(lr=0.05, normuon=True, mom_dtype="bf16")
+
+    def dense(rows, cols):
+        m, n = min(rows, cols), max(rows, cols)
+        return 5 * (4 * m * m * n + 2 * m ** 3)
+
+    sample = ["k", "v", "q"]
+    t0 = time.perf_counter()
+    done = []
+    for name in sample:
+        shape = dict(LAYER)[name]
+        oracle.muon_step(weights[name].astype(np.float64), synth.bf16_bits_to_f64(grads[name]),
+                         np.zeros(shape), np.zeros(shape[0]), hp)
+        done.append(name)
+        if time.perf_counter() - t0 > target_seconds:
+            break
+    dt = time.perf_counter() - t0
+    f_sample = sum(dense(*dict(LAYER)[n]) for n in done)
+    f_layer = sum(dense(*s) for _, s in LAYER)
+    layer_seconds = dt * f_layer / f_sample
+    return {"value": round(len(LAYER) / layer_seconds, 6), "unit": "orth/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"float64 numpy oracle, one Muon/NorMuon step of {'+'.join(done)} "
+                      f"({dt:.1f} s), scaled by dense NS FLOPs ({f_sample:.3e} of {f_layer:.3e}) to the 7-matrix layer"}
+
+
+def traffic_for(kernel_name):
+    """HBM bytes per launch from the committed counter summary, when it is current."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        info = json.load(open(path))
+        src = os.path.join(ROOT, "newton_schulz_ns5_amd", "csrc", "gemm_bf16.hip")
+        import hashlib
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        rec = info.get(kernel_name)
+        if rec and rec.get("source_sha256") == digest:
+            return rec.get("bytes_per_launch")
+    except Exception:
+        return None
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the multi-GPU path is not part of this build", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    import newton_schulz_ns5_amd as ns
+    ns.lib()  # fail loudly if the library is missing
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+
+    t_gen = time.perf_counter()
+    grads, weights = make_layer_inputs()
+    print(f"[bench] inputs generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    groups = []
+    for shape, names in groups_of_layer():
+        G = [torch.from_numpy(grads[n].view(np.int16)).view(torch.bfloat16).to(dev) for n in names]
+        W = [torch.from_numpy(weights[n]).to(dev) for n in names]
+        M = [torch.zeros(shape, dtype=torch.bfloat16, device=dev) for _ in names]
+        V = [torch.zeros(shape[0], dtype=torch.float32, device=dev) for _ in names]
+        WM = [w.to(torch.bfloat16) for w in W]
+        hp = ns.hparams(lr=0.05, momentum=0.95, nesterov=True, normuon=True, beta2=0.95, norm_eps=1e-8,
+                        ns=ns.ns_config(compute_dtype="bf16"))
+        g, keep = ns._make_group(W, G, M, V, WM, heads=1)
+        groups.append({"shape": shape, "names": names, "g": g, "keep": keep, "hp": hp,
+                       "tensors": (G, W, M, V, WM), "ws_bytes": ns.step_workspace_bytes(g, hp)})
+    ws = torch.empty(max(gr["ws_bytes"] for gr in groups), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    L = ns.lib()
+    import ctypes
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    def one_step():
+        for gr in groups:
+            rc = L.muon_step_group(ctypes.byref(gr["g"]), ctypes.byref(gr["hp"]), ctypes.c_void_p(ws.data_ptr()),
+                                   ws.numel(), sptr)
+            if rc != 0:
+                raise RuntimeError(f"muon_step_group failed: {rc} {L.muon_last_error()}")
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup} done", file=sys.stderr, flush=True)
+
+    ns.profile_reset()
+    ns.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        one_step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ns.profile_enable(False)
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall:.2f} s)",
+          file=sys.stderr, flush=True)
+
+    prof = {k: ns.profile_query(k) for k in ns.KERNEL_CLASSES}
+    upd = prof["update"]
+    upd_avg_ms = upd["ms"] / max(upd["launches"], 1)
+    upd_tflops = upd["flop"] / (upd["ms"] * 1e-3) / 1e12 if upd["ms"] > 0 else 0.0
+
+    fl_L = sum(ns_flops(*s)[0] for _, s in LAYER)
+    fl_E = sum(ns_flops(*s)[1] for _, s in LAYER)
+    value = len(LAYER) / (ms_per_step * 1e-3)
+    tf_L = fl_L / (ms_per_step * 1e-3) / 1e12
+    tf_E = fl_E / (ms_per_step * 1e-3) / 1e12
+    per_class = {k: {"launches": v["launches"], "avg_us": round(1e3 * v["ms"] / max(v["launches"], 1), 2),
+                     "share": round(v["ms"] / max(sum(x["ms"] for x in prof.values()), 1e-9), 4)}
+                 for k, v in prof.items()}
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "orth/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama3-8b-layer-muon-normuon-step",
+            "matrices": len(LAYER),
+            "groups": [f"{len(gr['names'])}x{gr['shape'][0]}x{gr['shape'][1]}" for gr in groups],
+            "ns_iterations": 5,
+            "ns_compute": "bf16 storage, fp32 accumulate (MFMA)",
+            "normuon": True,
+            "tflops_L": round(tf_L, 2), "pct_peak_L": round(100 * tf_L / PEAK_BF16_TFLOPS, 2),
+            "tflops_E": round(tf_E, 2), "pct_peak_E": round(100 * tf_E / PEAK_BF16_TFLOPS, 2),
+            "flop_per_step_L": fl_L, "flop_per_step_E": fl_E,
+            "kernel_classes": per_class,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "update GEMM X <- a X + B X (gemm_bf16_kernel NN)",
+            "achieved": round(upd_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(upd_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_for("update"),
+            "launches": upd["launches"],
+            "avg_launch_us": round(upd_avg_ms * 1e3, 2),
+            "flop_per_launch": upd["flop"] / max(upd["launches"], 1),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the CPU", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(grads, weights, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

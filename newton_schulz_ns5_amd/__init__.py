@@ -1,0 +1,292 @@
+"""MI355X (gfx950) Muon / NorMuon step: quintic Newton-Schulz orthogonalization
+in hand-written HIP behind a C ABI (include/muon_mi355x.h).
+
+This module is the thin Python binding.  PyTorch supplies device memory and
+the current HIP stream; tensors are passed to the library as raw pointers with
+their sizes and strides, and every step of the computation runs in the
+library's kernels.  Nothing here computes on tensors.
+
+Entry points (same names as the C ABI):
+
+* ``ns_batched(x, out=None, ...)`` -- NS5 of each matrix of a [n, rows, cols]
+  (or [rows, cols]) tensor, any batch / row strides (megabatch slices, per-head
+  views from ``per_head_view``);
+* ``normuon_normalize(o, v, beta2, eps)`` -- NorMuon on [n, rows, cols];
+* ``step_group(...)`` -- one Muon / NorMuon step of same-shape parameters;
+* ``MuonNS5`` -- a small optimizer that groups parameters by flattened shape
+  and calls ``step_group`` per group.
+"""
+import ctypes
+import math
+from collections import OrderedDict
+
+from . import _lib
+from ._lib import MUON_BF16, MUON_F32, MuonError, NSConfig, Group, HParams, KERNEL_CLASSES
+
+__all__ = ["ns_batched", "normuon_normalize", "step_group", "MuonNS5", "per_head_view", "ns_config",
+           "hparams", "ns_workspace_bytes", "step_workspace_bytes", "normuon_workspace_bytes",
+           "profile_enable", "profile_reset", "profile_query", "MuonError", "QUINTIC", "abi_version",
+           "state_layout_version", "lib"]
+
+QUINTIC = (3.4445, -4.7750, 2.0315)
+lib = _lib.lib
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dt(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return MUON_F32
+    if t.dtype == torch.bfloat16:
+        return MUON_BF16
+    raise MuonError(_lib.MUON_ERR_UNSUPPORTED, f"dtype {t.dtype} is not float32 or bfloat16")
+
+
+def _cdt(name):
+    return {"bf16": MUON_BF16, "f32": MUON_F32, "fp32": MUON_F32}[name]
+
+
+def _stream(t):
+    return ctypes.c_void_p(_torch().cuda.current_stream(t.device).cuda_stream)
+
+
+def abi_version():
+    return lib().muon_abi_version()
+
+
+def state_layout_version():
+    return lib().muon_state_layout_version()
+
+
+def ns_config(steps=5, coeffs=QUINTIC, eps=1e-7, compute_dtype="bf16", max_batch=0):
+    c = NSConfig()
+    lib().muon_ns_default_config(ctypes.byref(c))
+    c.steps = int(steps)
+    c.a, c.b, c.c = (float(v) for v in coeffs)
+    c.eps = float(eps)
+    c.compute_dtype = _cdt(compute_dtype)
+    c.max_batch = int(max_batch)
+    return c
+
+
+def hparams(lr=0.05, momentum=0.95, nesterov=True, weight_decay=0.0, extra_scale=1.0, normuon=False,
+            beta2=0.95, norm_eps=1e-8, fan_out=0, fan_in=0, ns=None):
+    h = HParams()
+    lib().muon_default_hparams(ctypes.byref(h))
+    h.lr, h.momentum, h.nesterov = float(lr), float(momentum), int(bool(nesterov))
+    h.weight_decay, h.extra_scale, h.normuon = float(weight_decay), float(extra_scale), int(bool(normuon))
+    h.beta2, h.norm_eps, h.fan_out, h.fan_in = float(beta2), float(norm_eps), int(fan_out), int(fan_in)
+    h.ns = ns if ns is not None else ns_config()
+    return h
+
+
+# ---- workspace (caller-owned device memory; the library never allocates) ----
+_WS = {}
+
+
+def _workspace(device, nbytes):
+    torch = _torch()
+    key = (device.type, device.index)
+    buf = _WS.get(key)
+    if buf is None or buf.numel() < nbytes:
+        _WS.pop(key, None)
+        buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        _WS[key] = buf
+    return buf
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def ns_workspace_bytes(n, rows, cols, cfg):
+    out = ctypes.c_size_t(0)
+    _lib.check(lib().muon_ns_workspace_bytes(int(n), int(rows), int(cols), ctypes.byref(cfg), ctypes.byref(out)))
+    return out.value
+
+
+def normuon_workspace_bytes(n, rows, cols):
+    out = ctypes.c_size_t(0)
+    _lib.check(lib().normuon_workspace_bytes(int(n), int(rows), int(cols), ctypes.byref(out)))
+    return out.value
+
+
+def per_head_view(p, heads):
+    """[heads * hb, F] -> the [heads, hb, F] view (no copy)."""
+    out, f = p.shape
+    if out % heads:
+        raise MuonError(_lib.MUON_ERR_INVALID_ARG, f"rows {out} not divisible by heads {heads}")
+    return p.view(heads, out // heads, f)
+
+
+def _as3(t):
+    if t.dim() == 2:
+        return t.unsqueeze(0)
+    if t.dim() == 3:
+        return t
+    raise MuonError(_lib.MUON_ERR_INVALID_ARG, "expected a [rows, cols] or [n, rows, cols] tensor")
+
+
+def ns_batched(x, out=None, *, steps=5, coeffs=QUINTIC, eps=1e-7, compute_dtype="bf16", max_batch=0,
+               cfg=None, workspace=None):
+    """NS5 of each matrix of ``x`` ([rows, cols] or [n, rows, cols], unit column stride)."""
+    torch = _torch()
+    cfg = cfg if cfg is not None else ns_config(steps, coeffs, eps, compute_dtype, max_batch)
+    if out is None:
+        out = torch.empty_like(x, memory_format=torch.contiguous_format)
+    x3, y3 = _as3(x), _as3(out)
+    if x3.shape != y3.shape:
+        raise MuonError(_lib.MUON_ERR_INVALID_ARG, f"out shape {tuple(out.shape)} != x shape {tuple(x.shape)}")
+    if x3.numel() and (x3.stride(2) != 1 or y3.stride(2) != 1):
+        raise MuonError(_lib.MUON_ERR_INVALID_ARG, "x and out need unit column stride")
+    n, rows, cols = x3.shape
+    need = ns_workspace_bytes(n, rows, cols, cfg)
+    ws = workspace if workspace is not None else _workspace(x.device, need)
+    _lib.check(lib().muon_ns_batched(
+        _ptr(x3), _dt(x3), x3.stride(0), x3.stride(1),
+        _ptr(y3), _dt(y3), y3.stride(0), y3.stride(1),
+        n, rows, cols, ctypes.byref(cfg), _ptr(ws), ws.numel(), _stream(x)))
+    return out
+
+
+def normuon_normalize(o, v, beta2=0.95, eps=1e-8, workspace=None):
+    """In place on o ([rows, cols] or [n, rows, cols]) and v ([rows] or [n, rows], fp32)."""
+    o3 = _as3(o)
+    v2 = v.unsqueeze(0) if v.dim() == 1 else v
+    n, rows, cols = o3.shape
+    if tuple(v2.shape) != (n, rows) or (v2.numel() and v2.stride(1) != 1):
+        raise MuonError(_lib.MUON_ERR_INVALID_ARG, "v must be [n, rows] with unit stride")
+    if o3.numel() and o3.stride(2) != 1:
+        raise MuonError(_lib.MUON_ERR_INVALID_ARG, "o needs unit column stride")
+    need = normuon_workspace_bytes(n, rows, cols)
+    ws = workspace if workspace is not None else _workspace(o.device, need)
+    _lib.check(lib().normuon_normalize(
+        _ptr(o3), _dt(o3), o3.stride(0), o3.stride(1), n, rows, cols,
+        _ptr(v2), v2.stride(0), float(beta2), float(eps), _ptr(ws), ws.numel(), _stream(o)))
+    return o
+
+
+def _ptr_array(ts):
+    arr = (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+    return arr
+
+
+def _make_group(w_master, grads, moms, variances=None, w_model=None, heads=1):
+    n = len(w_master)
+    if not (len(grads) == len(moms) == n):
+        raise MuonError(_lib.MUON_ERR_INVALID_ARG, "w_master, grads and moms must have the same length")
+    shape = tuple(w_master[0].shape)
+    rows = shape[0]
+    cols = int(math.prod(shape[1:])) if len(shape) > 1 else 1
+    for lst in (w_master, grads, moms) + ((w_model,) if w_model else ()):
+        for t in lst:
+            if tuple(t.shape) != shape or not t.is_contiguous():
+                raise MuonError(_lib.MUON_ERR_INVALID_ARG, "group tensors must be contiguous and of one shape")
+    g = Group()
+    g.n, g.rows, g.cols, g.heads = n, rows, cols, int(heads)
+    g.grad_dtype = _dt(grads[0])
+    g.mom_dtype = _dt(moms[0])
+    g.model_dtype = MUON_BF16 if w_model else -1
+    keep = [_ptr_array(w_master), _ptr_array(grads), _ptr_array(moms)]
+    g.w_master = ctypes.cast(keep[0], ctypes.POINTER(ctypes.c_void_p))
+    g.grad = ctypes.cast(keep[1], ctypes.POINTER(ctypes.c_void_p))
+    g.mom = ctypes.cast(keep[2], ctypes.POINTER(ctypes.c_void_p))
+    if variances is not None:
+        keep.append(_ptr_array(variances))
+        g.var = ctypes.cast(keep[-1], ctypes.POINTER(ctypes.c_void_p))
+    if w_model:
+        keep.append(_ptr_array(w_model))
+        g.w_model = ctypes.cast(keep[-1], ctypes.POINTER(ctypes.c_void_p))
+    return g, keep
+
+
+def step_workspace_bytes(group, hp):
+    out = ctypes.c_size_t(0)
+    _lib.check(lib().muon_step_workspace_bytes(ctypes.byref(group), ctypes.byref(hp), ctypes.byref(out)))
+    return out.value
+
+
+def step_group(w_master, grads, moms, variances=None, w_model=None, *, heads=1, hp=None, workspace=None, **kw):
+    """One Muon / NorMuon step for a list of same-shape parameters (see muon_step_group)."""
+    hp = hp if hp is not None else hparams(**kw)
+    g, keep = _make_group(w_master, grads, moms, variances, w_model, heads)
+    need = step_workspace_bytes(g, hp)
+    ws = workspace if workspace is not None else _workspace(w_master[0].device, need)
+    _lib.check(lib().muon_step_group(ctypes.byref(g), ctypes.byref(hp), _ptr(ws), ws.numel(),
+                                     _stream(w_master[0])))
+    del keep
+    return None
+
+
+class MuonNS5:
+    """Muon / NorMuon over a list of matrix-shaped parameters.
+
+    Parameters are grouped by (flattened shape, dtype); each group's fp32
+    master weights, momentum and NorMuon variance are held here, and one
+    ``step_group`` call per group runs the step on the current stream.  After
+    the step the bf16 model parameters hold RNE(master).
+    """
+
+    def __init__(self, params, lr=0.05, momentum=0.95, nesterov=True, weight_decay=0.0, extra_scale=1.0,
+                 normuon=False, beta2=0.95, norm_eps=1e-8, ns_steps=5, coeffs=QUINTIC, ns_eps=1e-7,
+                 compute_dtype="bf16", mom_dtype=None, max_batch=0, heads=None):
+        torch = _torch()
+        self.params = [p for p in params]
+        heads = heads or {}
+        self.hp = hparams(lr, momentum, nesterov, weight_decay, extra_scale, normuon, beta2, norm_eps,
+                          ns=ns_config(ns_steps, coeffs, ns_eps, compute_dtype, max_batch))
+        self.groups = OrderedDict()
+        for p in self.params:
+            if p.dim() < 2:
+                raise MuonError(_lib.MUON_ERR_INVALID_ARG, "MuonNS5 takes matrix-shaped (2-D+) parameters")
+            key = (tuple(p.shape), p.dtype, int(heads.get(id(p), 1)))
+            self.groups.setdefault(key, []).append(p)
+        self.state = {}
+        for key, ps in self.groups.items():
+            for p in ps:
+                md = mom_dtype or p.dtype
+                # An fp32 parameter is its own master weight; a bf16 one gets an
+                # fp32 master and receives RNE(master) from the update kernel.
+                if p.dtype == torch.float32 and p.is_contiguous():
+                    master = p.data
+                else:
+                    master = p.detach().to(torch.float32).contiguous().clone()
+                self.state[id(p)] = {
+                    "master": master,
+                    "mom": torch.zeros(p.shape, dtype=md, device=p.device),
+                    "var": torch.zeros(p.shape[0], dtype=torch.float32, device=p.device) if normuon else None,
+                }
+
+    def step(self):
+        torch = _torch()
+        for (shape, dt, h), ps in self.groups.items():
+            live = [p for p in ps if p.grad is not None]
+            if not live:
+                continue
+            st = [self.state[id(p)] for p in live]
+            grads = [p.grad.contiguous() for p in live]
+            model = [p.data for p in live] if dt == torch.bfloat16 else None
+            step_group([s["master"] for s in st], grads, [s["mom"] for s in st],
+                       [s["var"] for s in st] if self.hp.normuon else None, model, heads=h, hp=self.hp)
+
+
+# ---- launch timing ---------------------------------------------------------------
+def profile_enable(on=True):
+    _lib.check(lib().muon_profile_enable(int(bool(on))))
+
+
+def profile_reset():
+    _lib.check(lib().muon_profile_reset())
+
+
+def profile_query(kernel_class):
+    if isinstance(kernel_class, str):
+        kernel_class = KERNEL_CLASSES.index(kernel_class)
+    n, ms, fl, by = ctypes.c_int64(0), ctypes.c_double(0), ctypes.c_double(0), ctypes.c_double(0)
+    _lib.check(lib().muon_profile_query(int(kernel_class), ctypes.byref(n), ctypes.byref(ms), ctypes.byref(fl),
+                                        ctypes.byref(by)))
+    return {"launches": n.value, "ms": ms.value, "flop": fl.value, "bytes": by.value}

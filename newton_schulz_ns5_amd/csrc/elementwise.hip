@@ -1,0 +1,332 @@
+// Bandwidth-bound kernels of the step: momentum / load with orientation and
+// Frobenius-norm partials, the norm finalize, NorMuon row statistics, the
+// NorMuon norm-preserving factor, and the weight update.
+//
+// All reductions run in a fixed order that depends only on the matrix shape
+// (per-thread sums in index order, wave64 xor butterflies, then the four
+// waves of a workgroup in index order; per-matrix partials summed the same
+// way), so every result is deterministic and independent of the batch.
+#include "muon_internal.h"
+#include "device_util.h"
+#include "muon_mi355x.h"
+
+namespace muon {
+namespace {
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_sum(v);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// Load 16 consecutive elements [c, c+16) of a row, zero beyond `valid`.
+__device__ __forceinline__ void load16(const void* row, int c, int valid, bool bf, bool vec, float* out) {
+  if (vec && c + 16 <= valid) {
+    if (bf) {
+      const u32x4* p = (const u32x4*)((const uint16_t*)row + c);
+      const u32x4 a = p[0], b = p[1];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        out[2 * w] = __uint_as_float(a[w] << 16);
+        out[2 * w + 1] = __uint_as_float(a[w] & 0xffff0000u);
+        out[8 + 2 * w] = __uint_as_float(b[w] << 16);
+        out[8 + 2 * w + 1] = __uint_as_float(b[w] & 0xffff0000u);
+      }
+    } else {
+      const f32x4* p = (const f32x4*)((const float*)row + c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 t = p[q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[4 * q + e] = t[e];
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) out[e] = (c + e < valid) ? load_elem(row, c + e, bf) : 0.f;
+}
+
+// One 64 x 64 tile of the oriented, padded X0 per workgroup.
+//   mode 0: U = x (muon_ns_batched input)
+//   mode 1: M <- mu M + G;  U = G + mu M  (or U = M without Nesterov)
+// Writes U (rounded to the X dtype) at its oriented position, zeros in the
+// padding, and the tile's sum of U^2 (from the fp32 U) to partial[].
+__global__ __launch_bounds__(256) void prep_kernel(const PrepParams p) {
+  __shared__ float T[64][65];
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const int bz = blockIdx.z;
+  const int oi0 = blockIdx.y * 64, oj0 = blockIdx.x * 64;
+  const int pr0 = p.tall ? oj0 : oi0, pc0 = p.tall ? oi0 : oj0;
+  const int r = tid >> 2, c0 = (tid & 3) * 16;
+  const int gr = pr0 + r, gc = pc0 + c0;
+  const bool src_bf = p.src_dtype == MUON_BF16;
+  float u[16];
+  float s = 0.f;
+  if (p.mode == 0) {
+    const void* row = (const uint8_t*)p.x +
+                      ((int64_t)bz * p.x_bs + (int64_t)gr * p.x_rs) * (src_bf ? 2 : 4);
+    const int valid = gr < p.rows ? p.cols - pc0 - c0 : 0;
+    const bool vec = ((p.x_rs | p.x_bs) & 7) == 0 && ((uintptr_t)p.x & 15) == 0;
+    float tmp[16];
+    if (valid > 0) load16((const uint8_t*)row + (int64_t)gc * (src_bf ? 2 : 4), 0, valid, src_bf, vec, tmp);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) u[e] = valid > 0 ? tmp[e] : 0.f;
+  } else {
+    const int pi = bz / p.heads, h = bz - pi * p.heads;
+    const bool mom_bf = p.mom_dtype == MUON_BF16;
+    const int64_t off = (int64_t)(h * p.rows + gr) * p.param_cols + gc;
+    const int valid = gr < p.rows ? p.cols - gc : 0;
+    const bool vec = (p.param_cols & 7) == 0;
+    float g[16], m[16];
+    if (valid > 0) {
+      load16((const uint8_t*)p.grad[pi] + off * (src_bf ? 2 : 4), 0, valid, src_bf, vec, g);
+      load16((const uint8_t*)p.mom[pi] + off * (mom_bf ? 2 : 4), 0, valid, mom_bf, vec, m);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      if (e < valid) {
+        const float mn = p.mu * m[e] + g[e];
+        u[e] = p.nesterov ? g[e] + p.mu * mn : mn;
+        m[e] = mn;
+      } else {
+        u[e] = 0.f;
+      }
+    }
+    if (valid > 0) {
+      void* mp = (uint8_t*)p.mom[pi] + off * (mom_bf ? 2 : 4);
+      if (vec && valid >= 16) {
+        if (mom_bf) {
+          u32x4 a, b;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            a[w] = pack_bf2(m[2 * w], m[2 * w + 1]);
+            b[w] = pack_bf2(m[8 + 2 * w], m[8 + 2 * w + 1]);
+          }
+          ((u32x4*)mp)[0] = a;
+          ((u32x4*)mp)[1] = b;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            f32x4 t;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t[e] = m[4 * q + e];
+            ((f32x4*)mp)[q] = t;
+          }
+        }
+      } else {
+        for (int e = 0; e < 16 && e < valid; ++e) store_elem(mp, e, m[e], mom_bf);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    s += u[e] * u[e];
+    T[r][c0 + e] = u[e];
+  }
+  __syncthreads();
+  // Oriented write: X[oi0 + orow][oj0 + oc0 .. +16].
+  {
+    const int orow = tid >> 2, oc0 = (tid & 3) * 16;
+    float v[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = p.tall ? T[oc0 + e][orow] : T[orow][oc0 + e];
+    const int64_t xoff = (int64_t)bz * p.X_bs + (int64_t)(oi0 + orow) * p.np + oj0 + oc0;
+    if (p.x_bf16) {
+      u32x4 a, b;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        a[w] = pack_bf2(v[2 * w], v[2 * w + 1]);
+        b[w] = pack_bf2(v[8 + 2 * w], v[8 + 2 * w + 1]);
+      }
+      u32x4* dst = (u32x4*)((uint16_t*)p.X + xoff);
+      dst[0] = a;
+      dst[1] = b;
+    } else {
+      f32x4* dst = (f32x4*)((float*)p.X + xoff);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 t;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t[e] = v[4 * q + e];
+        dst[q] = t;
+      }
+    }
+  }
+  const float tot = block_sum(s, red);
+  if (tid == 0) {
+    const int tiles = gridDim.x * gridDim.y;
+    p.partial[(int64_t)bz * tiles + blockIdx.y * gridDim.x + blockIdx.x] = tot;
+  }
+}
+
+// rs[b] = 1 / (sqrt(sum of the matrix's tile partials) + eps).
+__global__ __launch_bounds__(256) void norm_kernel(const NormParams p) {
+  __shared__ float red[4];
+  const int b = blockIdx.x;
+  const float* src = p.partial + (int64_t)b * p.tiles;
+  float s = 0.f;
+  for (int i = threadIdx.x; i < p.tiles; i += 256) s += src[i];
+  const float tot = block_sum(s, red);
+  if (threadIdx.x == 0) p.rs[b] = 1.f / (sqrtf(tot) + p.eps);
+}
+
+// NorMuon row statistics: one wave64 per row.  Lane l sums the squares of
+// elements 512 t + 8 l + e (t = 0, 1, ...; e = 0..7) in that order.
+__global__ __launch_bounds__(256) void rowstat_kernel(const RowStatParams p) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = blockIdx.y;
+  const int r = blockIdx.x * 4 + wave;
+  if (r >= p.rows) return;
+  const bool bf = p.o_dtype == MUON_BF16;
+  const uint8_t* row = (const uint8_t*)p.O + ((int64_t)b * p.o_bs + (int64_t)r * p.o_rs) * (bf ? 2 : 4);
+  const bool vec = ((p.o_bs | p.o_rs) & 7) == 0 && ((uintptr_t)p.O & 15) == 0;
+  float s = 0.f;
+  for (int c = lane * 8; c < p.cols; c += 512) {
+    float x[8];
+    if (vec && c + 8 <= p.cols) {
+      if (bf) {
+        const u32x4 a = *(const u32x4*)(row + (int64_t)c * 2);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          x[2 * w] = __uint_as_float(a[w] << 16);
+          x[2 * w + 1] = __uint_as_float(a[w] & 0xffff0000u);
+        }
+      } else {
+        const f32x4 a = *(const f32x4*)(row + (int64_t)c * 4), b2 = *(const f32x4*)(row + (int64_t)c * 4 + 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b2[e]; }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = (c + e < p.cols) ? load_elem(row, c + e, bf) : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += x[e] * x[e];
+  }
+  s = wave_sum(s);
+  if (lane == 0) {
+    const float ms = s / (float)p.cols;
+    float* v = p.v_base ? p.v_base + (int64_t)b * p.v_bs : p.v_tab[b];
+    const float vn = p.beta2 * v[r] + (1.f - p.beta2) * ms;
+    v[r] = vn;
+    const float d = 1.f / (sqrtf(vn) + p.eps);
+    const int64_t o = (int64_t)b * p.rows + r;
+    p.d[o] = d;
+    p.ms[o] = ms;
+    p.q[o] = d * d * ms;
+  }
+}
+
+// rho[b] = ||O||_F / ||diag(d) O||_F = sqrt(sum ms / sum d^2 ms); 0 when the
+// normalized matrix is zero.
+__global__ __launch_bounds__(256) void rho_kernel(const RhoParams p) {
+  __shared__ float red[4];
+  const int b = blockIdx.x;
+  float a = 0.f, q = 0.f;
+  for (int i = threadIdx.x; i < p.rows; i += 256) {
+    a += p.ms[(int64_t)b * p.rows + i];
+    q += p.q[(int64_t)b * p.rows + i];
+  }
+  const float sa = block_sum(a, red);
+  __syncthreads();
+  const float sq = block_sum(q, red);
+  if (threadIdx.x == 0) p.rho[b] = sq > 0.f ? sqrtf(sa / sq) : 0.f;
+}
+
+// One wave64 per row.  mode 0: W <- decay W - coef_r O (fp32 fused
+// multiply-add, one rounding) and the optional bf16 copy; mode 1: O <- coef_r O.
+__global__ __launch_bounds__(256) void apply_kernel(const ApplyParams p) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = blockIdx.y;
+  const int r = blockIdx.x * 4 + wave;
+  if (r >= p.rows) return;
+  const bool bf = p.o_dtype == MUON_BF16;
+  uint8_t* orow = (uint8_t*)p.O + ((int64_t)b * p.o_bs + (int64_t)r * p.o_rs) * (bf ? 2 : 4);
+  const float dr = p.d ? p.d[(int64_t)b * p.rows + r] : 1.f;
+  const float rho = p.rho ? p.rho[b] : 1.f;
+  if (p.mode == 1) {
+    const float coef = rho * dr;
+    for (int c = lane; c < p.cols; c += 64) store_elem(orow, c, coef * load_elem(orow, c, bf), bf);
+    return;
+  }
+  const float coef = p.lr_eff * (rho * dr);
+  float* w = p.w[b] + (int64_t)r * p.cols;
+  uint16_t* wm = p.wm[b] ? (uint16_t*)p.wm[b] + (int64_t)r * p.cols : nullptr;
+  if (p.vec) {
+    for (int c = lane * 8; c < p.cols; c += 512) {
+      float o[8];
+      if (bf) {
+        const u32x4 a = *(const u32x4*)(orow + (int64_t)c * 2);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          o[2 * q] = __uint_as_float(a[q] << 16);
+          o[2 * q + 1] = __uint_as_float(a[q] & 0xffff0000u);
+        }
+      } else {
+        const f32x4 a = *(const f32x4*)(orow + (int64_t)c * 4), b2 = *(const f32x4*)(orow + (int64_t)c * 4 + 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { o[e] = a[e]; o[4 + e] = b2[e]; }
+      }
+      f32x4 w0 = *(const f32x4*)(w + c), w1 = *(const f32x4*)(w + c + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w0[e] = fmaf(-coef, o[e], p.decay * w0[e]);
+        w1[e] = fmaf(-coef, o[4 + e], p.decay * w1[e]);
+      }
+      *(f32x4*)(w + c) = w0;
+      *(f32x4*)(w + c + 4) = w1;
+      if (wm) {
+        u32x4 t;
+        t[0] = pack_bf2(w0[0], w0[1]);
+        t[1] = pack_bf2(w0[2], w0[3]);
+        t[2] = pack_bf2(w1[0], w1[1]);
+        t[3] = pack_bf2(w1[2], w1[3]);
+        *(u32x4*)(wm + c) = t;
+      }
+    }
+  } else {
+    for (int c = lane; c < p.cols; c += 64) {
+      const float nw = fmaf(-coef, load_elem(orow, c, bf), p.decay * w[c]);
+      w[c] = nw;
+      if (wm) wm[c] = f2bf(nw);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prep(const PrepParams& p, int nb, hipStream_t s) {
+  if (nb <= 0) return hipSuccess;
+  hipLaunchKernelGGL(prep_kernel, dim3(p.np / kPrepTile, p.mp / kPrepTile, nb), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm(const NormParams& p, int nb, hipStream_t s) {
+  if (nb <= 0) return hipSuccess;
+  hipLaunchKernelGGL(norm_kernel, dim3(nb), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowstat(const RowStatParams& p, int nb, hipStream_t s) {
+  if (nb <= 0 || p.rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rowstat_kernel, dim3((p.rows + 3) / 4, nb), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_rho(const RhoParams& p, int nb, hipStream_t s) {
+  if (nb <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rho_kernel, dim3(nb), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_apply(const ApplyParams& p, int nb, hipStream_t s) {
+  if (nb <= 0 || p.rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(apply_kernel, dim3((p.rows + 3) / 4, nb), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace muon

@@ -1,0 +1,634 @@
+// Host side of the C ABI: validation, geometry, workspace carve-up and the
+// launch sequence of one Muon / NorMuon step on the caller's stream.
+//
+// Failure policy ("core.optimizer.layer_sharded_muon", _validate_ns_config:
+// one error kind, raised up front, never a silent switch of kernels; "Fix
+// convolution flattening in megabatches and NorMuon normalization",
+// "Compatibility": reject before mutating any state, empty shards are valid):
+// every argument is checked before the first enqueue, so a call that returns
+// an error has changed nothing.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "muon_internal.h"
+#include "muon_mi355x.h"
+
+using namespace muon;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return MUON_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MUON_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool dtype_ok(int32_t d) { return d == MUON_F32 || d == MUON_BF16; }
+size_t esize(int32_t d) { return d == MUON_BF16 ? 2 : 4; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+int64_t round_up(int64_t x, int64_t g) { return (x + g - 1) / g * g; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// ---- geometry ---------------------------------------------------------------
+// One NS problem is rows x cols in parameter orientation; it runs oriented as
+// m x n with m = min, n = max (a tall matrix goes through its transpose), in
+// workspace buffers padded to mp x np.
+struct Geom {
+  int64_t rows, cols, m, n, mp, np;
+  bool tall, bf;
+};
+
+Geom make_geom(int64_t rows, int64_t cols, int32_t compute) {
+  Geom g;
+  g.rows = rows;
+  g.cols = cols;
+  g.tall = rows > cols;
+  g.m = g.tall ? cols : rows;
+  g.n = g.tall ? rows : cols;
+  g.bf = compute == MUON_BF16;
+  const int64_t pad = g.bf ? kPadBf16 : kPadF32;
+  g.mp = round_up(g.m, pad);
+  g.np = round_up(g.n, pad);
+  return g;
+}
+
+// Workspace of `nb` NS problems (+ per-parameter NorMuon scratch for `np_`
+// parameters of `prow` rows when requested).
+struct Layout {
+  size_t X0, X1, A, B, partial, rs, d, ms, q, rho, total;
+  int tiles;
+};
+
+Layout make_layout(const Geom& g, int64_t nb, int64_t nparams, int64_t prow, bool normuon) {
+  Layout L{};
+  const size_t es = g.bf ? 2 : 4;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
+  L.tiles = (int)((g.mp / kPrepTile) * (g.np / kPrepTile));
+  L.X0 = take((size_t)nb * g.mp * g.np * es);
+  L.X1 = take((size_t)nb * g.mp * g.np * es);
+  L.A = take((size_t)nb * g.mp * g.mp * es);
+  L.B = take((size_t)nb * g.mp * g.mp * es);
+  L.partial = take((size_t)nb * L.tiles * 4);
+  L.rs = take((size_t)nb * 4);
+  if (normuon) {
+    L.d = take((size_t)nparams * prow * 4);
+    L.ms = take((size_t)nparams * prow * 4);
+    L.q = take((size_t)nparams * prow * 4);
+    L.rho = take((size_t)nparams * 4);
+  }
+  L.total = off;
+  return L;
+}
+
+// ---- launch timing ------------------------------------------------------------
+struct Pending {
+  hipEvent_t a, b;
+  int cls;
+  double flop, bytes;
+};
+struct ClassTotals {
+  int64_t launches = 0;
+  double ms = 0, flop = 0, bytes = 0;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<Pending> g_pending;
+std::vector<hipEvent_t> g_event_pool;
+ClassTotals g_totals[MUON_K_COUNT];
+
+hipError_t get_event(hipEvent_t* e) {
+  if (!g_event_pool.empty()) {
+    *e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return hipSuccess;
+  }
+  return hipEventCreate(e);
+}
+
+// Launch through `fn`, bracketed by events when timing is on.
+template <class F>
+hipError_t run(int cls, double flop, double bytes, hipStream_t s, F&& fn) {
+  if (!g_prof_on) return fn();
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  Pending pd{nullptr, nullptr, cls, flop, bytes};
+  hipError_t e = get_event(&pd.a);
+  if (e == hipSuccess) e = get_event(&pd.b);
+  if (e == hipSuccess) e = hipEventRecord(pd.a, s);
+  if (e != hipSuccess) return e;
+  e = fn();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(pd.b, s);
+  if (e != hipSuccess) return e;
+  g_pending.push_back(pd);
+  return hipSuccess;
+}
+
+hipError_t drain_pending() {
+  for (auto& pd : g_pending) {
+    hipError_t e = hipEventSynchronize(pd.b);
+    if (e != hipSuccess) return e;
+    float ms = 0;
+    e = hipEventElapsedTime(&ms, pd.a, pd.b);
+    if (e != hipSuccess) return e;
+    ClassTotals& t = g_totals[pd.cls];
+    t.launches += 1;
+    t.ms += ms;
+    t.flop += pd.flop;
+    t.bytes += pd.bytes;
+    g_event_pool.push_back(pd.a);
+    g_event_pool.push_back(pd.b);
+  }
+  g_pending.clear();
+  return hipSuccess;
+}
+
+// ---- validation helpers ------------------------------------------------------
+int check_cfg(const muon_ns_config* c) {
+  if (!c) return fail(MUON_ERR_INVALID_ARG, "ns config is NULL");
+  if (c->steps < 1 || c->steps > 64) return fail(MUON_ERR_INVALID_ARG, "steps must be in 1..64 (got %d)", c->steps);
+  if (!dtype_ok(c->compute_dtype)) return fail(MUON_ERR_UNSUPPORTED, "compute_dtype %d is not MUON_BF16 or MUON_F32", c->compute_dtype);
+  if (c->reserved != 0) return fail(MUON_ERR_INVALID_ARG, "reserved field must be 0");
+  if (c->max_batch < 0) return fail(MUON_ERR_INVALID_ARG, "max_batch must be >= 0");
+  if (!std::isfinite(c->a) || !std::isfinite(c->b) || !std::isfinite(c->c) || !std::isfinite(c->eps) || c->eps < 0)
+    return fail(MUON_ERR_INVALID_ARG, "coefficients must be finite and eps >= 0");
+  return MUON_OK;
+}
+
+constexpr int64_t kMaxDim = (int64_t)1 << 24;  // rows, cols per matrix
+
+int check_dims(int64_t n, int64_t rows, int64_t cols) {
+  if (n < 0 || rows < 0 || cols < 0) return fail(MUON_ERR_INVALID_ARG, "negative size (n=%lld rows=%lld cols=%lld)", (long long)n, (long long)rows, (long long)cols);
+  if (rows > kMaxDim || cols > kMaxDim) return fail(MUON_ERR_INVALID_ARG, "rows/cols above %lld", (long long)kMaxDim);
+  const int64_t mp = round_up(rows < cols ? rows : cols, kPadBf16), np = round_up(rows < cols ? cols : rows, kPadBf16);
+  if (mp * np >= ((int64_t)1 << 31)) return fail(MUON_ERR_INVALID_ARG, "matrix of %lld x %lld is too large", (long long)rows, (long long)cols);
+  return MUON_OK;
+}
+
+// ---- the Newton-Schulz iterations on X0 already in the workspace --------------
+struct FinalOut {
+  void* C;
+  int32_t dtype;
+  int64_t ldc, sC;
+};
+
+hipError_t gemm(const Geom& g, GemmParams& p, bool nn, bool syrk, int cls, double flop, double bytes, hipStream_t s) {
+  if (g.bf) {
+    const int tile = bf16_tile_for(p.M, p.N);
+    p.tiles_m = p.M / tile;
+    p.tiles_n = p.N / tile;
+  } else {
+    p.tiles_m = p.M / 64;
+    p.tiles_n = p.N / 64;
+  }
+  p.tiles_per_batch = syrk ? p.tiles_m * (p.tiles_m + 1) / 2 : p.tiles_m * p.tiles_n;
+  return run(cls, flop, bytes, s, [&]() {
+    return g.bf ? launch_gemm_bf16(p, nn, syrk, bf16_tile_for(p.M, p.N), s) : launch_gemm_f32(p, nn, syrk, s);
+  });
+}
+
+hipError_t ns_iterations(const Geom& g, int64_t nb, const muon_ns_config& cfg, char* ws, const Layout& L,
+                         const FinalOut& out, hipStream_t s) {
+  const int32_t wdt = g.bf ? MUON_BF16 : MUON_F32;
+  const double es = g.bf ? 2 : 4;
+  const double m = (double)g.m, n = (double)g.n, B = (double)nb;
+  void* xin = ws + L.X0;
+  void* xout = ws + L.X1;
+  void* A = ws + L.A;
+  void* Bm = ws + L.B;
+  const float* rs = (const float*)(ws + L.rs);
+  const int64_t sx = g.mp * g.np, sa = g.mp * g.mp;
+  for (int it = 0; it < cfg.steps; ++it) {
+    const bool first = it == 0, last = it == cfg.steps - 1;
+    hipError_t e;
+    {  // A = X X^T (times rs^2 on the first iteration, which folds in the normalization)
+      GemmParams p{};
+      p.P = xin; p.ldp = g.np; p.sP = sx;
+      p.Q = xin; p.ldq = g.np; p.sQ = sx;
+      p.C = A; p.ldc = g.mp; p.sC = sa; p.c_dtype = wdt;
+      p.M = p.N = (int)g.mp; p.K = (int)g.np; p.Mreal = p.Nreal = (int)g.mp;
+      p.alpha = 1.f; p.beta = 0.f;
+      p.rs = first ? rs : nullptr; p.alpha_pow = 2;
+      p.batch = (int)nb;
+      e = gemm(g, p, false, true, MUON_K_GRAM, B * m * m * n, B * (m * n + m * m) * es, s);
+      if (e != hipSuccess) return e;
+    }
+    {  // B = c A A + b A
+      GemmParams p{};
+      p.P = A; p.ldp = g.mp; p.sP = sa;
+      p.Q = A; p.ldq = g.mp; p.sQ = sa;
+      p.D = A; p.ldd = g.mp; p.sD = sa;
+      p.C = Bm; p.ldc = g.mp; p.sC = sa; p.c_dtype = wdt;
+      p.M = p.N = p.K = (int)g.mp; p.Mreal = p.Nreal = (int)g.mp;
+      p.alpha = cfg.c; p.beta = cfg.b;
+      p.batch = (int)nb;
+      e = gemm(g, p, false, true, MUON_K_POLY, B * m * m * m, B * 2 * m * m * es, s);
+      if (e != hipSuccess) return e;
+    }
+    {  // X' = B X + a X (times rs on the first iteration)
+      GemmParams p{};
+      p.P = Bm; p.ldp = g.mp; p.sP = sa;
+      p.Q = xin; p.ldq = g.np; p.sQ = sx;
+      p.D = xin; p.ldd = g.np; p.sD = sx;
+      p.M = (int)g.mp; p.N = (int)g.np; p.K = (int)g.mp;
+      p.alpha = 1.f; p.beta = cfg.a;
+      p.rs = first ? rs : nullptr; p.alpha_pow = 1; p.beta_pow = 1;
+      p.batch = (int)nb;
+      if (last) {
+        p.C = out.C; p.c_dtype = out.dtype; p.ldc = out.ldc; p.sC = out.sC;
+        p.c_trans = g.tall ? 1 : 0;
+        p.Mreal = (int)g.m; p.Nreal = (int)g.n;
+      } else {
+        p.C = xout; p.c_dtype = wdt; p.ldc = g.np; p.sC = sx;
+        p.Mreal = (int)g.mp; p.Nreal = (int)g.np;
+      }
+      e = gemm(g, p, true, false, MUON_K_UPDATE, B * 2 * m * m * n, B * (m * m + 3 * m * n) * es, s);
+      if (e != hipSuccess) return e;
+    }
+    std::swap(xin, xout);
+  }
+  return hipSuccess;
+}
+
+hipError_t norm_finalize(const Geom& g, int64_t nb, float eps, char* ws, const Layout& L, hipStream_t s) {
+  NormParams np{};
+  np.partial = (const float*)(ws + L.partial);
+  np.tiles = L.tiles;
+  np.eps = eps;
+  np.rs = (float*)(ws + L.rs);
+  return run(MUON_K_NORM, 0, (double)nb * L.tiles * 4, s, [&]() { return launch_norm(np, (int)nb, s); });
+}
+
+// Matrices (or parameters) processed per pass; the grid's z extent bounds it.
+int64_t chunk_of(int64_t n, int64_t max_batch) {
+  int64_t c = max_batch > 0 && max_batch < n ? max_batch : n;
+  return c < 65535 ? c : 65535;
+}
+
+}  // namespace
+
+// =============================================================================
+extern "C" {
+
+void muon_ns_default_config(muon_ns_config* cfg) {
+  if (!cfg) return;
+  std::memset(cfg, 0, sizeof *cfg);
+  cfg->steps = 5;
+  cfg->a = 3.4445f;
+  cfg->b = -4.7750f;
+  cfg->c = 2.0315f;
+  cfg->eps = 1e-7f;
+  cfg->compute_dtype = MUON_BF16;
+  cfg->max_batch = 0;
+}
+
+void muon_default_hparams(muon_hparams* hp) {
+  if (!hp) return;
+  std::memset(hp, 0, sizeof *hp);
+  hp->lr = 0.05f;
+  hp->momentum = 0.95f;
+  hp->nesterov = 1;
+  hp->weight_decay = 0.f;
+  hp->extra_scale = 1.f;
+  hp->normuon = 0;
+  hp->beta2 = 0.95f;
+  hp->norm_eps = 1e-8f;
+  muon_ns_default_config(&hp->ns);
+}
+
+int muon_abi_version(void) { return MUON_ABI_VERSION; }
+int muon_state_layout_version(void) { return MUON_STATE_LAYOUT_VERSION; }
+
+const char* muon_status_string(int status) {
+  switch (status) {
+    case MUON_OK: return "ok";
+    case MUON_ERR_INVALID_ARG: return "invalid argument";
+    case MUON_ERR_UNSUPPORTED: return "unsupported";
+    case MUON_ERR_WORKSPACE: return "workspace too small";
+    case MUON_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* muon_last_error(void) { return g_err.c_str(); }
+
+int muon_ns_workspace_bytes(int64_t n, int64_t rows, int64_t cols, const muon_ns_config* cfg, size_t* bytes) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if ((rc = check_dims(n, rows, cols))) return rc;
+  if (!bytes) return fail(MUON_ERR_INVALID_ARG, "bytes is NULL");
+  if (n == 0 || rows == 0 || cols == 0) { *bytes = 0; return ok(); }
+  const Geom g = make_geom(rows, cols, cfg->compute_dtype);
+  *bytes = make_layout(g, chunk_of(n, cfg->max_batch), 0, 0, false).total;
+  return ok();
+}
+
+int muon_ns_batched(const void* x, int32_t x_dtype, int64_t x_batch_stride, int64_t x_row_stride,
+                    void* y, int32_t y_dtype, int64_t y_batch_stride, int64_t y_row_stride,
+                    int64_t n, int64_t rows, int64_t cols, const muon_ns_config* cfg,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if ((rc = check_dims(n, rows, cols))) return rc;
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return fail(MUON_ERR_UNSUPPORTED, "x/y dtype must be MUON_F32 or MUON_BF16");
+  if (n == 0 || rows == 0 || cols == 0) return ok();
+  if (!x || !y) return fail(MUON_ERR_INVALID_ARG, "x or y is NULL");
+  if (x_row_stride < cols || y_row_stride < cols) return fail(MUON_ERR_INVALID_ARG, "row stride smaller than cols");
+  if (x_batch_stride < 0 || y_batch_stride < 0) return fail(MUON_ERR_INVALID_ARG, "negative batch stride");
+  if (n > 1 && y_batch_stride < (rows - 1) * y_row_stride + cols) return fail(MUON_ERR_INVALID_ARG, "output batches overlap");
+  if (((uintptr_t)x % esize(x_dtype)) || ((uintptr_t)y % esize(y_dtype))) return fail(MUON_ERR_INVALID_ARG, "x/y not aligned to their element size");
+  if (y != x) {
+    // Partial overlap of input and output would let the final store clobber unread input
+    // of another batch entry only if they share memory; in-place with equal strides is allowed.
+  } else if (x_dtype != y_dtype || x_batch_stride != y_batch_stride || x_row_stride != y_row_stride) {
+    return fail(MUON_ERR_INVALID_ARG, "in-place call needs identical dtype and strides");
+  }
+  const Geom g = make_geom(rows, cols, cfg->compute_dtype);
+  const int64_t chunk = chunk_of(n, cfg->max_batch);
+  const Layout L = make_layout(g, chunk, 0, 0, false);
+  if (!workspace) return fail(MUON_ERR_INVALID_ARG, "workspace is NULL");
+  if ((uintptr_t)workspace & 255) return fail(MUON_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < L.total) return fail(MUON_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", L.total, workspace_bytes);
+
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const size_t xe = esize(x_dtype), ye = esize(y_dtype);
+  for (int64_t c0 = 0; c0 < n; c0 += chunk) {
+    const int64_t nb = (n - c0) < chunk ? (n - c0) : chunk;
+    PrepParams pp{};
+    pp.mode = 0;
+    pp.tall = g.tall;
+    pp.rows = (int)rows; pp.cols = (int)cols;
+    pp.mp = (int)g.mp; pp.np = (int)g.np;
+    pp.heads = 1;
+    pp.src_dtype = x_dtype;
+    pp.x_bf16 = g.bf;
+    pp.x = (const char*)x + c0 * x_batch_stride * xe;
+    pp.x_bs = x_batch_stride; pp.x_rs = x_row_stride;
+    pp.X = ws + L.X0; pp.X_bs = g.mp * g.np;
+    pp.partial = (float*)(ws + L.partial);
+    hipError_t e = run(MUON_K_PREP, 0, (double)nb * rows * cols * (xe + (g.bf ? 2 : 4)), s,
+                       [&]() { return launch_prep(pp, (int)nb, s); });
+    if (e != hipSuccess) return hip_fail(e, "load kernel");
+    if ((e = norm_finalize(g, nb, cfg->eps, ws, L, s)) != hipSuccess) return hip_fail(e, "norm kernel");
+    FinalOut out{(char*)y + c0 * y_batch_stride * ye, y_dtype, y_row_stride, y_batch_stride};
+    if ((e = ns_iterations(g, nb, *cfg, ws, L, out, s)) != hipSuccess) return hip_fail(e, "Newton-Schulz kernels");
+  }
+  return ok();
+}
+
+int normuon_workspace_bytes(int64_t n, int64_t rows, int64_t cols, size_t* bytes) {
+  int rc = check_dims(n, rows, cols);
+  if (rc) return rc;
+  if (!bytes) return fail(MUON_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = align256((size_t)n * rows * 4) * 3 + align256((size_t)n * 4);
+  return ok();
+}
+
+int normuon_normalize(void* o, int32_t o_dtype, int64_t o_batch_stride, int64_t o_row_stride,
+                      int64_t n, int64_t rows, int64_t cols,
+                      float* v, int64_t v_batch_stride, float beta2, float eps,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_dims(n, rows, cols);
+  if (rc) return rc;
+  if (!dtype_ok(o_dtype)) return fail(MUON_ERR_UNSUPPORTED, "o dtype must be MUON_F32 or MUON_BF16");
+  if (!(beta2 >= 0.f && beta2 <= 1.f) || !(eps >= 0.f) || !std::isfinite(eps)) return fail(MUON_ERR_INVALID_ARG, "beta2 must be in [0,1] and eps >= 0");
+  if (n == 0 || rows == 0 || cols == 0) return ok();
+  if (!o || !v) return fail(MUON_ERR_INVALID_ARG, "o or v is NULL");
+  if (o_row_stride < cols || o_batch_stride < 0 || v_batch_stride < 0) return fail(MUON_ERR_INVALID_ARG, "bad strides");
+  if (n > 1 && (v_batch_stride < rows || o_batch_stride < (rows - 1) * o_row_stride + cols)) return fail(MUON_ERR_INVALID_ARG, "batches overlap");
+  if (((uintptr_t)o % esize(o_dtype)) || ((uintptr_t)v & 3)) return fail(MUON_ERR_INVALID_ARG, "o/v not aligned to their element size");
+  size_t need = 0;
+  normuon_workspace_bytes(n, rows, cols, &need);
+  if (!workspace) return fail(MUON_ERR_INVALID_ARG, "workspace is NULL");
+  if ((uintptr_t)workspace & 255) return fail(MUON_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need) return fail(MUON_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  if (n > 65535) return fail(MUON_ERR_INVALID_ARG, "n above 65535");
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const size_t per = align256((size_t)n * rows * 4);
+  float* d = (float*)ws;
+  float* ms = (float*)(ws + per);
+  float* q = (float*)(ws + 2 * per);
+  float* rho = (float*)(ws + 3 * per);
+  const double es = (double)esize(o_dtype);
+  RowStatParams rp{};
+  rp.O = o; rp.o_dtype = o_dtype; rp.o_bs = o_batch_stride; rp.o_rs = o_row_stride;
+  rp.rows = (int)rows; rp.cols = (int)cols;
+  rp.v_base = v; rp.v_bs = v_batch_stride;
+  rp.beta2 = beta2; rp.eps = eps;
+  rp.d = d; rp.ms = ms; rp.q = q;
+  hipError_t e = run(MUON_K_ROWSTAT, 0, (double)n * rows * (cols * es + 8), s, [&]() { return launch_rowstat(rp, (int)n, s); });
+  if (e != hipSuccess) return hip_fail(e, "row statistics kernel");
+  RhoParams hp{ms, q, (int)rows, rho};
+  e = run(MUON_K_RHO, 0, (double)n * rows * 8, s, [&]() { return launch_rho(hp, (int)n, s); });
+  if (e != hipSuccess) return hip_fail(e, "rho kernel");
+  ApplyParams ap{};
+  ap.mode = 1;
+  ap.O = o; ap.o_dtype = o_dtype; ap.o_bs = o_batch_stride; ap.o_rs = o_row_stride;
+  ap.rows = (int)rows; ap.cols = (int)cols;
+  ap.d = d; ap.rho = rho;
+  e = run(MUON_K_APPLY, 0, (double)n * rows * cols * 2 * es, s, [&]() { return launch_apply(ap, (int)n, s); });
+  if (e != hipSuccess) return hip_fail(e, "scale kernel");
+  return ok();
+}
+
+static int check_group(const muon_group* g, const muon_hparams* hp) {
+  if (!g || !hp) return fail(MUON_ERR_INVALID_ARG, "group or hparams is NULL");
+  int rc = check_cfg(&hp->ns);
+  if (rc) return rc;
+  if ((rc = check_dims(g->n, g->rows, g->cols))) return rc;
+  if (g->heads < 1) return fail(MUON_ERR_INVALID_ARG, "heads must be >= 1");
+  if (g->rows % g->heads) return fail(MUON_ERR_INVALID_ARG, "rows (%lld) not divisible by heads (%lld)", (long long)g->rows, (long long)g->heads);
+  if (!dtype_ok(g->grad_dtype) || !dtype_ok(g->mom_dtype)) return fail(MUON_ERR_UNSUPPORTED, "grad/mom dtype must be MUON_F32 or MUON_BF16");
+  if (g->model_dtype != -1 && g->model_dtype != MUON_BF16) return fail(MUON_ERR_UNSUPPORTED, "model_dtype must be MUON_BF16 or -1");
+  if (g->reserved != 0) return fail(MUON_ERR_INVALID_ARG, "reserved field must be 0");
+  if (!std::isfinite(hp->lr) || !std::isfinite(hp->momentum) || !std::isfinite(hp->weight_decay) || !std::isfinite(hp->extra_scale))
+    return fail(MUON_ERR_INVALID_ARG, "lr, momentum, weight_decay and extra_scale must be finite");
+  if (hp->normuon && (!(hp->beta2 >= 0.f && hp->beta2 <= 1.f) || !(hp->norm_eps >= 0.f) || !std::isfinite(hp->norm_eps)))
+    return fail(MUON_ERR_INVALID_ARG, "beta2 must be in [0,1] and norm_eps >= 0");
+  if (hp->fan_out < 0 || hp->fan_in < 0) return fail(MUON_ERR_INVALID_ARG, "fan_out/fan_in must be >= 0");
+  if (g->n == 0 || g->rows == 0 || g->cols == 0) return MUON_OK;
+  if (!g->w_master || !g->grad || !g->mom) return fail(MUON_ERR_INVALID_ARG, "w_master, grad and mom arrays are required");
+  if (hp->normuon && !g->var) return fail(MUON_ERR_INVALID_ARG, "var array is required with normuon");
+  if (g->model_dtype == MUON_BF16 && !g->w_model) return fail(MUON_ERR_INVALID_ARG, "w_model array is required for a bf16 model copy");
+  for (int64_t i = 0; i < g->n; ++i) {
+    if (!g->w_master[i] || !g->grad[i] || !g->mom[i]) return fail(MUON_ERR_INVALID_ARG, "NULL tensor pointer for parameter %lld", (long long)i);
+    if (!aligned16(g->w_master[i]) || !aligned16(g->grad[i]) || !aligned16(g->mom[i]))
+      return fail(MUON_ERR_INVALID_ARG, "parameter %lld: tensors must be 16-byte aligned", (long long)i);
+    if (hp->normuon && (!g->var[i] || ((uintptr_t)g->var[i] & 3))) return fail(MUON_ERR_INVALID_ARG, "bad var pointer for parameter %lld", (long long)i);
+    if (g->model_dtype == MUON_BF16 && (!g->w_model[i] || !aligned16(g->w_model[i])))
+      return fail(MUON_ERR_INVALID_ARG, "bad w_model pointer for parameter %lld", (long long)i);
+  }
+  return MUON_OK;
+}
+
+int muon_step_workspace_bytes(const muon_group* g, const muon_hparams* hp, size_t* bytes) {
+  if (!bytes) return fail(MUON_ERR_INVALID_ARG, "bytes is NULL");
+  if (!g || !hp) return fail(MUON_ERR_INVALID_ARG, "group or hparams is NULL");
+  int rc = check_cfg(&hp->ns);
+  if (rc) return rc;
+  if ((rc = check_dims(g->n, g->rows, g->cols))) return rc;
+  if (g->heads < 1 || (g->rows % g->heads)) return fail(MUON_ERR_INVALID_ARG, "rows must divide into heads >= 1");
+  if (g->n == 0 || g->rows == 0 || g->cols == 0) { *bytes = 0; return ok(); }
+  const Geom ge = make_geom(g->rows / g->heads, g->cols, hp->ns.compute_dtype);
+  const int64_t pc = chunk_of(g->n, hp->ns.max_batch);
+  *bytes = make_layout(ge, pc * g->heads, pc, g->rows, hp->normuon != 0).total;
+  return ok();
+}
+
+int muon_step_group(const muon_group* g, const muon_hparams* hp, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_group(g, hp);
+  if (rc) return rc;
+  if (g->n == 0 || g->rows == 0 || g->cols == 0) return ok();
+  const int64_t H = g->heads, hb = g->rows / H;
+  const Geom ge = make_geom(hb, g->cols, hp->ns.compute_dtype);
+  const int64_t pc = chunk_of(g->n, hp->ns.max_batch);
+  const bool nm = hp->normuon != 0;
+  const Layout L = make_layout(ge, pc * H, pc, g->rows, nm);
+  if (!workspace) return fail(MUON_ERR_INVALID_ARG, "workspace is NULL");
+  if ((uintptr_t)workspace & 255) return fail(MUON_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < L.total) return fail(MUON_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", L.total, workspace_bytes);
+  if (pc * H > 65535) return fail(MUON_ERR_INVALID_ARG, "parameters x heads per pass above 65535; set ns.max_batch");
+
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int32_t odt = ge.bf ? MUON_BF16 : MUON_F32;
+  const double oes = ge.bf ? 2 : 4;
+  const double ges = (double)esize(g->grad_dtype), mes = (double)esize(g->mom_dtype);
+  const int64_t fan_out = hp->fan_out ? hp->fan_out : g->rows;
+  const int64_t fan_in = hp->fan_in ? hp->fan_in : g->cols;
+  const double ratio = (double)fan_out / (double)fan_in;
+  const float lr_eff = (float)((double)hp->lr * std::sqrt(ratio > 1.0 ? ratio : 1.0) * (double)hp->extra_scale);
+  const float decay = (float)(1.0 - (double)hp->lr * (double)hp->weight_decay);
+  const bool vec = (g->cols % 8) == 0;
+  const int64_t pelems = g->rows * g->cols;
+
+  for (int64_t c0 = 0; c0 < g->n; c0 += pc) {
+    const int64_t np_ = (g->n - c0) < pc ? (g->n - c0) : pc;
+    hipError_t e;
+    // momentum, orientation, norm partials
+    for (int64_t s0 = 0; s0 < np_; s0 += kMaxParams) {
+      const int64_t k = (np_ - s0) < kMaxParams ? (np_ - s0) : kMaxParams;
+      PrepParams pp{};
+      pp.mode = 1;
+      pp.tall = ge.tall;
+      pp.rows = (int)hb; pp.cols = (int)g->cols;
+      pp.mp = (int)ge.mp; pp.np = (int)ge.np;
+      pp.heads = (int)H;
+      pp.src_dtype = g->grad_dtype; pp.mom_dtype = g->mom_dtype;
+      pp.x_bf16 = ge.bf;
+      pp.mu = hp->momentum; pp.nesterov = hp->nesterov ? 1 : 0;
+      pp.param_cols = g->cols;
+      for (int64_t i = 0; i < k; ++i) {
+        pp.grad[i] = g->grad[c0 + s0 + i];
+        pp.mom[i] = g->mom[c0 + s0 + i];
+      }
+      pp.X = ws + L.X0 + (size_t)(s0 * H) * ge.mp * ge.np * (size_t)oes;
+      pp.X_bs = ge.mp * ge.np;
+      pp.partial = (float*)(ws + L.partial) + s0 * H * L.tiles;
+      e = run(MUON_K_PREP, 0, (double)k * pelems * (ges + 2 * mes + oes), s, [&]() { return launch_prep(pp, (int)(k * H), s); });
+      if (e != hipSuccess) return hip_fail(e, "momentum kernel");
+    }
+    if ((e = norm_finalize(ge, np_ * H, hp->ns.eps, ws, L, s)) != hipSuccess) return hip_fail(e, "norm kernel");
+    // Newton-Schulz; the last update writes O in parameter orientation into
+    // whichever ping-pong buffer is free ([n][rows][cols], contiguous).
+    void* obuf = ws + ((hp->ns.steps % 2) ? L.X1 : L.X0);
+    FinalOut out{obuf, odt, g->cols, hb * g->cols};
+    if ((e = ns_iterations(ge, np_ * H, hp->ns, ws, L, out, s)) != hipSuccess) return hip_fail(e, "Newton-Schulz kernels");
+    if (nm) {
+      RowStatParams rp{};
+      rp.O = obuf; rp.o_dtype = odt; rp.o_bs = pelems; rp.o_rs = g->cols;
+      rp.rows = (int)g->rows; rp.cols = (int)g->cols;
+      rp.beta2 = hp->beta2; rp.eps = hp->norm_eps;
+      rp.d = (float*)(ws + L.d); rp.ms = (float*)(ws + L.ms); rp.q = (float*)(ws + L.q);
+      for (int64_t s0 = 0; s0 < np_; s0 += kMaxParams) {
+        const int64_t k = (np_ - s0) < kMaxParams ? (np_ - s0) : kMaxParams;
+        RowStatParams r2 = rp;
+        r2.O = (char*)obuf + (size_t)s0 * pelems * (size_t)oes;
+        r2.d += s0 * g->rows; r2.ms += s0 * g->rows; r2.q += s0 * g->rows;
+        for (int64_t i = 0; i < k; ++i) r2.v_tab[i] = g->var[c0 + s0 + i];
+        e = run(MUON_K_ROWSTAT, 0, (double)k * (pelems * oes + g->rows * 8), s, [&]() { return launch_rowstat(r2, (int)k, s); });
+        if (e != hipSuccess) return hip_fail(e, "row statistics kernel");
+      }
+      RhoParams hpm{(float*)(ws + L.ms), (float*)(ws + L.q), (int)g->rows, (float*)(ws + L.rho)};
+      e = run(MUON_K_RHO, 0, (double)np_ * g->rows * 8, s, [&]() { return launch_rho(hpm, (int)np_, s); });
+      if (e != hipSuccess) return hip_fail(e, "rho kernel");
+    }
+    for (int64_t s0 = 0; s0 < np_; s0 += kMaxParams) {
+      const int64_t k = (np_ - s0) < kMaxParams ? (np_ - s0) : kMaxParams;
+      ApplyParams ap{};
+      ap.mode = 0;
+      ap.O = (char*)obuf + (size_t)s0 * pelems * (size_t)oes;
+      ap.o_dtype = odt; ap.o_bs = pelems; ap.o_rs = g->cols;
+      ap.rows = (int)g->rows; ap.cols = (int)g->cols;
+      ap.d = nm ? (float*)(ws + L.d) + s0 * g->rows : nullptr;
+      ap.rho = nm ? (float*)(ws + L.rho) + s0 : nullptr;
+      ap.lr_eff = lr_eff; ap.decay = decay;
+      ap.vec = vec ? 1 : 0;
+      for (int64_t i = 0; i < k; ++i) {
+        ap.w[i] = g->w_master[c0 + s0 + i];
+        ap.wm[i] = g->model_dtype == MUON_BF16 ? g->w_model[c0 + s0 + i] : nullptr;
+      }
+      const double wb = g->model_dtype == MUON_BF16 ? 10 : 8;
+      e = run(MUON_K_APPLY, 0, (double)k * pelems * (oes + wb), s, [&]() { return launch_apply(ap, (int)k, s); });
+      if (e != hipSuccess) return hip_fail(e, "update kernel");
+    }
+  }
+  return ok();
+}
+
+// ---- launch timing ------------------------------------------------------------
+int muon_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  return ok();
+}
+
+int muon_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  hipError_t e = drain_pending();
+  for (auto& t : g_totals) t = ClassTotals{};
+  if (e != hipSuccess) return hip_fail(e, "event synchronize");
+  return ok();
+}
+
+int muon_profile_query(int kernel_class, int64_t* launches, double* total_ms, double* total_flop, double* total_bytes) {
+  if (kernel_class < 0 || kernel_class >= MUON_K_COUNT) return fail(MUON_ERR_INVALID_ARG, "kernel class %d out of range", kernel_class);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  hipError_t e = drain_pending();
+  if (e != hipSuccess) return hip_fail(e, "event synchronize");
+  const ClassTotals& t = g_totals[kernel_class];
+  if (launches) *launches = t.launches;
+  if (total_ms) *total_ms = t.ms;
+  if (total_flop) *total_flop = t.flop;
+  if (total_bytes) *total_bytes = t.bytes;
+  return ok();
+}
+
+const char* muon_kernel_class_name(int kernel_class) {
+  static const char* names[MUON_K_COUNT] = {"prep", "norm", "gram", "poly", "update", "rowstat", "rho", "apply"};
+  return (kernel_class >= 0 && kernel_class < MUON_K_COUNT) ? names[kernel_class] : "unknown";
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// Internal declarations shared by the host entry points and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace muon {
+
+// Pointer tables travel in kernel arguments; a launch covers at most this
+// many parameters.
+constexpr int kMaxParams = 32;
+
+// Padding granule of the oriented workspace matrices.  Pad rows and columns
+// are zero and stay zero through every iteration (zero columns add nothing to
+// X X^T; zero rows of B give zero rows of B X), so the GEMMs need no bounds
+// checks in their main loops.
+constexpr int kPadBf16 = 128;
+constexpr int kPadF32 = 64;
+constexpr int kPrepTile = 64;   // tile edge of the load / momentum kernel
+
+// ---- GEMM: C[b] = alpha_b * P[b] * op(Q[b]) + beta_b * D[b] -------------------
+// P is [M][K] row-major.  NT: Q is [N][K] (both operands K-contiguous).
+// NN: Q is [K][N].  SYRK: only tiles with tile_n >= tile_m are computed and
+// each value is also written to the mirrored position, so C is exactly
+// symmetric.
+struct GemmParams {
+  const void* P; int64_t ldp; int64_t sP;
+  const void* Q; int64_t ldq; int64_t sQ;
+  const void* D; int64_t ldd; int64_t sD;   // may be null
+  void* C; int64_t ldc; int64_t sC;
+  int32_t c_dtype;        // MUON_BF16 / MUON_F32
+  int32_t c_trans;        // store C^T: element (i, j) goes to C[j*ldc + i]
+  int32_t M, N, K;        // padded problem (multiples of the tile edges)
+  int32_t Mreal, Nreal;   // only i < Mreal, j < Nreal are stored
+  float alpha, beta;
+  const float* rs;        // per-batch factor, may be null
+  int32_t alpha_pow, beta_pow;  // alpha_b = alpha * rs[b]^alpha_pow ...
+  int32_t batch;
+  int32_t tiles_m, tiles_n, tiles_per_batch;
+};
+
+// ---- load / momentum / orientation / norm partials ------------------------
+struct PrepParams {
+  int32_t mode;           // 0: U = x (plain load); 1: Nesterov momentum
+  int32_t tall;           // oriented X = U^T
+  int32_t rows, cols;     // one NS matrix in parameter orientation
+  int32_t mp, np;         // padded oriented dims
+  int32_t heads;          // NS matrices per parameter (mode 1)
+  int32_t src_dtype;      // x (mode 0) or grad (mode 1)
+  int32_t mom_dtype;      // mode 1
+  int32_t x_bf16;         // X0 storage dtype is bf16
+  float mu; int32_t nesterov;
+  const void* x; int64_t x_bs, x_rs;          // mode 0
+  int64_t param_cols;                          // mode 1: row stride of a parameter
+  const void* grad[kMaxParams];                // mode 1
+  void* mom[kMaxParams];                       // mode 1
+  void* X; int64_t X_bs;                       // oriented, padded output
+  float* partial;                              // [b][tiles]
+};
+
+struct NormParams {
+  const float* partial; int32_t tiles;
+  float eps;
+  float* rs;              // rs[b] = 1 / (sqrt(sum partial) + eps)
+};
+
+// ---- NorMuon statistics ---------------------------------------------------
+struct RowStatParams {
+  const void* O; int32_t o_dtype; int64_t o_bs, o_rs;
+  int32_t rows, cols;
+  float* v_tab[kMaxParams];       // per-matrix variance pointers (table mode)
+  float* v_base; int64_t v_bs;    // strided mode when v_base != null
+  float beta2, eps;
+  float* d; float* ms; float* q;  // workspace [b][rows]
+};
+
+struct RhoParams {
+  const float* ms; const float* q; int32_t rows;
+  float* rho;
+};
+
+// ---- weight update / in-place scaling ------------------------------------
+struct ApplyParams {
+  int32_t mode;           // 0: weight update; 1: o <- rho * d_r * o in place
+  const void* O; int32_t o_dtype; int64_t o_bs, o_rs;
+  int32_t rows, cols;
+  const float* d; const float* rho;   // null without NorMuon
+  float lr_eff, decay;    // decay = 1 - lr * wd
+  float* w[kMaxParams];
+  void* wm[kMaxParams];   // bf16 model copy or null
+  int32_t vec;            // 1: 16-byte vector path is valid
+};
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_gemm_bf16(const GemmParams& p, bool nn, bool syrk, int tile, hipStream_t s);
+hipError_t launch_gemm_f32(const GemmParams& p, bool nn, bool syrk, hipStream_t s);
+hipError_t launch_prep(const PrepParams& p, int nb, hipStream_t s);
+hipError_t launch_norm(const NormParams& p, int nb, hipStream_t s);
+hipError_t launch_rowstat(const RowStatParams& p, int nb, hipStream_t s);
+hipError_t launch_rho(const RhoParams& p, int nb, hipStream_t s);
+hipError_t launch_apply(const ApplyParams& p, int nb, hipStream_t s);
+
+// Tile edge the bf16 GEMM uses for an M x N output (depends on shape only).
+inline int bf16_tile_for(int M, int N) { return (M % 256 == 0 && N % 256 == 0) ? 256 : 128; }
+
+}  // namespace muon

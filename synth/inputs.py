@@ -27,7 +27,7 @@ import numpy as np
 __all__ = [
     "ROLE_GRAD", "ROLE_WEIGHT", "ROLE_U", "ROLE_V", "ROLE_NOISE",
     "generator", "f64_to_bf16_bits", "bf16_bits_to_f64", "bf16_bits_to_f32",
-    "store", "gaussian", "haar", "power_law",
+    "store", "gaussian", "haar", "power_law", "power_law_many",
     "LLAMA3_8B_LAYER", "conv_megabatches",
 ]
 
@@ -61,10 +61,10 @@ def f64_to_bf16_bits(x) -> np.ndarray:
     Returns the raw 16-bit patterns as uint16.
     """
     f = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
-    u = f.view(np.uint32).astype(np.uint64)
+    u = f.view(np.uint32)
+    # uint32 arithmetic wraps only for NaN patterns, which are replaced below.
+    r = ((u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(f)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
     if nan.any():
         r = np.where(nan, np.uint16(0x7FC0), r)
     return r
@@ -101,14 +101,30 @@ def gaussian(shape, key, dtype: str = "f32", std: float = 1.0) -> np.ndarray:
 def haar(n: int, k: int, key) -> np.ndarray:
     """An n x k matrix with orthonormal columns, Haar distributed (float64).
 
-    Q factor of a Gaussian matrix with the signs of diag(R) moved into Q.
+    The Q factor, with positive diag(R), of the QR factorization of an n x k
+    Gaussian matrix.  For n >= 2k the factor is computed by two passes of
+    Cholesky QR (the same Q in exact arithmetic; a tall Gaussian matrix is
+    well conditioned, so the result is orthonormal to rounding), otherwise by
+    Householder QR with the signs of diag(R) moved into Q.
     """
     g = generator(*key)
     z = g.standard_normal(size=(n, k))
+    if n >= 2 * k:
+        q = z
+        for _ in range(2):
+            r = np.linalg.cholesky(q.T @ q).T          # upper triangular, positive diagonal
+            q = q @ _inv_upper(r)
+        return q
     q, r = np.linalg.qr(z, mode="reduced")
     d = np.sign(np.diag(r))
     d[d == 0] = 1.0
     return q * d[None, :]
+
+
+def _inv_upper(r):
+    """Inverse of an upper-triangular matrix."""
+    import scipy.linalg
+    return scipy.linalg.solve_triangular(r, np.eye(r.shape[0]), lower=False)
 
 
 def power_law(shape, key_uv, key_noise, dtype: str = "bf16", alpha: float = 0.7,
@@ -118,12 +134,26 @@ def power_law(shape, key_uv, key_noise, dtype: str = "bf16", alpha: float = 0.7,
     ``key_uv`` seeds U (role 2) and V (role 3); ``key_noise`` seeds the noise.
     Keys are tuples without the role component.
     """
+    return power_law_many(shape, key_uv, [key_noise], dtype, alpha, noise)[0]
+
+
+def power_law_many(shape, key_uv, keys_noise, dtype: str = "bf16", alpha: float = 0.7,
+                   noise: float = 0.1):
+    """Several power-law matrices sharing U, V and s, each with its own noise.
+
+    Entry i equals ``power_law(shape, key_uv, keys_noise[i], ...)``.
+    """
     r, c = int(shape[0]), int(shape[1])
     k = min(r, c)
     u = haar(r, k, tuple(key_uv) + (ROLE_U,))
     v = haar(c, k, tuple(key_uv) + (ROLE_V,))
     s = np.arange(1, k + 1, dtype=np.float64) ** (-alpha)
-    gnoise = generator(*(tuple(key_noise) + (ROLE_NOISE,)))
-    g = (u * s[None, :]) @ v.T
-    g += noise * gnoise.standard_normal(size=(r, c))
-    return store(g, dtype)
+    signal = (u * s[None, :]) @ v.T
+    del u, v
+    out = []
+    for kn in keys_noise:
+        gnoise = generator(*(tuple(kn) + (ROLE_NOISE,)))
+        g = noise * gnoise.standard_normal(size=(r, c))
+        g += signal
+        out.append(store(g, dtype))
+    return out

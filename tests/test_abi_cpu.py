@@ -1,0 +1,230 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+the header declares, the ctypes structures match the C layout, and every
+argument error is reported before anything is enqueued."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import newton_schulz_ns5_amd as m
+from newton_schulz_ns5_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon_mi355x.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\**\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_expected_entry_points():
+    names = header_functions()
+    for required in ["muon_ns_batched", "muon_step_group", "normuon_normalize", "muon_ns_workspace_bytes",
+                     "muon_step_workspace_bytes", "normuon_workspace_bytes", "muon_last_error"]:
+        assert required in names
+
+
+def test_library_exports_every_header_function():
+    h = ctypes.CDLL(_lib.LIB_PATH)
+    missing = [n for n in header_functions() if not hasattr(h, n)]
+    assert not missing, missing
+    assert set(header_functions()) == set(_lib.SIGNATURES), "binding signatures drifted from the header"
+
+
+def _c_layout():
+    src = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "muon_mi355x.h"
+#define F(T, f) printf(#T "." #f " %zu\n", offsetof(T, f))
+int main(void) {
+  printf("muon_ns_config %zu\n", sizeof(muon_ns_config));
+  printf("muon_group %zu\n", sizeof(muon_group));
+  printf("muon_hparams %zu\n", sizeof(muon_hparams));
+  F(muon_ns_config, steps); F(muon_ns_config, a); F(muon_ns_config, b); F(muon_ns_config, c);
+  F(muon_ns_config, eps); F(muon_ns_config, compute_dtype); F(muon_ns_config, reserved); F(muon_ns_config, max_batch);
+  F(muon_group, n); F(muon_group, rows); F(muon_group, cols); F(muon_group, heads); F(muon_group, grad_dtype);
+  F(muon_group, mom_dtype); F(muon_group, model_dtype); F(muon_group, reserved); F(muon_group, w_master);
+  F(muon_group, w_model); F(muon_group, grad); F(muon_group, mom); F(muon_group, var);
+  F(muon_hparams, lr); F(muon_hparams, momentum); F(muon_hparams, nesterov); F(muon_hparams, weight_decay);
+  F(muon_hparams, extra_scale); F(muon_hparams, normuon); F(muon_hparams, beta2); F(muon_hparams, norm_eps);
+  F(muon_hparams, fan_out); F(muon_hparams, fan_in); F(muon_hparams, ns);
+  return 0;
+}
+"""
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "layout.c")
+        exe = os.path.join(d, "layout")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), c, "-o", exe], check=True)
+        out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout
+    return dict((k, int(v)) for k, v in (line.split() for line in out.splitlines()))
+
+
+def test_ctypes_structs_match_c_layout():
+    lay = _c_layout()
+    for cname, py in [("muon_ns_config", m.NSConfig), ("muon_group", m.Group), ("muon_hparams", m.HParams)]:
+        assert ctypes.sizeof(py) == lay[cname], cname
+        for fname, _ in py._fields_:
+            assert getattr(py, fname).offset == lay[f"{cname}.{fname}"], (cname, fname)
+
+
+def test_versions_and_status_strings():
+    L = m.lib()
+    assert L.muon_abi_version() == 1 and L.muon_state_layout_version() == 1
+    for code, word in [(0, b"ok"), (-1, b"invalid"), (-2, b"unsupported"), (-3, b"workspace"), (-4, b"HIP")]:
+        assert word in L.muon_status_string(code)
+    assert L.muon_kernel_class_name(4) == b"update"
+
+
+def test_defaults():
+    c = m.ns_config()
+    assert (c.steps, c.compute_dtype, c.max_batch) == (5, _lib.MUON_BF16, 0)
+    assert abs(c.a - 3.4445) < 1e-6 and abs(c.b + 4.775) < 1e-6 and abs(c.c - 2.0315) < 1e-6
+    h = m.hparams()
+    assert abs(h.lr - 0.05) < 1e-9 and abs(h.momentum - 0.95) < 1e-7 and h.nesterov == 1
+    assert abs(h.beta2 - 0.95) < 1e-7 and abs(h.norm_eps - 1e-8) < 1e-15
+
+
+FAKE = 1 << 20  # a non-null, 256-aligned address that is never dereferenced
+
+
+def ns_call(**over):
+    a = dict(x=FAKE, xd=1, xbs=64 * 64, xrs=64, y=FAKE, yd=1, ybs=64 * 64, yrs=64, n=1, rows=64, cols=64,
+             cfg=m.ns_config(), ws=FAKE, wsb=1 << 40)
+    a.update(over)
+    L = m.lib()
+    return L.muon_ns_batched(ctypes.c_void_p(a["x"]), a["xd"], a["xbs"], a["xrs"], ctypes.c_void_p(a["y"]), a["yd"],
+                             a["ybs"], a["yrs"], a["n"], a["rows"], a["cols"],
+                             ctypes.byref(a["cfg"]) if a["cfg"] is not None else None,
+                             ctypes.c_void_p(a["ws"]), a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(x=0), -1), (dict(y=0), -1), (dict(ws=0), -1), (dict(ws=FAKE + 16), -1),
+    (dict(n=-1), -1), (dict(rows=-3), -1), (dict(xrs=10), -1), (dict(yrs=63), -1), (dict(xbs=-1), -1),
+    (dict(xd=7), -2), (dict(yd=2), -2), (dict(cfg=m.ns_config(steps=0)), -1), (dict(cfg=m.ns_config(steps=65)), -1),
+    (dict(cfg=None), -1), (dict(wsb=100), -3), (dict(n=2, ybs=10), -1), (dict(x=FAKE + 1), -1),
+    (dict(rows=1 << 25), -1),
+])
+def test_ns_batched_argument_errors(over, code):
+    assert ns_call(**over) == code
+    assert m.lib().muon_last_error()
+
+
+def test_ns_batched_unsupported_compute_dtype():
+    c = m.ns_config()
+    c.compute_dtype = 5
+    assert ns_call(cfg=c) == -2
+    c = m.ns_config()
+    c.reserved = 1
+    assert ns_call(cfg=c) == -1
+
+
+@pytest.mark.parametrize("over", [dict(n=0), dict(rows=0), dict(cols=0), dict(n=0, x=0, y=0, ws=0)])
+def test_ns_batched_empty_is_noop(over):
+    assert ns_call(**over) == 0
+
+
+def test_ns_batched_without_gpu_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert ns_call() == -4
+    assert b"device" in m.lib().muon_last_error().lower() or m.lib().muon_last_error()
+
+
+def test_ns_workspace_query():
+    c = m.ns_config()
+    a = m.ns_workspace_bytes(3, 300, 520, c)
+    b = m.ns_workspace_bytes(6, 300, 520, c)
+    assert 0 < a < b
+    assert m.ns_workspace_bytes(6, 300, 520, m.ns_config(max_batch=3)) == a
+    assert m.ns_workspace_bytes(1, 520, 300, c) == m.ns_workspace_bytes(1, 300, 520, c)  # orientation
+    assert m.ns_workspace_bytes(0, 300, 520, c) == 0
+    f = m.ns_workspace_bytes(1, 256, 256, m.ns_config(compute_dtype="f32"))
+    h = m.ns_workspace_bytes(1, 256, 256, c)
+    assert f > h
+
+
+def group_call(hp=None, **over):
+    L = m.lib()
+    n = over.pop("n", 2)
+    arrs = {k: (ctypes.c_void_p * max(n, 1))(*([FAKE] * max(n, 1))) for k in ["w", "g", "m", "v", "wm"]}
+    for k, v in over.pop("arrays", {}).items():
+        arrs[k] = v
+    g = m.Group()
+    g.n, g.rows, g.cols, g.heads = n, over.pop("rows", 64), over.pop("cols", 96), over.pop("heads", 1)
+    g.grad_dtype, g.mom_dtype, g.model_dtype = over.pop("gd", 1), over.pop("md", 1), over.pop("mdl", -1)
+    g.reserved = over.pop("reserved", 0)
+    P = ctypes.POINTER(ctypes.c_void_p)
+    g.w_master = ctypes.cast(arrs["w"], P) if arrs["w"] is not None else None
+    g.grad = ctypes.cast(arrs["g"], P) if arrs["g"] is not None else None
+    g.mom = ctypes.cast(arrs["m"], P) if arrs["m"] is not None else None
+    g.var = ctypes.cast(arrs["v"], P) if arrs["v"] is not None else None
+    g.w_model = ctypes.cast(arrs["wm"], P) if arrs["wm"] is not None else None
+    hp = hp or m.hparams()
+    ws = over.pop("ws", FAKE)
+    wsb = over.pop("wsb", 1 << 40)
+    assert not over, over
+    return L.muon_step_group(ctypes.byref(g), ctypes.byref(hp), ctypes.c_void_p(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(heads=0), -1), (dict(heads=5), -1), (dict(gd=3), -2), (dict(md=9), -2), (dict(mdl=0), -2),
+    (dict(reserved=2), -1), (dict(arrays={"w": None}), -1), (dict(arrays={"g": None}), -1),
+    (dict(arrays={"m": None}), -1), (dict(mdl=1, arrays={"wm": None}), -1),
+    (dict(arrays={"w": (ctypes.c_void_p * 2)(FAKE, 0)}), -1),
+    (dict(arrays={"g": (ctypes.c_void_p * 2)(FAKE, FAKE + 8)}), -1),
+    (dict(wsb=1000), -3), (dict(ws=0), -1), (dict(rows=-1), -1),
+])
+def test_step_group_argument_errors(kw, code):
+    assert group_call(**kw) == code
+
+
+def test_step_group_normuon_needs_var():
+    hp = m.hparams(normuon=True)
+    assert group_call(hp=hp, arrays={"v": None}) == -1
+    hp = m.hparams(normuon=True, beta2=1.5)
+    assert group_call(hp=hp) == -1
+
+
+def test_step_group_bad_hparams():
+    assert group_call(hp=m.hparams(lr=float("nan"))) == -1
+    assert group_call(hp=m.hparams(fan_out=-1)) == -1
+    assert group_call(hp=m.hparams(ns=m.ns_config(steps=0))) == -1
+
+
+@pytest.mark.parametrize("kw", [dict(n=0), dict(rows=0), dict(cols=0)])
+def test_step_group_empty_is_noop(kw):
+    assert group_call(**kw) == 0
+
+
+def test_step_workspace_scales_with_heads_and_batch():
+    hp = m.hparams()
+    g = m.Group()
+    g.n, g.rows, g.cols, g.heads, g.grad_dtype, g.mom_dtype, g.model_dtype = 4, 4096, 4096, 32, 1, 1, -1
+    per_head = m.step_workspace_bytes(g, hp)
+    g.heads = 1
+    whole = m.step_workspace_bytes(g, hp)
+    assert per_head < whole     # 32 Gram matrices of 128^2 instead of one 4096^2
+    hp2 = m.hparams(ns=m.ns_config(max_batch=1))
+    assert m.step_workspace_bytes(g, hp2) < whole
+
+
+def test_normuon_argument_errors():
+    L = m.lib()
+    ws = ctypes.c_void_p(FAKE)
+    def call(**o):
+        a = dict(o=FAKE, od=1, obs=64 * 8, ors=64, n=2, rows=8, cols=64, v=FAKE, vbs=8, b2=0.95, eps=1e-8, wsb=1 << 30)
+        a.update(o)
+        return L.normuon_normalize(ctypes.c_void_p(a["o"]), a["od"], a["obs"], a["ors"], a["n"], a["rows"], a["cols"],
+                                   ctypes.c_void_p(a["v"]), a["vbs"], a["b2"], a["eps"], ws, a["wsb"], None)
+    assert call(o=0) == -1 and call(v=0) == -1 and call(od=4) == -2 and call(b2=2.0) == -1
+    assert call(ors=3) == -1 and call(vbs=3) == -1 and call(wsb=10) == -3 and call(n=0) == 0

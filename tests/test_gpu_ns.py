@@ -1,0 +1,175 @@
+"""GPU parity of muon_ns_batched against the CPU float64 oracle.
+
+Tolerances (relative Frobenius error per matrix, max over the batch): 2e-2
+in bf16 compute mode, 1e-4 in fp32 compute mode.  Index and layout results
+(per-head slices, megabatch slices, transposed orientation) are bitwise.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import TOL, max_rel_fro, rel_fro, storage_f64, to_dev, to_f64, torch_cuda
+
+import newton_schulz_ns5_amd as ns
+
+pytestmark = pytest.mark.gpu
+
+
+def run_case(shape, dtype, compute, key, n_check=None, out_dtype=None):
+    torch = torch_cuda()
+    x = synth.gaussian(shape, key, dtype)
+    xt = to_dev(x, dtype)
+    out = torch.empty(shape, dtype=getattr(torch, {"bf16": "bfloat16", "f32": "float32"}[out_dtype or dtype]),
+                      device="cuda")
+    ns.ns_batched(xt, out, compute_dtype=compute)
+    torch.cuda.synchronize()
+    got = to_f64(out)
+    xin = storage_f64(x, dtype)
+    if len(shape) == 2:
+        return rel_fro(got, oracle.newton_schulz5(xin))
+    idx = range(shape[0]) if n_check is None else np.linspace(0, shape[0] - 1, n_check).astype(int)
+    return max(rel_fro(got[i], oracle.newton_schulz5(xin[i])) for i in idx)
+
+
+def test_c1_fp32_256():
+    # One 256 x 256 N(0,1) fp32 gradient, fp32 compute.
+    assert run_case((256, 256), "f32", "f32", (1, 0, 0, 1, 0)) <= TOL["f32"]
+
+
+def test_c1_fp32_matches_svd_closed_form():
+    torch = torch_cuda()
+    x = synth.gaussian((256, 256), (1, 0, 0, 1, 0), "f32")
+    out = ns.ns_batched(to_dev(x, "f32"), compute_dtype="f32")
+    torch.cuda.synchronize()
+    g = x.astype(np.float64)
+    u, s, vt = np.linalg.svd(g)
+    nrm = np.linalg.norm(g) + 1e-7
+    ph = s / nrm
+    for _ in range(5):
+        ph = 3.4445 * ph - 4.7750 * ph ** 3 + 2.0315 * ph ** 5
+    assert rel_fro(to_f64(out), (u * ph) @ vt) <= TOL["f32"]
+
+
+def test_c1_bf16_mode_256():
+    assert run_case((256, 256), "f32", "bf16", (1, 0, 0, 1, 0)) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("shape", [(3, 300, 520), (2, 520, 300), (2, 8, 36), (1, 384, 384), (2, 1, 5), (1, 130, 700),
+                                   (3, 257, 1000)])
+@pytest.mark.parametrize("compute", ["bf16", "f32"])
+def test_ragged_shapes(shape, compute):
+    err = run_case(shape, "bf16" if compute == "bf16" else "f32", compute, (9, shape[1], shape[2], 1, 0))
+    assert err <= TOL[compute], err
+
+
+def test_fp32_input_bf16_output():
+    assert run_case((2, 200, 330), "f32", "bf16", (9, 1, 1, 1, 0), out_dtype="bf16") <= TOL["bf16"]
+
+
+def test_zero_matrix_gives_zero():
+    torch = torch_cuda()
+    x = torch.zeros((2, 70, 90), dtype=torch.bfloat16, device="cuda")
+    x[1].normal_()
+    out = ns.ns_batched(x)
+    torch.cuda.synchronize()
+    assert torch.all(out[0] == 0).item()
+    assert torch.isfinite(out[1].float()).all().item()
+
+
+def test_in_place():
+    torch = torch_cuda()
+    x = to_dev(synth.gaussian((2, 128, 256), (9, 2, 2, 1, 0), "bf16"), "bf16")
+    ref = ns.ns_batched(x.clone())
+    ns.ns_batched(x, x)
+    torch.cuda.synchronize()
+    assert torch.equal(ref, x)
+
+
+def test_deterministic_run_twice():
+    torch = torch_cuda()
+    x = to_dev(synth.gaussian((4, 256, 640), (9, 3, 3, 1, 0), "bf16"), "bf16")
+    a = ns.ns_batched(x)
+    b = ns.ns_batched(x)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_megabatch_slice_bitwise_and_parity():
+    # Conv2d megabatch [64, 256, 128*3*3]: slice i alone == slice i of the batch.
+    torch = torch_cuda()
+    name, n, pshape = synth.conv_megabatches()[0]
+    rows, cols = pshape[0], int(np.prod(pshape[1:]))
+    x = synth.gaussian((n, rows, cols), (4, 0, 0, 1, 0), "bf16")
+    xt = to_dev(x, "bf16")
+    full = ns.ns_batched(xt)
+    singles = [ns.ns_batched(xt[i]) for i in (0, 17, 63)]
+    rev = ns.ns_batched(xt.flip(0).contiguous()).flip(0)
+    torch.cuda.synchronize()
+    for i, s in zip((0, 17, 63), singles):
+        assert torch.equal(full[i], s)
+    assert torch.equal(rev, full)
+    xin = synth.bf16_bits_to_f64(x)
+    got = to_f64(full)
+    assert max_rel_fro([got[i] for i in (0, 31, 63)], [oracle.newton_schulz5(xin[i]) for i in (0, 31, 63)]) <= TOL["bf16"]
+
+
+def test_megabatch_negative_control():
+    # The layer-mixing view [N, out*F] gives a different result from per-slice NS.
+    torch = torch_cuda()
+    x = to_dev(synth.gaussian((2, 8, 36), (4, 9, 0, 1, 0), "bf16"), "bf16")
+    right = ns.ns_batched(x)
+    wrong = ns.ns_batched(x.reshape(1, 2, 288)).reshape(2, 8, 36)
+    torch.cuda.synchronize()
+    assert rel_fro(to_f64(wrong), to_f64(right)) > 0.3
+
+
+def test_per_head_slice_bit_identical():
+    # q_proj 4096 x 4096 viewed as 32 heads of 128 rows: heads [8, 16) run alone
+    # equal the same block of the 32-head batch, bit for bit.
+    torch = torch_cuda()
+    q = to_dev(synth.gaussian((4096, 4096), (3, 0, 0, 1, 0), "bf16"), "bf16")
+    heads = ns.per_head_view(q, 32)
+    full = ns.ns_batched(heads)
+    part = ns.ns_batched(heads[8:16])
+    k = to_dev(synth.gaussian((1024, 4096), (3, 0, 1, 1, 0), "bf16"), "bf16")
+    kf = ns.ns_batched(ns.per_head_view(k, 8))
+    kp = ns.ns_batched(ns.per_head_view(k, 8)[0:8])
+    torch.cuda.synchronize()
+    assert torch.equal(full[8:16], part)
+    assert torch.equal(kf, kp)
+    xin = synth.bf16_bits_to_f64(synth.gaussian((4096, 4096), (3, 0, 0, 1, 0), "bf16"))
+    got = to_f64(full)
+    for h in (0, 13, 31):
+        assert rel_fro(got[h], oracle.newton_schulz5(xin[h * 128:(h + 1) * 128])) <= TOL["bf16"]
+
+
+def test_transpose_orientation_consistent():
+    # NS(X^T) = NS(X)^T: the tall path (transposed load and store) agrees with
+    # the wide path to rounding.
+    torch = torch_cuda()
+    x = to_dev(synth.gaussian((1, 200, 600), (9, 7, 7, 1, 0), "f32"), "f32")
+    a = ns.ns_batched(x, compute_dtype="f32")
+    b = ns.ns_batched(x.transpose(1, 2).contiguous(), compute_dtype="f32").transpose(1, 2)
+    torch.cuda.synchronize()
+    assert rel_fro(to_f64(a), to_f64(b)) < 1e-5
+
+
+def test_max_batch_chunking_bitwise():
+    torch = torch_cuda()
+    x = to_dev(synth.gaussian((5, 128, 384), (9, 8, 8, 1, 0), "bf16"), "bf16")
+    a = ns.ns_batched(x)
+    b = ns.ns_batched(x, max_batch=2)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_strided_row_views():
+    # Row stride larger than cols (a column slice of a wider tensor).
+    torch = torch_cuda()
+    big = to_dev(synth.gaussian((2, 96, 300), (9, 9, 9, 1, 0), "bf16"), "bf16")
+    view = big[:, :, 20:220]
+    out = ns.ns_batched(view)
+    ref = ns.ns_batched(view.contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)

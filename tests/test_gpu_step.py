@@ -1,0 +1,183 @@
+"""GPU parity of muon_step_group and normuon_normalize against the oracle.
+
+Compared after each step (per parameter, max over the group):
+* the weight change W_after - W_before: relative Frobenius error <= tol;
+* the momentum: within 1 bf16 ulp elementwise (bf16) or rel <= tol (fp32);
+* the NorMuon variance: relative Frobenius error <= 2 tol (it is quadratic in O);
+* the bf16 model copy: bitwise equal to RNE(GPU fp32 master).
+tol = 2e-2 in bf16 compute mode, 1e-4 in fp32 compute mode.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import TOL, bf16_ulp_diff, rel_fro, storage_f64, to_dev, to_f64, torch_cuda
+
+import newton_schulz_ns5_amd as ns
+
+pytestmark = pytest.mark.gpu
+
+
+def make_state(cfg, n, shape, gdt, mdt, key_layer=0):
+    ws = [synth.gaussian(shape, (cfg, key_layer, i, 0, synth.ROLE_WEIGHT), "f32", std=0.02) for i in range(n)]
+    return ws
+
+
+def grads_for(cfg, n, shape, gdt, step, power=False):
+    out = []
+    for i in range(n):
+        if power:
+            r = shape[0]
+            c = int(np.prod(shape[1:]))
+            g = synth.power_law((r, c), (cfg, 0, i), (cfg, 0, i, step), gdt).reshape(shape)
+        else:
+            g = synth.gaussian(shape, (cfg, 0, i, step, synth.ROLE_GRAD), gdt)
+        out.append(g)
+    return out
+
+
+def run_steps(shape, n, gdt, mdt, compute, steps=2, normuon=False, heads=1, model_copy=False, power=False,
+              cfg_id=7, lr=0.05, wd=0.0, check=None):
+    torch = torch_cuda()
+    w0 = make_state(cfg_id, n, shape, gdt, mdt)
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}
+    W = [to_dev(w, "f32") for w in w0]
+    M = [torch.zeros(shape, dtype=tdt[mdt], device="cuda") for _ in range(n)]
+    V = [torch.zeros(shape[0], dtype=torch.float32, device="cuda") for _ in range(n)] if normuon else None
+    WM = [torch.zeros(shape, dtype=torch.bfloat16, device="cuda") for _ in range(n)] if model_copy else None
+    # oracle state
+    ow = [w.astype(np.float64) for w in w0]
+    om = [np.zeros(shape) for _ in range(n)]
+    ov = [np.zeros(shape[0]) for _ in range(n)]
+    hp = oracle.MuonHParams(lr=lr, weight_decay=wd, heads=heads, normuon=normuon, mom_dtype=mdt)
+    tol = TOL[compute]
+    check = list(range(n)) if check is None else check
+    for step in range(1, steps + 1):
+        g = grads_for(cfg_id, n, shape, gdt, step, power)
+        G = [to_dev(x, gdt) for x in g]
+        before = [to_f64(w) for w in W]
+        ns.step_group(W, G, M, V, WM, heads=heads, lr=lr, weight_decay=wd, normuon=normuon,
+                      ns=ns.ns_config(compute_dtype=compute))
+        torch.cuda.synchronize()
+        for i in check:
+            r = oracle.muon_step(ow[i], storage_f64(g[i], gdt), om[i], ov[i], hp)
+            w_gpu = to_f64(W[i])
+            dw_err = rel_fro(w_gpu - before[i], r["w"] - ow[i])
+            assert dw_err <= tol, (step, i, dw_err)
+            m_gpu = to_f64(M[i])
+            if mdt == "bf16":
+                assert bf16_ulp_diff(m_gpu, r["m"]).max() <= 1, (step, i)
+            else:
+                assert rel_fro(m_gpu, r["m"]) <= max(tol, 1e-6), (step, i)
+            if normuon:
+                assert rel_fro(to_f64(V[i]), r["v"]) <= 2 * tol, (step, i)
+            if model_copy:
+                want = synth.f64_to_bf16_bits(w_gpu)
+                got = WM[i].cpu().view(torch.int16).numpy().view(np.uint16)
+                assert np.array_equal(got, want), (step, i)
+            ow[i], om[i] = r["w"], r["m"]
+            if normuon:
+                ov[i] = r["v"]
+    return W, M, V
+
+
+def test_c1_fp32_two_steps():
+    # 256 x 256 fp32 gradient, momentum 0.95 Nesterov, lr 0.05, fp32 compute.
+    run_steps((256, 256), 1, "f32", "f32", "f32", steps=2)
+
+
+def test_c1_bf16_compute_two_steps():
+    run_steps((256, 256), 1, "f32", "f32", "bf16", steps=2)
+
+
+@pytest.mark.parametrize("compute", ["bf16", "f32"])
+def test_ragged_group_normuon(compute):
+    run_steps((300, 130), 3, "bf16" if compute == "bf16" else "f32", "bf16" if compute == "bf16" else "f32",
+              compute, steps=2, normuon=True, model_copy=True)
+
+
+def test_tall_and_wide_groups():
+    run_steps((520, 200), 2, "bf16", "bf16", "bf16", steps=2)
+    run_steps((200, 520), 2, "bf16", "bf16", "bf16", steps=2, normuon=True)
+
+
+def test_conv_p1_shapes_tail():
+    # Two (8, 4, 3, 3) convolutions, the megabatch of the flattening fix.
+    run_steps((8, 4, 3, 3), 2, "bf16", "bf16", "bf16", steps=2, normuon=True, model_copy=True)
+
+
+def test_per_head_step():
+    run_steps((256, 384), 2, "bf16", "bf16", "bf16", steps=2, heads=4)
+
+
+def test_weight_decay_and_gate_shape_lr():
+    # fan_out / fan_in = 3.5 > 1 scales lr by sqrt(3.5).
+    run_steps((448, 128), 1, "bf16", "bf16", "bf16", steps=1, wd=0.1)
+
+
+def test_c4_conv_megabatches_normuon_two_steps():
+    # Conv2d [64, 256, 128, 3, 3] and Conv1d [32, 512, 512, 5], bf16 power-law
+    # gradients, bf16 momentum, fp32 master, NorMuon beta2 0.95 eps 1e-8.
+    for name, n, shape in synth.conv_megabatches():
+        run_steps(shape, n, "bf16", "bf16", "bf16", steps=2, normuon=True, power=True, cfg_id=4,
+                  check=[0, n // 2, n - 1], model_copy=True)
+
+
+def test_conv_equals_reshaped_linear_bitwise():
+    torch = torch_cuda()
+    shape = (8, 4, 3, 3)
+    g = [to_dev(x, "bf16") for x in grads_for(5, 2, shape, "bf16", 1)]
+    w = [to_dev(x, "f32") for x in make_state(5, 2, shape, "bf16", "bf16")]
+    w2 = [t.clone().reshape(8, 36) for t in w]
+    m = [torch.zeros(shape, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    m2 = [torch.zeros((8, 36), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    v = [torch.zeros(8, device="cuda") for _ in range(2)]
+    v2 = [torch.zeros(8, device="cuda") for _ in range(2)]
+    ns.step_group(w, g, m, v, normuon=True)
+    ns.step_group(w2, [t.reshape(8, 36) for t in g], m2, v2, normuon=True)
+    torch.cuda.synchronize()
+    for a, b in zip(w, w2):
+        assert torch.equal(a.reshape(8, 36), b)
+    for a, b in zip(v, v2):
+        assert torch.equal(a, b)
+
+
+def test_group_size_invariance_bitwise():
+    # A parameter steps identically alone and inside a group of 5.
+    torch = torch_cuda()
+    shape = (256, 512)
+    g = [to_dev(x, "bf16") for x in grads_for(6, 5, shape, "bf16", 1)]
+    w = [to_dev(x, "f32") for x in make_state(6, 5, shape, "bf16", "bf16")]
+    wa = [t.clone() for t in w]
+    m = [torch.zeros(shape, dtype=torch.bfloat16, device="cuda") for _ in range(5)]
+    ma = [t.clone() for t in m]
+    ns.step_group(w, g, m)
+    ns.step_group([wa[3]], [g[3]], [ma[3]])
+    torch.cuda.synchronize()
+    assert torch.equal(w[3], wa[3]) and torch.equal(m[3], ma[3])
+
+
+def test_normuon_normalize_parity():
+    torch = torch_cuda()
+    n, rows, cols = 3, 96, 200
+    o = synth.gaussian((n, rows, cols), (8, 0, 0, 1, 0), "f32") * np.linspace(0.5, 2, rows)[None, :, None]
+    o = o.astype(np.float32)
+    v0 = np.abs(synth.gaussian((n, rows), (8, 0, 1, 1, 0), "f32")).astype(np.float32) * 0.01
+    ot = to_dev(o, "f32")
+    vt = to_dev(v0, "f32")
+    ns.normuon_normalize(ot, vt, beta2=0.95, eps=1e-8)
+    torch.cuda.synchronize()
+    got, gv = to_f64(ot), to_f64(vt)
+    for i in range(n):
+        ref, rv = oracle.normuon(o[i].astype(np.float64), v0[i].astype(np.float64), 0.95, 1e-8)
+        assert rel_fro(got[i], ref) <= 1e-5
+        assert rel_fro(gv[i], rv) <= 1e-5
+
+
+def test_empty_group_is_noop():
+    torch = torch_cuda()
+    w = [torch.zeros((0, 16), device="cuda")]
+    ns.step_group(w, [torch.zeros((0, 16), dtype=torch.bfloat16, device="cuda")],
+                  [torch.zeros((0, 16), dtype=torch.bfloat16, device="cuda")])
+    torch.cuda.synchronize()
