@@ -81,15 +81,37 @@ def status_name(status):
             -3: "MUON_ERR_WORKSPACE", -4: "MUON_ERR_HIP"}.get(status, "MUON_ERR_?")
 
 
+def _hip_runtimes_mapped():
+    try:
+        maps = open("/proc/self/maps").read()
+    except OSError:
+        return []
+    return sorted({line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line})
+
+
 def lib():
-    """The loaded library.  Raises if it has not been built."""
+    """The loaded library.  Raises if it has not been built.
+
+    PyTorch ships its own HIP runtime.  The library is loaded after torch so
+    that its libamdhip64.so.7 dependency resolves (by soname) to the runtime
+    torch already holds: one process, one HIP runtime, so device pointers and
+    streams from torch are valid in the library.  Two runtimes in one process
+    are refused.
+    """
     global _LIB
     if _LIB is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(
                 f"{LIB_PATH} is missing: build it with `python -m newton_schulz_ns5_amd.build` "
                 "(there is no fallback implementation)")
+        try:
+            import torch  # noqa: F401  (binds the HIP runtime first)
+        except ImportError:
+            pass
         h = ctypes.CDLL(LIB_PATH)
+        runtimes = _hip_runtimes_mapped()
+        if len(runtimes) > 1:
+            raise RuntimeError(f"two HIP runtimes are loaded in this process: {runtimes}")
         for name, (res, args) in SIGNATURES.items():
             f = getattr(h, name)
             f.restype = res

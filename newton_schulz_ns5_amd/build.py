@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libmuon_mi355x.so")
 SOURCES = ["gemm_bf16.hip", "gemm_f32.hip", "elementwise.hip", "muon_host.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "--offload-arch=gfx950", "-mcode-object-version=5", "-O3", "-std=c++17", "-fPIC",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
@@ -43,7 +43,8 @@ def build(verbose=False):
         if verbose and err.strip():
             print(err, file=sys.stderr)
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *[o for o, _ in results]]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-mcode-object-version=5", "-shared", "-fPIC", "-o", tmp,
+           *[o for o, _ in results]]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)

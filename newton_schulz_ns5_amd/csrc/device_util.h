@@ -44,4 +44,12 @@ __device__ __forceinline__ void store_elem(void* base, int64_t idx, float v, boo
   else ((float*)base)[idx] = v;
 }
 
+// Launch a kernel taking one parameter block by value, 256 threads per
+// workgroup; returns the launch's own status.
+template <typename P>
+inline hipError_t launch_kernel(void (*kernel)(const P), dim3 grid, const P& p, hipStream_t s) {
+  void* args[] = {const_cast<P*>(&p)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, dim3(256), args, 0, s);
+}
+
 }  // namespace muon

@@ -301,32 +301,27 @@ __global__ __launch_bounds__(256) void apply_kernel(const ApplyParams p) {
 
 hipError_t launch_prep(const PrepParams& p, int nb, hipStream_t s) {
   if (nb <= 0) return hipSuccess;
-  hipLaunchKernelGGL(prep_kernel, dim3(p.np / kPrepTile, p.mp / kPrepTile, nb), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return launch_kernel(prep_kernel, dim3(p.np / kPrepTile, p.mp / kPrepTile, nb), p, s);
 }
 
 hipError_t launch_norm(const NormParams& p, int nb, hipStream_t s) {
   if (nb <= 0) return hipSuccess;
-  hipLaunchKernelGGL(norm_kernel, dim3(nb), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return launch_kernel(norm_kernel, dim3(nb), p, s);
 }
 
 hipError_t launch_rowstat(const RowStatParams& p, int nb, hipStream_t s) {
   if (nb <= 0 || p.rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rowstat_kernel, dim3((p.rows + 3) / 4, nb), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return launch_kernel(rowstat_kernel, dim3((p.rows + 3) / 4, nb), p, s);
 }
 
 hipError_t launch_rho(const RhoParams& p, int nb, hipStream_t s) {
   if (nb <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rho_kernel, dim3(nb), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return launch_kernel(rho_kernel, dim3(nb), p, s);
 }
 
 hipError_t launch_apply(const ApplyParams& p, int nb, hipStream_t s) {
   if (nb <= 0 || p.rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(apply_kernel, dim3((p.rows + 3) / 4, nb), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return launch_kernel(apply_kernel, dim3((p.rows + 3) / 4, nb), p, s);
 }
 
 }  // namespace muon

@@ -245,8 +245,7 @@ template <int BM, int BN, bool NN, bool SYRK>
 hipError_t launch_one(const GemmParams& p, hipStream_t s) {
   const int64_t grid = (int64_t)p.batch * p.tiles_per_batch;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, NN, SYRK>), dim3((unsigned)grid), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return launch_kernel(gemm_bf16_kernel<BM, BN, NN, SYRK>, dim3((unsigned)grid), p, s);
 }
 
 }  // namespace

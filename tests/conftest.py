@@ -3,6 +3,13 @@ import sys
 
 import pytest
 
+try:
+    # torch first: the HIP library then binds to torch's HIP runtime (one
+    # runtime per process), whatever order the test modules load it in.
+    import torch  # noqa: F401
+except ImportError:
+    pass
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)

@@ -31,7 +31,7 @@ def test_header_declares_the_expected_entry_points():
 
 
 def test_library_exports_every_header_function():
-    h = ctypes.CDLL(_lib.LIB_PATH)
+    h = m.lib()
     missing = [n for n in header_functions() if not hasattr(h, n)]
     assert not missing, missing
     assert set(header_functions()) == set(_lib.SIGNATURES), "binding signatures drifted from the header"
@@ -75,6 +75,15 @@ def test_ctypes_structs_match_c_layout():
             assert getattr(py, fname).offset == lay[f"{cname}.{fname}"], (cname, fname)
 
 
+def test_one_hip_runtime_per_process():
+    # The library must bind to the HIP runtime torch already holds; two
+    # runtimes in one process do not see each other's streams or work.
+    m.lib()
+    import sys
+    assert "torch" in sys.modules
+    assert len(_lib._hip_runtimes_mapped()) == 1, _lib._hip_runtimes_mapped()
+
+
 def test_versions_and_status_strings():
     L = m.lib()
     assert L.muon_abi_version() == 1 and L.muon_state_layout_version() == 1
@@ -97,7 +106,9 @@ FAKE = 1 << 20  # a non-null, 256-aligned address that is never dereferenced
 
 def ns_call(**over):
     a = dict(x=FAKE, xd=1, xbs=64 * 64, xrs=64, y=FAKE, yd=1, ybs=64 * 64, yrs=64, n=1, rows=64, cols=64,
-             cfg=m.ns_config(), ws=FAKE, wsb=1 << 40)
+             ws=FAKE, wsb=1 << 40)
+    cfg_kw = over.pop("cfg_kw", {})
+    a["cfg"] = over.pop("cfg") if "cfg" in over else m.ns_config(**cfg_kw)
     a.update(over)
     L = m.lib()
     return L.muon_ns_batched(ctypes.c_void_p(a["x"]), a["xd"], a["xbs"], a["xrs"], ctypes.c_void_p(a["y"]), a["yd"],
@@ -109,7 +120,7 @@ def ns_call(**over):
 @pytest.mark.parametrize("over,code", [
     (dict(x=0), -1), (dict(y=0), -1), (dict(ws=0), -1), (dict(ws=FAKE + 16), -1),
     (dict(n=-1), -1), (dict(rows=-3), -1), (dict(xrs=10), -1), (dict(yrs=63), -1), (dict(xbs=-1), -1),
-    (dict(xd=7), -2), (dict(yd=2), -2), (dict(cfg=m.ns_config(steps=0)), -1), (dict(cfg=m.ns_config(steps=65)), -1),
+    (dict(xd=7), -2), (dict(yd=2), -2), (dict(cfg_kw=dict(steps=0)), -1), (dict(cfg_kw=dict(steps=65)), -1),
     (dict(cfg=None), -1), (dict(wsb=100), -3), (dict(n=2, ybs=10), -1), (dict(x=FAKE + 1), -1),
     (dict(rows=1 << 25), -1),
 ])
