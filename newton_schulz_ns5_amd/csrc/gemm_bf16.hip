@@ -69,8 +69,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const GemmParams p) {
   constexpr int PL = BM * BK / 8 / 256;          // 16-byte P chunks per thread
   constexpr int QL = NN ? 8 : BN * BK / 8 / 256;  // Q chunks per thread
   constexpr int NB8 = BN / 8;                     // NN: 8x8 blocks along N (x 8 along K)
-  __shared__ __attribute__((aligned(16))) uint16_t Ps[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BN * LDK];
+  constexpr int PS = BM * LDK, QS = BN * LDK;     // one LDS stage of P / Q, in bf16 elements
+  constexpr int RH = BM / 2;                      // epilogue: tile rows staged per pass
+  constexpr int RP = RH + 1;                      // epilogue: odd LDS pitch (floats)
+  static_assert(BN * RP * 4 <= 2 * (PS + QS) * 2, "epilogue staging must fit in the main-loop LDS");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (PS + QS)];
+  uint16_t* const Ps = smem;            // [2][BM][LDK]
+  uint16_t* const Qs = smem + 2 * PS;   // [2][BN][LDK]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -108,10 +113,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const GemmParams p) {
   };
 
   auto sstore = [&](int s) {
+    uint16_t* const ps = Ps + s * PS;
+    uint16_t* const qs = Qs + s * QS;
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
       const int c = tid + 256 * i, row = c >> 3, kc = c & 7;
-      *(u32x4*)(&Ps[s][row * LDK + kc * 8]) = pr[i];
+      *(u32x4*)(ps + row * LDK + kc * 8) = pr[i];
     }
     if constexpr (NN) {
       if (q_active) {
@@ -126,14 +133,14 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const GemmParams p) {
             const uint32_t lo = qr[2 * h][w], hi = qr[2 * h + 1][w];
             o[h] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
           }
-          *(u32x4*)(&Qs[s][(nb * 8 + i) * LDK + kb * 8]) = o;
+          *(u32x4*)(qs + (nb * 8 + i) * LDK + kb * 8) = o;
         }
       }
     } else {
 #pragma unroll
       for (int i = 0; i < QL; ++i) {
         const int c = tid + 256 * i, row = c >> 3, kc = c & 7;
-        *(u32x4*)(&Qs[s][row * LDK + kc * 8]) = qr[i];
+        *(u32x4*)(qs + row * LDK + kc * 8) = qr[i];
       }
     }
   };
@@ -148,24 +155,35 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const GemmParams p) {
 
   // MFMA operand layout (32x32x16): lane l supplies row (l % 32) of the A
   // block and column (l % 32) of the B block, each with the 8 K values
-  // 8 (l / 32) .. 8 (l / 32) + 7 of the 16-wide K step.
+  // 8 (l / 32) .. 8 (l / 32) + 7 of the 16-wide K step.  Fragments of the
+  // next K step are read from LDS while the MFMAs of the current one run.
   auto compute = [&](int s) {
-    const uint16_t* pa = &Ps[s][(wm * WM + (lane & 31)) * LDK + (lane >> 5) * 8];
-    const uint16_t* qa = &Qs[s][(wn * WN + (lane & 31)) * LDK + (lane >> 5) * 8];
+    const uint16_t* pa = Ps + s * PS + (wm * WM + (lane & 31)) * LDK + (lane >> 5) * 8;
+    const uint16_t* qa = Qs + s * QS + (wn * WN + (lane & 31)) * LDK + (lane >> 5) * 8;
+    bf16x8 af[2][FM], bq[2][FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) af[0][fm] = __builtin_bit_cast(bf16x8, *(const u32x4*)(pa + fm * 32 * LDK));
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) bq[0][fn] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qa + fn * 32 * LDK));
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[FM], bq[FN];
+      const int cur = ks & 1;
+      if (ks + 1 < BK / 16) {
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-        af[fm] = __builtin_bit_cast(bf16x8, *(const u32x4*)(pa + fm * 32 * LDK + ks * 16));
+        for (int fm = 0; fm < FM; ++fm)
+          af[cur ^ 1][fm] = __builtin_bit_cast(bf16x8, *(const u32x4*)(pa + fm * 32 * LDK + (ks + 1) * 16));
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-        bq[fn] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qa + fn * 32 * LDK + ks * 16));
+        for (int fn = 0; fn < FN; ++fn)
+          bq[cur ^ 1][fn] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qa + fn * 32 * LDK + (ks + 1) * 16));
+      }
+      // Keep the reads of step ks+1 ahead of the MFMAs of step ks.
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bq[fn], acc[fm][fn], 0, 0, 0);
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][fm], bq[cur][fn], acc[fm][fn], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -181,63 +199,65 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const GemmParams p) {
     __syncthreads();
   }
 
-  // Epilogue.  Accumulator register r of a 32x32 block holds row
-  // 8 (r / 4) + 4 (l / 32) + (r % 4), column l % 32.
+  // ---- epilogue --------------------------------------------------------------
+  // Accumulator register r of a 32x32 block holds row 8 (r / 4) + 4 (l / 32)
+  // + (r % 4) and column l % 32.  The tile is staged through LDS in two
+  // passes of BM/2 rows (the waves with wm == pass write theirs) as
+  // S[col][row] fp32 with an odd pitch; all register indices are compile-time
+  // constants.  A cooperative loop then applies alpha, beta * D and the
+  // rounding, and writes C row-major (consecutive threads -> consecutive
+  // columns) and/or transposed (consecutive threads -> consecutive rows).
+  float* const S = reinterpret_cast<float*>(smem);
   const float rsb = p.rs ? p.rs[b] : 1.f;
   const float alpha = p.alpha * (p.alpha_pow == 2 ? rsb * rsb : (p.alpha_pow == 1 ? rsb : 1.f));
   const float beta = p.beta * (p.beta_pow == 1 ? rsb : 1.f);
   const uint16_t* Dg = p.D ? (const uint16_t*)p.D + (int64_t)b * p.sD : nullptr;
-  const int i_base = tm * BM + wm * WM + (lane >> 5) * 4;
-  const int j_base = tn * BN + wn * WN + (lane & 31);
+  const bool obf = SYRK || p.c_dtype == MUON_BF16;
+  uint8_t* const Cg = (uint8_t*)p.C + (int64_t)b * p.sC * (obf ? 2 : 4);
+  const bool do_rows = SYRK || !p.c_trans;
+  const bool do_trans = SYRK || p.c_trans;
+  const int Mlim = SYRK ? p.M : p.Mreal, Nlim = SYRK ? p.N : p.Nreal;
 
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
+  for (int pass = 0; pass < 2; ++pass) {
+    if (wm == pass) {
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      const int j = j_base + fn * 32;
+      for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int ib = i_base + fm * 32 + g * 8;
-        float v[4];
+        for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[e] = alpha * acc[fm][fn][4 * g + e];
-          if (Dg) v[e] += beta * bf2f(Dg[(int64_t)(ib + e) * p.ldd + j]);
-        }
-        if constexpr (SYRK) {
-          uint16_t* Cg = (uint16_t*)p.C + (int64_t)b * p.sC;
-          if (tm < tn) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Cg[(int64_t)(ib + e) * p.ldc + j] = f2bf(v[e]);
-            u32x2 t2;
-            t2[0] = pack_bf2(v[0], v[1]);
-            t2[1] = pack_bf2(v[2], v[3]);
-            *(u32x2*)(Cg + (int64_t)j * p.ldc + ib) = t2;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int i = ib + e;
-              const uint16_t h = f2bf(v[e]);
-              if (i <= j) Cg[(int64_t)i * p.ldc + j] = h;
-              if (i < j) Cg[(int64_t)j * p.ldc + i] = h;
-            }
+          for (int r = 0; r < 16; ++r) {
+            const int row = fm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            const int col = wn * WN + fn * 32 + (lane & 31);
+            S[col * RP + row] = acc[fm][fn][r];
           }
-        } else {
-          const bool obf = p.c_dtype == MUON_BF16;
-          uint8_t* Cg = (uint8_t*)p.C + (int64_t)b * p.sC * (obf ? 2 : 4);
-          if (j < p.Nreal) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int i = ib + e;
-              if (i < p.Mreal) {
-                const int64_t idx = p.c_trans ? (int64_t)j * p.ldc + i : (int64_t)i * p.ldc + j;
-                store_elem(Cg, idx, v[e], obf);
-              }
-            }
-          }
-        }
+    }
+    __syncthreads();
+    const int i0 = tm * BM + pass * RH;
+    const int j0 = tn * BN;
+    {  // row-major pass: thread -> column, loop over rows
+      constexpr int TPC = 256 / BN;  // threads per column
+      const int jj = tid % BN, rsub = tid / BN;
+      const int j = j0 + jj;
+      for (int rr = rsub; rr < RH; rr += TPC) {
+        const int i = i0 + rr;
+        float v = alpha * S[jj * RP + rr];
+        if (Dg) v += beta * bf2f(Dg[(int64_t)i * p.ldd + j]);
+        S[jj * RP + rr] = v;
+        if (do_rows && i < Mlim && j < Nlim && (!SYRK || tm < tn || i <= j))
+          store_elem(Cg, (int64_t)i * p.ldc + j, v, obf);
       }
     }
+    if (do_trans) {
+      __syncthreads();
+      for (int idx = tid; idx < RH * BN; idx += 256) {
+        const int rr = idx % RH, jj = idx / RH;
+        const int i = i0 + rr, j = j0 + jj;
+        if (i < Mlim && j < Nlim && (!SYRK || tm < tn || i < j))
+          store_elem(Cg, (int64_t)j * p.ldc + i, S[jj * RP + rr], obf);
+      }
+    }
+    __syncthreads();
   }
 }
 

@@ -2,7 +2,9 @@
 
 Compared after each step (per parameter, max over the group):
 * the weight change W_after - W_before: relative Frobenius error <= tol;
-* the momentum: within 1 bf16 ulp elementwise (bf16) or rel <= tol (fp32);
+* the momentum: elementwise within 1 bf16 ulp, or within 2^-20 (|mu m_prev| + |g|)
+  where the update cancels (the ABI carries mu as the float 0.95f, so an exact
+  fp64 zero comes out as ~1e-8 on the GPU); fp32 momentum: rel <= tol;
 * the NorMuon variance: relative Frobenius error <= 2 tol (it is quadratic in O);
 * the bf16 model copy: bitwise equal to RNE(GPU fp32 master).
 tol = 2e-2 in bf16 compute mode, 1e-4 in fp32 compute mode.
@@ -67,7 +69,16 @@ def run_steps(shape, n, gdt, mdt, compute, steps=2, normuon=False, heads=1, mode
             assert dw_err <= tol, (step, i, dw_err)
             m_gpu = to_f64(M[i])
             if mdt == "bf16":
-                assert bf16_ulp_diff(m_gpu, r["m"]).max() <= 1, (step, i)
+                diff = bf16_ulp_diff(m_gpu, r["m"])
+                gin = storage_f64(g[i], gdt)
+                scale = 0.95 * np.abs(om[i]) + np.abs(gin)
+                off = (diff > 1) & (np.abs(m_gpu - r["m"]) > 2.0 ** -20 * scale)
+                if off.any():
+                    bad = np.argwhere(off)
+                    info = [(tuple(int(t) for t in ix), m_gpu[tuple(ix)], r["m"][tuple(ix)], om[i][tuple(ix)],
+                             gin[tuple(ix)]) for ix in bad[:6]]
+                    raise AssertionError(f"momentum step {step} param {i}: {len(bad)} elements off by >1 ulp; "
+                                         f"(index, gpu, oracle, previous m, grad): {info}")
             else:
                 assert rel_fro(m_gpu, r["m"]) <= max(tol, 1e-6), (step, i)
             if normuon:
