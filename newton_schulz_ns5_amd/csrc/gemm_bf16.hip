@@ -2,20 +2,26 @@
 //
 // The three products of an iteration ("core.optimizer.layer_sharded_muon",
 // LayerShardedMuon, use_syrk: A = X X^T and B = b A + c A^2 are symmetric and
-// need one triangle only; the update X <- a X + B X is a full product):
+// need one triangle only; the update X <- a X + B X is a full product) are
+// all computed here in "NT" form, C = alpha P Q^T + beta D, with both operands
+// stored K-contiguous:
 //
-//   Gram   A = alpha X X^T        NT, SYRK (upper tiles, mirrored store)
-//   Poly   B = c A A + b A        NT, SYRK (A symmetric, so A A = A A^T)
-//   Update X' = B X + a X         NN (X is [K][N]; transposed on its way to LDS)
+//   Gram   A  = alpha X X^T       P = Q = X,          SYRK
+//   Poly   B  = c A A + b A       P = Q = A (A = A^T), SYRK, D = A
+//   Update X' = B X + a X         P = B, Q = X^T,     D = X, writes X' and X'^T
 //
-// One kernel template serves all three.  A workgroup of 256 threads (four
-// wave64s in a 2x2 arrangement) owns a BM x BN output tile; each wave owns a
-// (BM/2) x (BN/2) sub-tile made of 32x32 blocks computed with
-// v_mfma_f32_32x32x16_bf16 (fp32 accumulation).  K advances in steps of 64
-// through two LDS stages: the next K slice is fetched from HBM into registers
-// while the current one feeds the MFMAs, then written to the other stage.
-// LDS rows are padded by 16 bytes so that the 16-byte fragment reads of 16
-// consecutive rows fall in distinct banks.
+// The update writes its result both row-major and transposed, so the next
+// update reads X^T without any transpose in its main loop.
+//
+// Work decomposition: one workgroup of 256 threads (four wave64s, 2 x 2) per
+// BT x BT output tile (BT = 256 or 128); each wave owns a (BT/2)^2 sub-tile of
+// 32x32 blocks computed with v_mfma_f32_32x32x16_bf16 (fp32 accumulation in
+// AGPRs).  K advances 32 at a time through a ring of four LDS stages filled by
+// direct HBM -> LDS buffer loads (buffer_load_dwordx4 ... lds): no registers
+// hold prefetched data, and about two stages of loads are in flight while a
+// third is multiplied.  Each LDS row holds 32 bf16 (64 bytes) of one operand
+// row; its four 16-byte chunks are XOR-swizzled by bits 1-2 of the row index,
+// so the 16-byte fragment reads of eight consecutive rows hit distinct banks.
 //
 // Every output tile is computed by the same instruction sequence whatever the
 // batch size or the tile's position, so a matrix's result is bitwise
@@ -30,8 +36,18 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BK = 64;
-constexpr int LDK = BK + 8;  // padded LDS row, in bf16 elements (144 bytes)
+#define MUON_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+constexpr int KS = 32;        // K per LDS stage
+constexpr int NSTAGE = 4;     // LDS ring depth
+constexpr int ROWB = KS * 2;  // bytes per LDS row
+
+// s_waitcnt with only a vector-memory count (expcnt and lgkmcnt left open).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
 // Workgroup -> (batch, tile row, tile col).
 //
@@ -62,20 +78,29 @@ __device__ __forceinline__ void decode_tile(const GemmParams& p, int& b, int& tm
   }
 }
 
-template <int BM, int BN, bool NN, bool SYRK>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const GemmParams p) {
-  constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int FM = WM / 32, FN = WN / 32;
-  constexpr int PL = BM * BK / 8 / 256;          // 16-byte P chunks per thread
-  constexpr int QL = NN ? 8 : BN * BK / 8 / 256;  // Q chunks per thread
-  constexpr int NB8 = BN / 8;                     // NN: 8x8 blocks along N (x 8 along K)
-  constexpr int PS = BM * LDK, QS = BN * LDK;     // one LDS stage of P / Q, in bf16 elements
-  constexpr int RH = BM / 2;                      // epilogue: tile rows staged per pass
-  constexpr int RP = RH + 1;                      // epilogue: odd LDS pitch (floats)
-  static_assert(BN * RP * 4 <= 2 * (PS + QS) * 2, "epilogue staging must fit in the main-loop LDS");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (PS + QS)];
-  uint16_t* const Ps = smem;            // [2][BM][LDK]
-  uint16_t* const Qs = smem + 2 * PS;   // [2][BN][LDK]
+// Buffer descriptor of a panel: base address and size in bytes, both made
+// explicitly wave-uniform so the descriptor lives in SGPRs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, n, 0x00020000);
+}
+
+template <int BT, bool SYRK>
+__global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmParams p) {
+  constexpr int WT = BT / 2;          // wave tile edge
+  constexpr int F = WT / 32;          // 32x32 MFMA blocks per wave tile edge
+  constexpr int OPB = BT * ROWB;      // bytes of one operand in one stage
+  constexpr int STB = 2 * OPB;        // bytes of one stage
+  constexpr int RPW = BT / 4;         // operand rows loaded by each wave per stage
+  constexpr int DPW = RPW / 16;       // DMA instructions per wave per operand per stage
+  constexpr int DPT = 2 * DPW;        // DMA instructions per wave per stage
+  constexpr int RH = BT / 2;          // epilogue: tile rows staged per pass
+  constexpr int EPI = RH * (BT + 4) * 4;  // epilogue staging bytes
+  constexpr int LDS_BYTES = (NSTAGE * STB > EPI) ? NSTAGE * STB : EPI;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -83,200 +108,258 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const GemmParams p) {
   int b, tm, tn;
   decode_tile<SYRK>(p, b, tm, tn);
 
-  const uint16_t* Pg = (const uint16_t*)p.P + (int64_t)b * p.sP + (int64_t)tm * BM * p.ldp;
-  const uint16_t* Qg = NN ? (const uint16_t*)p.Q + (int64_t)b * p.sQ + (int64_t)tn * BN
-                          : (const uint16_t*)p.Q + (int64_t)b * p.sQ + (int64_t)tn * BN * p.ldq;
+  const int ldp = __builtin_amdgcn_readfirstlane((int)p.ldp);
+  const int ldq = __builtin_amdgcn_readfirstlane((int)p.ldq);
+  const uint16_t* Pg = (const uint16_t*)p.P + (int64_t)b * p.sP + (int64_t)tm * BT * p.ldp;
+  const uint16_t* Qg = (const uint16_t*)p.Q + (int64_t)b * p.sQ + (int64_t)tn * BT * p.ldq;
+  const __amdgpu_buffer_rsrc_t prs = make_rsrc(Pg, (int64_t)BT * p.ldp * 2);
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Qg, (int64_t)BT * p.ldq * 2);
 
-  u32x4 pr[PL], qr[QL];
-  const int kb = tid & 7, nb = tid >> 3;  // NN: this thread's 8x8 block (k block, n block)
-  const bool q_active = !NN || nb < NB8;
+  // DMA: instruction j of a wave fills LDS rows wave*RPW + 16 j .. +15 of an
+  // operand; lane l lands at row (l / 4), slot (l % 4) and therefore fetches
+  // the global chunk slot ^ swizzle(row) = (l & 3) ^ ((l >> 3) & 3).
+  const int dkc = (lane & 3) ^ ((lane >> 3) & 3);
+  const int prow = wave * RPW + (lane >> 2);
+  const int pvo = prow * ldp * 2 + dkc * 16;
+  const int qvo = prow * ldq * 2 + dkc * 16;
 
-  auto gload = [&](int k0) {
+  auto issue = [&](int t) {  // K slice t -> stage t % NSTAGE
+    uint8_t* const st = smem + (t % NSTAGE) * STB;
+    const int k0b = t * KS * 2;
 #pragma unroll
-    for (int i = 0; i < PL; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, kc = c & 7;
-      pr[i] = *(const u32x4*)(Pg + (int64_t)row * p.ldp + k0 + kc * 8);
-    }
-    if constexpr (NN) {
-      if (q_active) {
+    for (int j = 0; j < DPW; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, MUON_LDS(st + (wave * RPW + 16 * j) * ROWB), 16, pvo,
+                                               16 * j * ldp * 2 + k0b, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          qr[j] = *(const u32x4*)(Qg + (int64_t)(k0 + kb * 8 + j) * p.ldq + nb * 8);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < QL; ++i) {
-        const int c = tid + 256 * i, row = c >> 3, kc = c & 7;
-        qr[i] = *(const u32x4*)(Qg + (int64_t)row * p.ldq + k0 + kc * 8);
-      }
-    }
+    for (int j = 0; j < DPW; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, MUON_LDS(st + OPB + (wave * RPW + 16 * j) * ROWB), 16, qvo,
+                                               16 * j * ldq * 2 + k0b, 0, 0);
   };
-
-  auto sstore = [&](int s) {
-    uint16_t* const ps = Ps + s * PS;
-    uint16_t* const qs = Qs + s * QS;
-#pragma unroll
-    for (int i = 0; i < PL; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, kc = c & 7;
-      *(u32x4*)(ps + row * LDK + kc * 8) = pr[i];
-    }
-    if constexpr (NN) {
-      if (q_active) {
-        // qr[j] holds Q[k0 + 8 kb + j][8 nb .. 8 nb + 7]; write column 8 nb + i
-        // of the tile as the K-contiguous LDS row Qs[8 nb + i][8 kb .. 8 kb + 7].
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int w = i >> 1;
-          u32x4 o;
-#pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            const uint32_t lo = qr[2 * h][w], hi = qr[2 * h + 1][w];
-            o[h] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-          }
-          *(u32x4*)(qs + (nb * 8 + i) * LDK + kb * 8) = o;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < QL; ++i) {
-        const int c = tid + 256 * i, row = c >> 3, kc = c & 7;
-        *(u32x4*)(qs + row * LDK + kc * 8) = qr[i];
-      }
-    }
+  // Wait until at most n stages (of this wave's DMA) are still in flight.
+  auto wait_stages = [&](int n) {
+    if (n >= 2) wait_vmcnt<2 * DPT>();
+    else if (n == 1) wait_vmcnt<DPT>();
+    else wait_vmcnt<0>();
   };
-
-  f32x16 acc[FM][FN];
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.f;
 
   // MFMA operand layout (32x32x16): lane l supplies row (l % 32) of the A
   // block and column (l % 32) of the B block, each with the 8 K values
-  // 8 (l / 32) .. 8 (l / 32) + 7 of the 16-wide K step.  Fragments of the
-  // next K step are read from LDS while the MFMAs of the current one run.
-  auto compute = [&](int s) {
-    const uint16_t* pa = Ps + s * PS + (wm * WM + (lane & 31)) * LDK + (lane >> 5) * 8;
-    const uint16_t* qa = Qs + s * QS + (wn * WN + (lane & 31)) * LDK + (lane >> 5) * 8;
-    bf16x8 af[2][FM], bq[2][FN];
+  // 8 (l / 32) .. 8 (l / 32) + 7 of the 16-wide K step.  Rows of a block start
+  // at multiples of 32, so a row's swizzle depends on l only.
+  const int fsw = ((lane & 31) >> 1) & 3;
+  const int prd = (wm * WT + (lane & 31)) * ROWB;
+  const int qrd = OPB + (wn * WT + (lane & 31)) * ROWB;
+  auto frags = [&](int stage, int ks, bf16x8 (&a)[F], bf16x8 (&q)[F]) {
+    const uint8_t* st = smem + stage * STB;
+    const int so = (((2 * ks + (lane >> 5)) ^ fsw) * 16);
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) af[0][fm] = __builtin_bit_cast(bf16x8, *(const u32x4*)(pa + fm * 32 * LDK));
+    for (int f = 0; f < F; ++f) a[f] = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + prd + f * 32 * ROWB + so));
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) bq[0][fn] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qa + fn * 32 * LDK));
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < BK / 16) {
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-          af[cur ^ 1][fm] = __builtin_bit_cast(bf16x8, *(const u32x4*)(pa + fm * 32 * LDK + (ks + 1) * 16));
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-          bq[cur ^ 1][fn] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qa + fn * 32 * LDK + (ks + 1) * 16));
-      }
-      // Keep the reads of step ks+1 ahead of the MFMAs of step ks.
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][fm], bq[cur][fn], acc[fm][fn], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int f = 0; f < F; ++f) q[f] = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + qrd + f * 32 * ROWB + so));
   };
 
-  const int KT = p.K / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  f32x16 acc[F][F];
+#pragma unroll
+  for (int i = 0; i < F; ++i)
+#pragma unroll
+    for (int j = 0; j < F; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  auto mfmas = [&](const bf16x8 (&a)[F], const bf16x8 (&q)[F]) {
+#pragma unroll
+    for (int i = 0; i < F; ++i)
+#pragma unroll
+      for (int j = 0; j < F; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], q[j], acc[i][j], 0, 0, 0);
+  };
+
+  // Slice t: DMA issued at step t - 3 (after that step's barrier), waited for
+  // and published by the barrier of step t - 1, multiplied at step t (its
+  // first K half's fragments read right after that barrier).  The barrier of
+  // step t also tells every wave that slice t - 1's stage has been consumed,
+  // so it can be refilled.
+  const int KT = p.K / KS;
+  const int pre = KT < NSTAGE - 1 ? KT : NSTAGE - 1;
+  for (int t = 0; t < pre; ++t) issue(t);
+  wait_stages(pre - 1);
+  __builtin_amdgcn_s_barrier();
+  bf16x8 a0[F], q0[F], a1[F], q1[F];
+  frags(0, 0, a0, q0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): both paths into the loop arrive with no reads pending
+  __builtin_amdgcn_sched_barrier(0);
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * BK);
-    compute(cur);
-    if (kt + 1 < KT) sstore(cur ^ 1);
-    __syncthreads();
+    const int st = kt % NSTAGE;
+    frags(st, 1, a1, q1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(a0, q0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < KT) {
+      const int issued = (kt + NSTAGE - 1 < KT) ? kt + NSTAGE - 1 : KT;
+      wait_stages(issued - (kt + 2));
+      __builtin_amdgcn_s_barrier();
+      if (kt + NSTAGE - 1 < KT) issue(kt + NSTAGE - 1);
+      frags((kt + 1) % NSTAGE, 0, a0, q0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(a1, q1);
+    // The next slice's first fragments were read before these MFMAs; wait for
+    // them here so the loop head does not wait for its own new reads.
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
   }
+  __syncthreads();  // every wave is done with the LDS ring before it is reused
 
   // ---- epilogue --------------------------------------------------------------
   // Accumulator register r of a 32x32 block holds row 8 (r / 4) + 4 (l / 32)
   // + (r % 4) and column l % 32.  The tile is staged through LDS in two
-  // passes of BM/2 rows (the waves with wm == pass write theirs) as
-  // S[col][row] fp32 with an odd pitch; all register indices are compile-time
-  // constants.  A cooperative loop then applies alpha, beta * D and the
-  // rounding, and writes C row-major (consecutive threads -> consecutive
-  // columns) and/or transposed (consecutive threads -> consecutive rows).
+  // passes of BT/2 rows (the waves with wm == pass write theirs) as a
+  // row-major fp32 array S with a 16-byte aligned pitch; register indices are
+  // compile-time constants.  Then, with 16-byte global accesses:
+  //  - row pass: thread -> (row, 8 consecutive columns); all of the thread's
+  //    D loads are issued first; v = alpha S + beta D is written back to S
+  //    and stored row-major to C;
+  //  - transposed pass: thread -> (column, 8 consecutive rows), stored to
+  //    T[j][i .. i+7] (SYRK: the mirrored half of C; update: X'^T).
+  // Diagonal SYRK tiles and the ragged edge of a final output fall back to
+  // element stores.
   float* const S = reinterpret_cast<float*>(smem);
   const float rsb = p.rs ? p.rs[b] : 1.f;
   const float alpha = p.alpha * (p.alpha_pow == 2 ? rsb * rsb : (p.alpha_pow == 1 ? rsb : 1.f));
   const float beta = p.beta * (p.beta_pow == 1 ? rsb : 1.f);
-  const uint16_t* Dg = p.D ? (const uint16_t*)p.D + (int64_t)b * p.sD : nullptr;
+  const uint16_t* __restrict__ Dg = p.D ? (const uint16_t*)p.D + (int64_t)b * p.sD : nullptr;
   const bool obf = SYRK || p.c_dtype == MUON_BF16;
-  uint8_t* const Cg = (uint8_t*)p.C + (int64_t)b * p.sC * (obf ? 2 : 4);
-  const bool do_rows = SYRK || !p.c_trans;
-  const bool do_trans = SYRK || p.c_trans;
-  const int Mlim = SYRK ? p.M : p.Mreal, Nlim = SYRK ? p.N : p.Nreal;
+  const int esz = obf ? 2 : 4;
+  uint8_t* const Cg = p.C ? (uint8_t*)p.C + (int64_t)b * p.sC * esz : nullptr;
+  uint8_t* const Tg = SYRK ? Cg : (p.Ct ? (uint8_t*)p.Ct + (int64_t)b * p.sCt * esz : nullptr);
+  const int64_t ldc = p.ldc, ldt = SYRK ? p.ldc : p.ldct;
+  const int Mlim = p.Mreal, Nlim = p.Nreal;
+  const bool diag = SYRK && tm == tn;
+  // 16-byte stores need the row starts aligned: ld * esz and the base.
+  const bool cvec = Cg && ((ldc * esz) & 15) == 0 && (((uintptr_t)Cg) & 15) == 0;
+  const bool tvec = Tg && ((ldt * esz) & 15) == 0 && (((uintptr_t)Tg) & 15) == 0;
+
+  // Store v[0..7] at elements base[idx .. idx+7]; `valid` leading elements only.
+  auto store8 = [&](uint8_t* base, int64_t idx, const float* v, int valid, bool vec) {
+    if (vec && valid >= 8) {
+      if (obf) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf2(v[2 * e], v[2 * e + 1]);
+        *(u32x4*)(base + idx * 2) = w;
+      } else {
+        f32x4 w0, w1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { w0[e] = v[e]; w1[e] = v[4 + e]; }
+        *(f32x4*)(base + idx * 4) = w0;
+        *(f32x4*)(base + idx * 4 + 16) = w1;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e < valid) store_elem(base, idx + e, v[e], obf);
+    }
+  };
+
+  constexpr int PITCH = BT + 4;      // floats per staged row
+  constexpr int CPR = BT / 8;        // 8-column chunks per row
+  constexpr int RPI = 256 / CPR;     // rows per step of the row pass
+  constexpr int NIT = RH / RPI;      // steps of the row pass
+  static_assert(RH * PITCH * 4 <= LDS_BYTES, "epilogue staging must fit");
 
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     if (wm == pass) {
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
+      for (int i = 0; i < F; ++i)
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
+        for (int j = 0; j < F; ++j)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int row = fm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-            const int col = wn * WN + fn * 32 + (lane & 31);
-            S[col * RP + row] = acc[fm][fn][r];
+            const int row = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            const int col = wn * WT + j * 32 + (lane & 31);
+            S[row * PITCH + col] = acc[i][j][r];
           }
     }
     __syncthreads();
-    const int i0 = tm * BM + pass * RH;
-    const int j0 = tn * BN;
-    {  // row-major pass: thread -> column, loop over rows
-      constexpr int TPC = 256 / BN;  // threads per column
-      const int jj = tid % BN, rsub = tid / BN;
-      const int j = j0 + jj;
-      for (int rr = rsub; rr < RH; rr += TPC) {
+    const int i0 = tm * BT + pass * RH;
+    const int j0 = tn * BT;
+    {
+      const int c8 = (tid % CPR) * 8, r0 = tid / CPR;
+      const int j = j0 + c8;
+      u32x4 dreg[NIT];
+      if (Dg) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it)
+          dreg[it] = *(const u32x4*)(Dg + (int64_t)(i0 + r0 + it * RPI) * p.ldd + j);
+      }
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int rr = r0 + it * RPI;
         const int i = i0 + rr;
-        float v = alpha * S[jj * RP + rr];
-        if (Dg) v += beta * bf2f(Dg[(int64_t)i * p.ldd + j]);
-        S[jj * RP + rr] = v;
-        if (do_rows && i < Mlim && j < Nlim && (!SYRK || tm < tn || i <= j))
-          store_elem(Cg, (int64_t)i * p.ldc + j, v, obf);
+        float* srow = S + rr * PITCH + c8;
+        f32x4 s0 = *(const f32x4*)srow, s1 = *(const f32x4*)(srow + 4);
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { v[e] = alpha * s0[e]; v[4 + e] = alpha * s1[e]; }
+        if (Dg) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[2 * e] += beta * __uint_as_float(dreg[it][e] << 16);
+            v[2 * e + 1] += beta * __uint_as_float(dreg[it][e] & 0xffff0000u);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { s0[e] = v[e]; s1[e] = v[4 + e]; }
+        *(f32x4*)srow = s0;
+        *(f32x4*)(srow + 4) = s1;
+        if (Cg && i < Mlim) {
+          if (diag) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (i <= j + e) store_elem(Cg, (int64_t)i * ldc + j + e, v[e], obf);
+          } else {
+            store8(Cg, (int64_t)i * ldc + j, v, Nlim - j, cvec);
+          }
+        }
       }
     }
-    if (do_trans) {
+    if (Tg) {
       __syncthreads();
-      for (int idx = tid; idx < RH * BN; idx += 256) {
-        const int rr = idx % RH, jj = idx / RH;
-        const int i = i0 + rr, j = j0 + jj;
-        if (i < Mlim && j < Nlim && (!SYRK || tm < tn || i < j))
-          store_elem(Cg, (int64_t)j * p.ldc + i, S[jj * RP + rr], obf);
+      constexpr int R8 = RH / 8;  // 8-row chunks per pass
+      for (int idx = tid; idx < BT * R8; idx += 256) {
+        const int jj = idx % BT, i8 = (idx / BT) * 8;
+        const int j = j0 + jj, i = i0 + i8;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = S[(i8 + e) * PITCH + jj];
+        if (j < Nlim) {
+          if (diag) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (i + e < j) store_elem(Tg, (int64_t)j * ldt + i + e, v[e], obf);
+          } else {
+            store8(Tg, (int64_t)j * ldt + i, v, Mlim - i, tvec);
+          }
+        }
       }
     }
     __syncthreads();
   }
 }
 
-template <int BM, int BN, bool NN, bool SYRK>
+template <int BT, bool SYRK>
 hipError_t launch_one(const GemmParams& p, hipStream_t s) {
   const int64_t grid = (int64_t)p.batch * p.tiles_per_batch;
   if (grid <= 0) return hipSuccess;
-  return launch_kernel(gemm_bf16_kernel<BM, BN, NN, SYRK>, dim3((unsigned)grid), p, s);
+  return launch_kernel(gemm_nt_bf16_kernel<BT, SYRK>, dim3((unsigned)grid), p, s);
 }
 
 }  // namespace
 
-hipError_t launch_gemm_bf16(const GemmParams& p, bool nn, bool syrk, int tile, hipStream_t s) {
-  if (tile == 256) {
-    if (syrk) return launch_one<256, 256, false, true>(p, s);
-    return nn ? launch_one<256, 256, true, false>(p, s) : launch_one<256, 256, false, false>(p, s);
-  }
-  if (syrk) return launch_one<128, 128, false, true>(p, s);
-  return nn ? launch_one<128, 128, true, false>(p, s) : launch_one<128, 128, false, false>(p, s);
+hipError_t launch_gemm_bf16(const GemmParams& p, bool syrk, int tile, hipStream_t s) {
+  if (tile == 256) return syrk ? launch_one<256, true>(p, s) : launch_one<256, false>(p, s);
+  return syrk ? launch_one<128, true>(p, s) : launch_one<128, false>(p, s);
 }
 
 }  // namespace muon

@@ -75,7 +75,7 @@ Geom make_geom(int64_t rows, int64_t cols, int32_t compute) {
 // Workspace of `nb` NS problems (+ per-parameter NorMuon scratch for `np_`
 // parameters of `prow` rows when requested).
 struct Layout {
-  size_t X0, X1, A, B, partial, rs, d, ms, q, rho, total;
+  size_t X0, X1, XT0, XT1, A, B, partial, rs, d, ms, q, rho, total;
   int tiles;
 };
 
@@ -87,6 +87,10 @@ Layout make_layout(const Geom& g, int64_t nb, int64_t nparams, int64_t prow, boo
   L.tiles = (int)((g.mp / kPrepTile) * (g.np / kPrepTile));
   L.X0 = take((size_t)nb * g.mp * g.np * es);
   L.X1 = take((size_t)nb * g.mp * g.np * es);
+  if (g.bf) {  // bf16 mode keeps X^T next to X (the update reads it as its K-contiguous operand)
+    L.XT0 = take((size_t)nb * g.mp * g.np * es);
+    L.XT1 = take((size_t)nb * g.mp * g.np * es);
+  }
   L.A = take((size_t)nb * g.mp * g.mp * es);
   L.B = take((size_t)nb * g.mp * g.mp * es);
   L.partial = take((size_t)nb * L.tiles * 4);
@@ -193,22 +197,86 @@ struct FinalOut {
 };
 
 hipError_t gemm(const Geom& g, GemmParams& p, bool nn, bool syrk, int cls, double flop, double bytes, hipStream_t s) {
-  if (g.bf) {
-    const int tile = bf16_tile_for(p.M, p.N);
-    p.tiles_m = p.M / tile;
-    p.tiles_n = p.N / tile;
-  } else {
-    p.tiles_m = p.M / 64;
-    p.tiles_n = p.N / 64;
-  }
+  const int tile = g.bf ? bf16_tile_for(p.M, p.N) : 64;
+  p.tiles_m = p.M / tile;
+  p.tiles_n = p.N / tile;
   p.tiles_per_batch = syrk ? p.tiles_m * (p.tiles_m + 1) / 2 : p.tiles_m * p.tiles_n;
   return run(cls, flop, bytes, s, [&]() {
-    return g.bf ? launch_gemm_bf16(p, nn, syrk, bf16_tile_for(p.M, p.N), s) : launch_gemm_f32(p, nn, syrk, s);
+    return g.bf ? launch_gemm_bf16(p, syrk, tile, s) : launch_gemm_f32(p, nn, syrk, s);
   });
 }
 
-hipError_t ns_iterations(const Geom& g, int64_t nb, const muon_ns_config& cfg, char* ws, const Layout& L,
-                         const FinalOut& out, hipStream_t s) {
+// bf16 mode: every product is NT.  X and X^T ping-pong between two buffer
+// pairs; the update writes both (or, on the last iteration, the output in
+// parameter orientation).
+hipError_t ns_iterations_bf16(const Geom& g, int64_t nb, const muon_ns_config& cfg, char* ws, const Layout& L,
+                              const FinalOut& out, hipStream_t s) {
+  const double m = (double)g.m, n = (double)g.n, B = (double)nb;
+  void* X[2] = {ws + L.X0, ws + L.X1};
+  void* XT[2] = {ws + L.XT0, ws + L.XT1};
+  void* A = ws + L.A;
+  void* Bm = ws + L.B;
+  const float* rs = (const float*)(ws + L.rs);
+  const int64_t sx = g.mp * g.np, sa = g.mp * g.mp;
+  int cur = 0;
+  for (int it = 0; it < cfg.steps; ++it) {
+    const bool first = it == 0, last = it == cfg.steps - 1;
+    hipError_t e;
+    {  // A = X X^T (times rs^2 on the first iteration, which folds in the normalization)
+      GemmParams p{};
+      p.P = X[cur]; p.ldp = g.np; p.sP = sx;
+      p.Q = X[cur]; p.ldq = g.np; p.sQ = sx;
+      p.C = A; p.ldc = g.mp; p.sC = sa; p.c_dtype = MUON_BF16;
+      p.M = p.N = (int)g.mp; p.K = (int)g.np; p.Mreal = p.Nreal = (int)g.mp;
+      p.alpha = 1.f;
+      p.rs = first ? rs : nullptr; p.alpha_pow = 2;
+      p.batch = (int)nb;
+      e = gemm(g, p, false, true, MUON_K_GRAM, B * m * m * n, B * (m * n + m * m) * 2, s);
+      if (e != hipSuccess) return e;
+    }
+    {  // B = c A A + b A
+      GemmParams p{};
+      p.P = A; p.ldp = g.mp; p.sP = sa;
+      p.Q = A; p.ldq = g.mp; p.sQ = sa;
+      p.D = A; p.ldd = g.mp; p.sD = sa;
+      p.C = Bm; p.ldc = g.mp; p.sC = sa; p.c_dtype = MUON_BF16;
+      p.M = p.N = p.K = (int)g.mp; p.Mreal = p.Nreal = (int)g.mp;
+      p.alpha = cfg.c; p.beta = cfg.b;
+      p.batch = (int)nb;
+      e = gemm(g, p, false, true, MUON_K_POLY, B * m * m * m, B * 2 * m * m * 2, s);
+      if (e != hipSuccess) return e;
+    }
+    {  // X' = B X + a X (times rs on the first iteration)
+      GemmParams p{};
+      p.P = Bm; p.ldp = g.mp; p.sP = sa;
+      p.Q = XT[cur]; p.ldq = g.mp; p.sQ = sx;
+      p.D = X[cur]; p.ldd = g.np; p.sD = sx;
+      p.M = (int)g.mp; p.N = (int)g.np; p.K = (int)g.mp;
+      p.alpha = 1.f; p.beta = cfg.a;
+      p.rs = first ? rs : nullptr; p.alpha_pow = 1; p.beta_pow = 1;
+      p.batch = (int)nb;
+      if (last) {
+        p.c_dtype = out.dtype;
+        if (g.tall) { p.Ct = out.C; p.ldct = out.ldc; p.sCt = out.sC; }
+        else { p.C = out.C; p.ldc = out.ldc; p.sC = out.sC; }
+        p.Mreal = (int)g.m; p.Nreal = (int)g.n;
+      } else {
+        p.c_dtype = MUON_BF16;
+        p.C = X[cur ^ 1]; p.ldc = g.np; p.sC = sx;
+        p.Ct = XT[cur ^ 1]; p.ldct = g.mp; p.sCt = sx;
+        p.Mreal = (int)g.mp; p.Nreal = (int)g.np;
+      }
+      e = gemm(g, p, false, false, MUON_K_UPDATE, B * 2 * m * m * n, B * (m * m + 4 * m * n) * 2, s);
+      if (e != hipSuccess) return e;
+    }
+    cur ^= 1;
+  }
+  return hipSuccess;
+}
+
+// fp32 mode: Gram and poly NT (SYRK), update NN reading X itself.
+hipError_t ns_iterations_f32(const Geom& g, int64_t nb, const muon_ns_config& cfg, char* ws, const Layout& L,
+                             const FinalOut& out, hipStream_t s) {
   const int32_t wdt = g.bf ? MUON_BF16 : MUON_F32;
   const double es = g.bf ? 2 : 4;
   const double m = (double)g.m, n = (double)g.n, B = (double)nb;
@@ -268,6 +336,11 @@ hipError_t ns_iterations(const Geom& g, int64_t nb, const muon_ns_config& cfg, c
     std::swap(xin, xout);
   }
   return hipSuccess;
+}
+
+hipError_t ns_iterations(const Geom& g, int64_t nb, const muon_ns_config& cfg, char* ws, const Layout& L,
+                         const FinalOut& out, hipStream_t s) {
+  return g.bf ? ns_iterations_bf16(g, nb, cfg, ws, L, out, s) : ns_iterations_f32(g, nb, cfg, ws, L, out, s);
 }
 
 hipError_t norm_finalize(const Geom& g, int64_t nb, float eps, char* ws, const Layout& L, hipStream_t s) {
@@ -386,6 +459,7 @@ int muon_ns_batched(const void* x, int32_t x_dtype, int64_t x_batch_stride, int6
     pp.x = (const char*)x + c0 * x_batch_stride * xe;
     pp.x_bs = x_batch_stride; pp.x_rs = x_row_stride;
     pp.X = ws + L.X0; pp.X_bs = g.mp * g.np;
+    pp.XT = g.bf ? ws + L.XT0 : nullptr;
     pp.partial = (float*)(ws + L.partial);
     hipError_t e = run(MUON_K_PREP, 0, (double)nb * rows * cols * (xe + (g.bf ? 2 : 4)), s,
                        [&]() { return launch_prep(pp, (int)nb, s); });
@@ -545,6 +619,7 @@ int muon_step_group(const muon_group* g, const muon_hparams* hp, void* workspace
         pp.mom[i] = g->mom[c0 + s0 + i];
       }
       pp.X = ws + L.X0 + (size_t)(s0 * H) * ge.mp * ge.np * (size_t)oes;
+      pp.XT = ge.bf ? ws + L.XT0 + (size_t)(s0 * H) * ge.mp * ge.np * (size_t)oes : nullptr;
       pp.X_bs = ge.mp * ge.np;
       pp.partial = (float*)(ws + L.partial) + s0 * H * L.tiles;
       e = run(MUON_K_PREP, 0, (double)k * pelems * (ges + 2 * mes + oes), s, [&]() { return launch_prep(pp, (int)(k * H), s); });

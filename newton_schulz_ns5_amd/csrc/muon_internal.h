@@ -21,16 +21,17 @@ constexpr int kPrepTile = 64;   // tile edge of the load / momentum kernel
 
 // ---- GEMM: C[b] = alpha_b * P[b] * op(Q[b]) + beta_b * D[b] -------------------
 // P is [M][K] row-major.  NT: Q is [N][K] (both operands K-contiguous).
-// NN: Q is [K][N].  SYRK: only tiles with tile_n >= tile_m are computed and
-// each value is also written to the mirrored position, so C is exactly
-// symmetric.
+// NN: Q is [K][N] (fp32 kernels only).  SYRK: only tiles with tile_n >=
+// tile_m are computed and each value is also written to the mirrored
+// position, so C is exactly symmetric.
 struct GemmParams {
   const void* P; int64_t ldp; int64_t sP;
   const void* Q; int64_t ldq; int64_t sQ;
   const void* D; int64_t ldd; int64_t sD;   // may be null
-  void* C; int64_t ldc; int64_t sC;
+  void* C; int64_t ldc; int64_t sC;         // row-major result, may be null (bf16 kernels)
+  void* Ct; int64_t ldct; int64_t sCt;      // transposed result: (i, j) -> Ct[j*ldct + i] (bf16 kernels)
   int32_t c_dtype;        // MUON_BF16 / MUON_F32
-  int32_t c_trans;        // store C^T: element (i, j) goes to C[j*ldc + i]
+  int32_t c_trans;        // fp32 kernels: store C^T into C instead of C
   int32_t M, N, K;        // padded problem (multiples of the tile edges)
   int32_t Mreal, Nreal;   // only i < Mreal, j < Nreal are stored
   float alpha, beta;
@@ -50,6 +51,7 @@ struct PrepParams {
   int32_t src_dtype;      // x (mode 0) or grad (mode 1)
   int32_t mom_dtype;      // mode 1
   int32_t x_bf16;         // X0 storage dtype is bf16
+  void* XT;               // bf16 mode: X0^T [b][np][mp] as well (null otherwise)
   float mu; int32_t nesterov;
   const void* x; int64_t x_bs, x_rs;          // mode 0
   int64_t param_cols;                          // mode 1: row stride of a parameter
@@ -93,7 +95,7 @@ struct ApplyParams {
 };
 
 // Launchers (return hipSuccess or the launch error).
-hipError_t launch_gemm_bf16(const GemmParams& p, bool nn, bool syrk, int tile, hipStream_t s);
+hipError_t launch_gemm_bf16(const GemmParams& p, bool syrk, int tile, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmParams& p, bool nn, bool syrk, hipStream_t s);
 hipError_t launch_prep(const PrepParams& p, int nb, hipStream_t s);
 hipError_t launch_norm(const NormParams& p, int nb, hipStream_t s);
