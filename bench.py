@@ -108,7 +108,8 @@ def cpu_baseline(grads, weights, target_seconds=20.0):
 
 
 def traffic_for(kernel_name):
-    """HBM bytes per launch from the committed counter summary, when it is current."""
+    """HBM bytes per launch from the committed counter summary (profiles/traffic.json),
+    used only while the GEMM source still has the hash the counters were taken with."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -132,6 +133,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before the steps, run one plain device copy of this many MiB (for counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -176,6 +179,13 @@ def main():
             if rc != 0:
                 raise RuntimeError(f"muon_step_group failed: {rc} {L.muon_last_error()}")
 
+    if args.copy_calibration_mib > 0:
+        src = torch.ones(args.copy_calibration_mib << 19, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
@@ -239,7 +249,7 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "update GEMM X <- a X + B X (gemm_bf16_kernel NN)",
+            "kernel": "update GEMM X' = B X + a X (gemm_nt_bf16_kernel<256, false>)",
             "achieved": round(upd_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
