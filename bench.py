@@ -1,5 +1,6 @@
 """Benchmark: one Muon / NorMuon optimizer step over one Llama-3-8B-shaped layer
-on one MI355X, through the C ABI (muon_step_group per shape group).
+on one MI355X, through the C ABI (one muon_step_groups call over the layer's
+four shape groups).
 
 A step is the whole hot path for the layer's seven matrices: Nesterov
 momentum, Frobenius normalization, five quintic Newton-Schulz iterations
@@ -161,23 +162,24 @@ def main():
         M = [torch.zeros(shape, dtype=torch.bfloat16, device=dev) for _ in names]
         V = [torch.zeros(shape[0], dtype=torch.float32, device=dev) for _ in names]
         WM = [w.to(torch.bfloat16) for w in W]
-        hp = ns.hparams(lr=0.05, momentum=0.95, nesterov=True, normuon=True, beta2=0.95, norm_eps=1e-8,
-                        ns=ns.ns_config(compute_dtype="bf16"))
         g, keep = ns._make_group(W, G, M, V, WM, heads=1)
-        groups.append({"shape": shape, "names": names, "g": g, "keep": keep, "hp": hp,
-                       "tensors": (G, W, M, V, WM), "ws_bytes": ns.step_workspace_bytes(g, hp)})
-    ws = torch.empty(max(gr["ws_bytes"] for gr in groups), dtype=torch.uint8, device=dev)
+        groups.append({"shape": shape, "names": names, "g": g, "keep": keep, "tensors": (G, W, M, V, WM)})
+    hp = ns.hparams(lr=0.05, momentum=0.95, nesterov=True, normuon=True, beta2=0.95, norm_eps=1e-8,
+                    ns=ns.ns_config(compute_dtype="bf16"))
+    import ctypes
+    garr = (ns.Group * len(groups))(*[gr["g"] for gr in groups])
+    ws_bytes = ns.step_groups_workspace_bytes([gr["g"] for gr in groups], hp)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    print(f"[bench] workspace {ws_bytes / 2**30:.2f} GiB", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream(dev)
     L = ns.lib()
-    import ctypes
     sptr = ctypes.c_void_p(stream.cuda_stream)
 
     def one_step():
-        for gr in groups:
-            rc = L.muon_step_group(ctypes.byref(gr["g"]), ctypes.byref(gr["hp"]), ctypes.c_void_p(ws.data_ptr()),
-                                   ws.numel(), sptr)
-            if rc != 0:
-                raise RuntimeError(f"muon_step_group failed: {rc} {L.muon_last_error()}")
+        rc = L.muon_step_groups(garr, len(groups), ctypes.byref(hp), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                sptr)
+        if rc != 0:
+            raise RuntimeError(f"muon_step_groups failed: {rc} {L.muon_last_error()}")
 
     if args.copy_calibration_mib > 0:
         src = torch.ones(args.copy_calibration_mib << 19, dtype=torch.int16, device=dev)
@@ -249,7 +251,7 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "update GEMM X' = B X + a X (gemm_nt_bf16_kernel<256, false>)",
+            "kernel": "update GEMM X' = B X + a X, all seven matrices per launch (gemm_nt_bf16_kernel<256, false>)",
             "achieved": round(upd_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",

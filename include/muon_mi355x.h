@@ -39,7 +39,10 @@
  *    synchronizes: work is only enqueued on `stream` (a hipStream_t; NULL is
  *    the default stream) and the call returns after the enqueue.
  *  - Matrices are row-major with unit column stride; row and batch strides
- *    are in elements.  Device pointers must be 16-byte aligned.
+ *    are in elements.  Matrix pointers of muon_ns_batched and
+ *    normuon_normalize need only be aligned to their element size; the
+ *    per-parameter tensors of the step entry points must be 16-byte aligned
+ *    (as every tensor allocation is).  Workspaces must be 256-byte aligned.
  *  - Zero-sized problems (n == 0, rows == 0 or cols == 0) are valid no-ops.
  *  - Results for one matrix are bitwise independent of how many other
  *    matrices share the call and of its position in the batch.
@@ -198,6 +201,7 @@ typedef struct muon_hparams {
  * normuon 0, beta2 0.95, norm_eps 1e-8, fan_out = fan_in = 0, default ns. */
 void muon_default_hparams(muon_hparams* hp);
 
+/* Workspace bytes muon_step_group needs for this group (0 for an empty one). */
 int muon_step_workspace_bytes(const muon_group* g, const muon_hparams* hp, size_t* bytes);
 
 /* One Muon (or NorMuon) step for every parameter of the group:
@@ -211,6 +215,23 @@ int muon_step_workspace_bytes(const muon_group* g, const muon_hparams* hp, size_
  * rows % heads != 0 or a pointer array / entry is NULL. */
 int muon_step_group(const muon_group* g, const muon_hparams* hp,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes muon_step_groups needs for these ngroups groups. */
+int muon_step_groups_workspace_bytes(const muon_group* groups, int64_t ngroups,
+                                     const muon_hparams* hp, size_t* bytes);
+
+/* One step over several groups (one per parameter shape, e.g. every matrix
+ * of a layer): [LSMuon] _run_ns batches same-shape matrices only, and
+ * [ConvFix] "Problem and fix" builds one megabatch per shape; this call
+ * steps all of them at once.  groups: host array of ngroups (0..4096)
+ * descriptors as for muon_step_group; hp applies to every group, with
+ * fan_out / fan_in taken from each group's rows / cols unless set.  The
+ * Newton-Schulz launches of the different groups are shared, so small
+ * groups fill the GPU together; each parameter's results are bitwise
+ * identical to a muon_step_group call on its own group.  Errors as for
+ * muon_step_group (nothing is enqueued when any group is invalid). */
+int muon_step_groups(const muon_group* groups, int64_t ngroups, const muon_hparams* hp,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- launch timing ------------------------------------------------------ */
 

@@ -23,7 +23,7 @@ from collections import OrderedDict
 from . import _lib
 from ._lib import MUON_BF16, MUON_F32, MuonError, NSConfig, Group, HParams, KERNEL_CLASSES
 
-__all__ = ["ns_batched", "normuon_normalize", "step_group", "MuonNS5", "per_head_view", "ns_config",
+__all__ = ["ns_batched", "normuon_normalize", "step_group", "step_groups", "step_groups_workspace_bytes", "MuonNS5", "per_head_view", "ns_config",
            "hparams", "ns_workspace_bytes", "step_workspace_bytes", "normuon_workspace_bytes",
            "profile_enable", "profile_reset", "profile_query", "MuonError", "QUINTIC", "abi_version",
            "state_layout_version", "lib"]
@@ -222,13 +222,43 @@ def step_group(w_master, grads, moms, variances=None, w_model=None, *, heads=1, 
     return None
 
 
+def step_groups_workspace_bytes(groups, hp):
+    arr = (Group * max(1, len(groups)))(*groups)
+    out = ctypes.c_size_t(0)
+    _lib.check(lib().muon_step_groups_workspace_bytes(arr, len(groups), ctypes.byref(hp), ctypes.byref(out)))
+    return out.value
+
+
+def step_groups(groups, *, hp=None, workspace=None, **kw):
+    """One Muon / NorMuon step over several shape groups in one call (see muon_step_groups).
+
+    ``groups`` is a list of dicts with the arguments of :func:`step_group`:
+    ``w_master``, ``grads``, ``moms`` and optionally ``variances``, ``w_model``,
+    ``heads``.  Every parameter comes out bitwise as it would from its own
+    ``step_group`` call.
+    """
+    hp = hp if hp is not None else hparams(**kw)
+    made = [_make_group(d["w_master"], d["grads"], d["moms"], d.get("variances"), d.get("w_model"),
+                        d.get("heads", 1)) for d in groups]
+    if not made:
+        return None
+    arr = (Group * len(made))(*[g for g, _ in made])
+    need = ctypes.c_size_t(0)
+    _lib.check(lib().muon_step_groups_workspace_bytes(arr, len(made), ctypes.byref(hp), ctypes.byref(need)))
+    first = groups[0]["w_master"][0]
+    ws = workspace if workspace is not None else _workspace(first.device, need.value)
+    _lib.check(lib().muon_step_groups(arr, len(made), ctypes.byref(hp), _ptr(ws), ws.numel(), _stream(first)))
+    del made
+    return None
+
+
 class MuonNS5:
     """Muon / NorMuon over a list of matrix-shaped parameters.
 
     Parameters are grouped by (flattened shape, dtype); each group's fp32
     master weights, momentum and NorMuon variance are held here, and one
-    ``step_group`` call per group runs the step on the current stream.  After
-    the step the bf16 model parameters hold RNE(master).
+    ``step_groups`` call runs the step of every group on the current stream.
+    After the step the bf16 model parameters hold RNE(master).
     """
 
     def __init__(self, params, lr=0.05, momentum=0.95, nesterov=True, weight_decay=0.0, extra_scale=1.0,
@@ -263,15 +293,21 @@ class MuonNS5:
 
     def step(self):
         torch = _torch()
+        todo = []
         for (shape, dt, h), ps in self.groups.items():
             live = [p for p in ps if p.grad is not None]
             if not live:
                 continue
             st = [self.state[id(p)] for p in live]
-            grads = [p.grad.contiguous() for p in live]
-            model = [p.data for p in live] if dt == torch.bfloat16 else None
-            step_group([s["master"] for s in st], grads, [s["mom"] for s in st],
-                       [s["var"] for s in st] if self.hp.normuon else None, model, heads=h, hp=self.hp)
+            todo.append({
+                "w_master": [s["master"] for s in st],
+                "grads": [p.grad.contiguous() for p in live],
+                "moms": [s["mom"] for s in st],
+                "variances": [s["var"] for s in st] if self.hp.normuon else None,
+                "w_model": [p.data for p in live] if dt == torch.bfloat16 else None,
+                "heads": h,
+            })
+        step_groups(todo, hp=self.hp)
 
 
 # ---- launch timing ---------------------------------------------------------------

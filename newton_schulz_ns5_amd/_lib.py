@@ -60,6 +60,9 @@ SIGNATURES = {
                                   c_vp, c_sz, c_vp]),
     "muon_step_workspace_bytes": (c_i32, [ctypes.POINTER(Group), ctypes.POINTER(HParams), ctypes.POINTER(c_sz)]),
     "muon_step_group": (c_i32, [ctypes.POINTER(Group), ctypes.POINTER(HParams), c_vp, c_sz, c_vp]),
+    "muon_step_groups_workspace_bytes": (c_i32, [ctypes.POINTER(Group), c_i64, ctypes.POINTER(HParams),
+                                                 ctypes.POINTER(c_sz)]),
+    "muon_step_groups": (c_i32, [ctypes.POINTER(Group), c_i64, ctypes.POINTER(HParams), c_vp, c_sz, c_vp]),
     "muon_profile_enable": (c_i32, [c_i32]),
     "muon_profile_reset": (c_i32, []),
     "muon_profile_query": (c_i32, [c_i32, ctypes.POINTER(c_i64), ctypes.POINTER(c_f64), ctypes.POINTER(c_f64),

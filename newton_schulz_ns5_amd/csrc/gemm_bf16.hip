@@ -49,19 +49,31 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Workgroup -> (batch, tile row, tile col).
+// Workgroup -> (problem, batch, tile row, tile col).
 //
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup w runs on
-// XCD w % 8); the remap gives each XCD a contiguous range of logical tiles so
-// that tiles sharing operand panels share that XCD's L2.  Full tiles are then
-// ordered in groups of 4 tile rows (all tile columns of a group before the
-// next group), SYRK tiles row by row over the upper triangle.
+// XCD w % 8).  Logical tiles are handed out in rounds of 8 x 32: in each round
+// XCD x takes the 32 consecutive logical tiles [x*32, x*32 + 32), so tiles
+// that share operand panels run together on one XCD's L2 while every XCD
+// moves through the problem list at the same pace.  Within a problem, full
+// tiles are ordered in groups of 4 tile rows (all tile columns of a group
+// before the next group); SYRK tiles row by row over the upper triangle.
 template <bool SYRK>
-__device__ __forceinline__ void decode_tile(const GemmParams& p, int& b, int& tm, int& tn) {
-  const int G = gridDim.x, wg = blockIdx.x, per = G >> 3;
-  const int pid = wg < (per << 3) ? (wg & 7) * per + (wg >> 3) : wg;
-  b = pid / p.tiles_per_batch;
-  int t = pid - b * p.tiles_per_batch;
+__device__ __forceinline__ const GemmParams& decode_tile(const GemmGroup& g, int& b, int& tm, int& tn) {
+  constexpr int CH = 32;
+  const int G = gridDim.x, wg = blockIdx.x;
+  const int full = (G / (8 * CH)) * (8 * CH);
+  int pid = wg;
+  if (wg < full) {
+    const int x = wg & 7, k = wg >> 3;
+    pid = (k / CH) * (8 * CH) + x * CH + (k % CH);
+  }
+  int pi = 0;
+  while (pi + 1 < g.nprob && pid >= g.tile_start[pi + 1]) ++pi;
+  const GemmParams& p = g.prob[pi];
+  const int local = pid - g.tile_start[pi];
+  b = local / p.tiles_per_batch;
+  int t = local - b * p.tiles_per_batch;
   if constexpr (SYRK) {
     const int T = p.tiles_m;
     tm = 0;
@@ -76,6 +88,7 @@ __device__ __forceinline__ void decode_tile(const GemmParams& p, int& b, int& tm
     tm = first + r % gsz;
     tn = r / gsz;
   }
+  return p;
 }
 
 // Buffer descriptor of a panel: base address and size in bytes, both made
@@ -89,7 +102,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 }
 
 template <int BT, bool SYRK>
-__global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmParams p) {
+__global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup grp) {
   constexpr int WT = BT / 2;          // wave tile edge
   constexpr int F = WT / 32;          // 32x32 MFMA blocks per wave tile edge
   constexpr int OPB = BT * ROWB;      // bytes of one operand in one stage
@@ -106,7 +119,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmParams p
   const int wm = wave >> 1, wn = wave & 1;
 
   int b, tm, tn;
-  decode_tile<SYRK>(p, b, tm, tn);
+  const GemmParams& p = decode_tile<SYRK>(grp, b, tm, tn);
 
   const int ldp = __builtin_amdgcn_readfirstlane((int)p.ldp);
   const int ldq = __builtin_amdgcn_readfirstlane((int)p.ldq);
@@ -349,17 +362,17 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmParams p
 }
 
 template <int BT, bool SYRK>
-hipError_t launch_one(const GemmParams& p, hipStream_t s) {
-  const int64_t grid = (int64_t)p.batch * p.tiles_per_batch;
+hipError_t launch_one(const GemmGroup& g, hipStream_t s) {
+  const int64_t grid = g.tile_start[g.nprob];
   if (grid <= 0) return hipSuccess;
-  return launch_kernel(gemm_nt_bf16_kernel<BT, SYRK>, dim3((unsigned)grid), p, s);
+  return launch_kernel(gemm_nt_bf16_kernel<BT, SYRK>, dim3((unsigned)grid), g, s);
 }
 
 }  // namespace
 
-hipError_t launch_gemm_bf16(const GemmParams& p, bool syrk, int tile, hipStream_t s) {
-  if (tile == 256) return syrk ? launch_one<256, true>(p, s) : launch_one<256, false>(p, s);
-  return syrk ? launch_one<128, true>(p, s) : launch_one<128, false>(p, s);
+hipError_t launch_gemm_bf16(const GemmGroup& g, bool syrk, int tile, hipStream_t s) {
+  if (tile == 256) return syrk ? launch_one<256, true>(g, s) : launch_one<256, false>(g, s);
+  return syrk ? launch_one<128, true>(g, s) : launch_one<128, false>(g, s);
 }
 
 }  // namespace muon

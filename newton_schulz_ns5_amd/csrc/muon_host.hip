@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -196,80 +197,132 @@ struct FinalOut {
   int64_t ldc, sC;
 };
 
-hipError_t gemm(const Geom& g, GemmParams& p, bool nn, bool syrk, int cls, double flop, double bytes, hipStream_t s) {
-  const int tile = g.bf ? bf16_tile_for(p.M, p.N) : 64;
-  p.tiles_m = p.M / tile;
-  p.tiles_n = p.N / tile;
+// One fp32-compute GEMM launch (64 x 64 tiles).
+hipError_t gemm_f32(GemmParams& p, bool nn, bool syrk, int cls, double flop, double bytes, hipStream_t s) {
+  p.tiles_m = p.M / 64;
+  p.tiles_n = p.N / 64;
   p.tiles_per_batch = syrk ? p.tiles_m * (p.tiles_m + 1) / 2 : p.tiles_m * p.tiles_n;
-  return run(cls, flop, bytes, s, [&]() {
-    return g.bf ? launch_gemm_bf16(p, syrk, tile, s) : launch_gemm_f32(p, nn, syrk, s);
-  });
+  return run(cls, flop, bytes, s, [&]() { return launch_gemm_f32(p, nn, syrk, s); });
+}
+
+// One pass of Newton-Schulz over nb same-shape matrices already loaded (X0,
+// X0^T, norm scales) into their own workspace region.
+struct NsJob {
+  Geom g;
+  int64_t nb;
+  char* ws;
+  Layout L;
+  FinalOut out;
+};
+
+// Launch one phase (Gram, poly or update) of several jobs: problems with the
+// same tile edge share a launch (at most kMaxProblems each), longest K first
+// so that the long tiles start in the first waves.
+hipError_t launch_phase(std::vector<GemmParams>& probs, bool syrk, int cls, hipStream_t s) {
+  for (int tile : {256, 128}) {
+    std::vector<GemmParams*> sel;
+    for (auto& p : probs)
+      if (bf16_tile_for(p.M, p.N) == tile) sel.push_back(&p);
+    std::stable_sort(sel.begin(), sel.end(), [](const GemmParams* x, const GemmParams* y) { return x->K > y->K; });
+    for (size_t i0 = 0; i0 < sel.size(); i0 += kMaxProblems) {
+      GemmGroup grp{};
+      grp.nprob = 0;
+      int64_t tiles = 0;
+      for (size_t i = i0; i < sel.size() && i < i0 + kMaxProblems; ++i) {
+        GemmParams& p = *sel[i];
+        p.tiles_m = p.M / tile;
+        p.tiles_n = p.N / tile;
+        p.tiles_per_batch = syrk ? p.tiles_m * (p.tiles_m + 1) / 2 : p.tiles_m * p.tiles_n;
+        grp.tile_start[grp.nprob] = (int32_t)tiles;
+        grp.prob[grp.nprob++] = p;
+        tiles += (int64_t)p.batch * p.tiles_per_batch;
+      }
+      grp.tile_start[grp.nprob] = (int32_t)tiles;
+      double fl = 0, by = 0;  // algorithmic FLOPs and bytes of this launch
+      for (int i = 0; i < grp.nprob; ++i) {
+        fl += grp.prob[i].flop;
+        by += grp.prob[i].bytes;
+      }
+      hipError_t e = run(cls, fl, by, s, [&]() { return launch_gemm_bf16(grp, syrk, tile, s); });
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
 }
 
 // bf16 mode: every product is NT.  X and X^T ping-pong between two buffer
 // pairs; the update writes both (or, on the last iteration, the output in
 // parameter orientation).
-hipError_t ns_iterations_bf16(const Geom& g, int64_t nb, const muon_ns_config& cfg, char* ws, const Layout& L,
-                              const FinalOut& out, hipStream_t s) {
-  const double m = (double)g.m, n = (double)g.n, B = (double)nb;
-  void* X[2] = {ws + L.X0, ws + L.X1};
-  void* XT[2] = {ws + L.XT0, ws + L.XT1};
-  void* A = ws + L.A;
-  void* Bm = ws + L.B;
-  const float* rs = (const float*)(ws + L.rs);
-  const int64_t sx = g.mp * g.np, sa = g.mp * g.mp;
-  int cur = 0;
+hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_config& cfg, hipStream_t s) {
+  std::vector<int> cur(jobs.size(), 0);
   for (int it = 0; it < cfg.steps; ++it) {
     const bool first = it == 0, last = it == cfg.steps - 1;
-    hipError_t e;
-    {  // A = X X^T (times rs^2 on the first iteration, which folds in the normalization)
-      GemmParams p{};
-      p.P = X[cur]; p.ldp = g.np; p.sP = sx;
-      p.Q = X[cur]; p.ldq = g.np; p.sQ = sx;
-      p.C = A; p.ldc = g.mp; p.sC = sa; p.c_dtype = MUON_BF16;
-      p.M = p.N = (int)g.mp; p.K = (int)g.np; p.Mreal = p.Nreal = (int)g.mp;
-      p.alpha = 1.f;
-      p.rs = first ? rs : nullptr; p.alpha_pow = 2;
-      p.batch = (int)nb;
-      e = gemm(g, p, false, true, MUON_K_GRAM, B * m * m * n, B * (m * n + m * m) * 2, s);
-      if (e != hipSuccess) return e;
-    }
-    {  // B = c A A + b A
-      GemmParams p{};
-      p.P = A; p.ldp = g.mp; p.sP = sa;
-      p.Q = A; p.ldq = g.mp; p.sQ = sa;
-      p.D = A; p.ldd = g.mp; p.sD = sa;
-      p.C = Bm; p.ldc = g.mp; p.sC = sa; p.c_dtype = MUON_BF16;
-      p.M = p.N = p.K = (int)g.mp; p.Mreal = p.Nreal = (int)g.mp;
-      p.alpha = cfg.c; p.beta = cfg.b;
-      p.batch = (int)nb;
-      e = gemm(g, p, false, true, MUON_K_POLY, B * m * m * m, B * 2 * m * m * 2, s);
-      if (e != hipSuccess) return e;
-    }
-    {  // X' = B X + a X (times rs on the first iteration)
-      GemmParams p{};
-      p.P = Bm; p.ldp = g.mp; p.sP = sa;
-      p.Q = XT[cur]; p.ldq = g.mp; p.sQ = sx;
-      p.D = X[cur]; p.ldd = g.np; p.sD = sx;
-      p.M = (int)g.mp; p.N = (int)g.np; p.K = (int)g.mp;
-      p.alpha = 1.f; p.beta = cfg.a;
-      p.rs = first ? rs : nullptr; p.alpha_pow = 1; p.beta_pow = 1;
-      p.batch = (int)nb;
-      if (last) {
-        p.c_dtype = out.dtype;
-        if (g.tall) { p.Ct = out.C; p.ldct = out.ldc; p.sCt = out.sC; }
-        else { p.C = out.C; p.ldc = out.ldc; p.sC = out.sC; }
-        p.Mreal = (int)g.m; p.Nreal = (int)g.n;
-      } else {
-        p.c_dtype = MUON_BF16;
-        p.C = X[cur ^ 1]; p.ldc = g.np; p.sC = sx;
-        p.Ct = XT[cur ^ 1]; p.ldct = g.mp; p.sCt = sx;
-        p.Mreal = (int)g.mp; p.Nreal = (int)g.np;
+    std::vector<GemmParams> gram, poly, upd;
+    for (size_t k = 0; k < jobs.size(); ++k) {
+      const NsJob& J = jobs[k];
+      const Geom& g = J.g;
+      const double m = (double)g.m, n = (double)g.n, B = (double)J.nb;
+      char* ws = J.ws;
+      void* X[2] = {ws + J.L.X0, ws + J.L.X1};
+      void* XT[2] = {ws + J.L.XT0, ws + J.L.XT1};
+      void* A = ws + J.L.A;
+      void* Bm = ws + J.L.B;
+      const float* rs = (const float*)(ws + J.L.rs);
+      const int64_t sx = g.mp * g.np, sa = g.mp * g.mp;
+      const int c = cur[k];
+      {  // A = X X^T (times rs^2 on the first iteration, which folds in the normalization)
+        GemmParams p{};
+        p.P = X[c]; p.ldp = g.np; p.sP = sx;
+        p.Q = X[c]; p.ldq = g.np; p.sQ = sx;
+        p.C = A; p.ldc = g.mp; p.sC = sa; p.c_dtype = MUON_BF16;
+        p.M = p.N = (int)g.mp; p.K = (int)g.np; p.Mreal = p.Nreal = (int)g.mp;
+        p.alpha = 1.f;
+        p.rs = first ? rs : nullptr; p.alpha_pow = 2;
+        p.batch = (int)J.nb;
+        p.flop = B * m * m * n; p.bytes = B * (m * n + m * m) * 2;
+        gram.push_back(p);
       }
-      e = gemm(g, p, false, false, MUON_K_UPDATE, B * 2 * m * m * n, B * (m * m + 4 * m * n) * 2, s);
-      if (e != hipSuccess) return e;
+      {  // B = c A A + b A
+        GemmParams p{};
+        p.P = A; p.ldp = g.mp; p.sP = sa;
+        p.Q = A; p.ldq = g.mp; p.sQ = sa;
+        p.D = A; p.ldd = g.mp; p.sD = sa;
+        p.C = Bm; p.ldc = g.mp; p.sC = sa; p.c_dtype = MUON_BF16;
+        p.M = p.N = p.K = (int)g.mp; p.Mreal = p.Nreal = (int)g.mp;
+        p.alpha = cfg.c; p.beta = cfg.b;
+        p.batch = (int)J.nb;
+        p.flop = B * m * m * m; p.bytes = B * 2 * m * m * 2;
+        poly.push_back(p);
+      }
+      {  // X' = B X + a X (times rs on the first iteration)
+        GemmParams p{};
+        p.P = Bm; p.ldp = g.mp; p.sP = sa;
+        p.Q = XT[c]; p.ldq = g.mp; p.sQ = sx;
+        p.D = X[c]; p.ldd = g.np; p.sD = sx;
+        p.M = (int)g.mp; p.N = (int)g.np; p.K = (int)g.mp;
+        p.alpha = 1.f; p.beta = cfg.a;
+        p.rs = first ? rs : nullptr; p.alpha_pow = 1; p.beta_pow = 1;
+        p.batch = (int)J.nb;
+        if (last) {
+          p.c_dtype = J.out.dtype;
+          if (g.tall) { p.Ct = J.out.C; p.ldct = J.out.ldc; p.sCt = J.out.sC; }
+          else { p.C = J.out.C; p.ldc = J.out.ldc; p.sC = J.out.sC; }
+          p.Mreal = (int)g.m; p.Nreal = (int)g.n;
+        } else {
+          p.c_dtype = MUON_BF16;
+          p.C = X[c ^ 1]; p.ldc = g.np; p.sC = sx;
+          p.Ct = XT[c ^ 1]; p.ldct = g.mp; p.sCt = sx;
+          p.Mreal = (int)g.mp; p.Nreal = (int)g.np;
+        }
+        p.flop = B * 2 * m * m * n; p.bytes = B * (m * m + 4 * m * n) * 2;
+        upd.push_back(p);
+      }
     }
-    cur ^= 1;
+    hipError_t e;
+    if ((e = launch_phase(gram, true, MUON_K_GRAM, s)) != hipSuccess) return e;
+    if ((e = launch_phase(poly, true, MUON_K_POLY, s)) != hipSuccess) return e;
+    if ((e = launch_phase(upd, false, MUON_K_UPDATE, s)) != hipSuccess) return e;
+    for (auto& c : cur) c ^= 1;
   }
   return hipSuccess;
 }
@@ -298,7 +351,7 @@ hipError_t ns_iterations_f32(const Geom& g, int64_t nb, const muon_ns_config& cf
       p.alpha = 1.f; p.beta = 0.f;
       p.rs = first ? rs : nullptr; p.alpha_pow = 2;
       p.batch = (int)nb;
-      e = gemm(g, p, false, true, MUON_K_GRAM, B * m * m * n, B * (m * n + m * m) * es, s);
+      e = gemm_f32(p, false, true, MUON_K_GRAM, B * m * m * n, B * (m * n + m * m) * es, s);
       if (e != hipSuccess) return e;
     }
     {  // B = c A A + b A
@@ -310,7 +363,7 @@ hipError_t ns_iterations_f32(const Geom& g, int64_t nb, const muon_ns_config& cf
       p.M = p.N = p.K = (int)g.mp; p.Mreal = p.Nreal = (int)g.mp;
       p.alpha = cfg.c; p.beta = cfg.b;
       p.batch = (int)nb;
-      e = gemm(g, p, false, true, MUON_K_POLY, B * m * m * m, B * 2 * m * m * es, s);
+      e = gemm_f32(p, false, true, MUON_K_POLY, B * m * m * m, B * 2 * m * m * es, s);
       if (e != hipSuccess) return e;
     }
     {  // X' = B X + a X (times rs on the first iteration)
@@ -330,7 +383,7 @@ hipError_t ns_iterations_f32(const Geom& g, int64_t nb, const muon_ns_config& cf
         p.C = xout; p.c_dtype = wdt; p.ldc = g.np; p.sC = sx;
         p.Mreal = (int)g.mp; p.Nreal = (int)g.np;
       }
-      e = gemm(g, p, true, false, MUON_K_UPDATE, B * 2 * m * m * n, B * (m * m + 3 * m * n) * es, s);
+      e = gemm_f32(p, true, false, MUON_K_UPDATE, B * 2 * m * m * n, B * (m * m + 3 * m * n) * es, s);
       if (e != hipSuccess) return e;
     }
     std::swap(xin, xout);
@@ -338,9 +391,14 @@ hipError_t ns_iterations_f32(const Geom& g, int64_t nb, const muon_ns_config& cf
   return hipSuccess;
 }
 
-hipError_t ns_iterations(const Geom& g, int64_t nb, const muon_ns_config& cfg, char* ws, const Layout& L,
-                         const FinalOut& out, hipStream_t s) {
-  return g.bf ? ns_iterations_bf16(g, nb, cfg, ws, L, out, s) : ns_iterations_f32(g, nb, cfg, ws, L, out, s);
+hipError_t ns_iterations(const std::vector<NsJob>& jobs, const muon_ns_config& cfg, hipStream_t s) {
+  if (jobs.empty()) return hipSuccess;
+  if (cfg.compute_dtype == MUON_BF16) return ns_iterations_bf16(jobs, cfg, s);
+  for (const NsJob& J : jobs) {
+    hipError_t e = ns_iterations_f32(J.g, J.nb, cfg, J.ws, J.L, J.out, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t norm_finalize(const Geom& g, int64_t nb, float eps, char* ws, const Layout& L, hipStream_t s) {
@@ -466,7 +524,7 @@ int muon_ns_batched(const void* x, int32_t x_dtype, int64_t x_batch_stride, int6
     if (e != hipSuccess) return hip_fail(e, "load kernel");
     if ((e = norm_finalize(g, nb, cfg->eps, ws, L, s)) != hipSuccess) return hip_fail(e, "norm kernel");
     FinalOut out{(char*)y + c0 * y_batch_stride * ye, y_dtype, y_row_stride, y_batch_stride};
-    if ((e = ns_iterations(g, nb, *cfg, ws, L, out, s)) != hipSuccess) return hip_fail(e, "Newton-Schulz kernels");
+    if ((e = ns_iterations({NsJob{g, nb, ws, L, out}}, *cfg, s)) != hipSuccess) return hip_fail(e, "Newton-Schulz kernels");
   }
   return ok();
 }
@@ -557,120 +615,231 @@ static int check_group(const muon_group* g, const muon_hparams* hp) {
   return MUON_OK;
 }
 
-int muon_step_workspace_bytes(const muon_group* g, const muon_hparams* hp, size_t* bytes) {
-  if (!bytes) return fail(MUON_ERR_INVALID_ARG, "bytes is NULL");
-  if (!g || !hp) return fail(MUON_ERR_INVALID_ARG, "group or hparams is NULL");
-  int rc = check_cfg(&hp->ns);
-  if (rc) return rc;
-  if ((rc = check_dims(g->n, g->rows, g->cols))) return rc;
-  if (g->heads < 1 || (g->rows % g->heads)) return fail(MUON_ERR_INVALID_ARG, "rows must divide into heads >= 1");
-  if (g->n == 0 || g->rows == 0 || g->cols == 0) { *bytes = 0; return ok(); }
-  const Geom ge = make_geom(g->rows / g->heads, g->cols, hp->ns.compute_dtype);
-  const int64_t pc = chunk_of(g->n, hp->ns.max_batch);
-  *bytes = make_layout(ge, pc * g->heads, pc, g->rows, hp->normuon != 0).total;
-  return ok();
+}  // extern "C"
+
+namespace {
+
+// Where each group of a step call lives in the workspace and how it is cut
+// into passes of at most pc parameters.
+struct GroupPlan {
+  const muon_group* g;
+  bool live;               // non-empty group
+  int64_t H, hb, pc, pelems;
+  Geom ge;
+  Layout L;
+  size_t offset;           // of the group's region in the workspace
+};
+
+int plan_groups(const muon_group* groups, int64_t ng, const muon_hparams* hp, std::vector<GroupPlan>& plans,
+                size_t* total) {
+  if (ng < 0 || ng > 4096) return fail(MUON_ERR_INVALID_ARG, "ngroups must be in 0..4096");
+  if (ng > 0 && !groups) return fail(MUON_ERR_INVALID_ARG, "groups is NULL");
+  if (!hp) return fail(MUON_ERR_INVALID_ARG, "hparams is NULL");
+  plans.clear();
+  size_t off = 0;
+  for (int64_t i = 0; i < ng; ++i) {
+    const muon_group* g = &groups[i];
+    GroupPlan P{};
+    P.g = g;
+    P.live = !(g->n == 0 || g->rows == 0 || g->cols == 0);
+    if (P.live) {
+      P.H = g->heads;
+      P.hb = g->rows / P.H;
+      P.ge = make_geom(P.hb, g->cols, hp->ns.compute_dtype);
+      P.pc = chunk_of(g->n, hp->ns.max_batch);
+      P.pelems = g->rows * g->cols;
+      P.L = make_layout(P.ge, P.pc * P.H, P.pc, g->rows, hp->normuon != 0);
+      P.offset = off;
+      off = align256(off + P.L.total);
+      if (P.pc * P.H > 65535) return fail(MUON_ERR_INVALID_ARG, "group %lld: parameters x heads per pass above 65535; set ns.max_batch", (long long)i);
+    }
+    plans.push_back(P);
+  }
+  *total = off;
+  return MUON_OK;
 }
 
-int muon_step_group(const muon_group* g, const muon_hparams* hp, void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = check_group(g, hp);
-  if (rc) return rc;
-  if (g->n == 0 || g->rows == 0 || g->cols == 0) return ok();
-  const int64_t H = g->heads, hb = g->rows / H;
-  const Geom ge = make_geom(hb, g->cols, hp->ns.compute_dtype);
-  const int64_t pc = chunk_of(g->n, hp->ns.max_batch);
-  const bool nm = hp->normuon != 0;
-  const Layout L = make_layout(ge, pc * H, pc, g->rows, nm);
-  if (!workspace) return fail(MUON_ERR_INVALID_ARG, "workspace is NULL");
-  if ((uintptr_t)workspace & 255) return fail(MUON_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  if (workspace_bytes < L.total) return fail(MUON_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", L.total, workspace_bytes);
-  if (pc * H > 65535) return fail(MUON_ERR_INVALID_ARG, "parameters x heads per pass above 65535; set ns.max_batch");
+int check_groups(const muon_group* groups, int64_t ng, const muon_hparams* hp) {
+  if (ng < 0 || ng > 4096) return fail(MUON_ERR_INVALID_ARG, "ngroups must be in 0..4096");
+  if (ng > 0 && !groups) return fail(MUON_ERR_INVALID_ARG, "groups is NULL");
+  for (int64_t i = 0; i < ng; ++i) {
+    int rc = check_group(&groups[i], hp);
+    if (rc) return rc;
+  }
+  if (ng == 0 && !hp) return fail(MUON_ERR_INVALID_ARG, "hparams is NULL");
+  return ng == 0 ? check_cfg(&hp->ns) : MUON_OK;
+}
 
-  hipStream_t s = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  const int32_t odt = ge.bf ? MUON_BF16 : MUON_F32;
+// Momentum (+ orientation and norm partials) and the norm finalize of one pass
+// of one group; returns the Newton-Schulz job of the pass.
+int stage_group(const GroupPlan& P, const muon_hparams* hp, char* ws, int64_t c0, int64_t np_, hipStream_t s,
+                NsJob* job) {
+  const muon_group* g = P.g;
+  const Geom& ge = P.ge;
+  const Layout& L = P.L;
   const double oes = ge.bf ? 2 : 4;
   const double ges = (double)esize(g->grad_dtype), mes = (double)esize(g->mom_dtype);
+  hipError_t e;
+  for (int64_t s0 = 0; s0 < np_; s0 += kMaxParams) {
+    const int64_t k = (np_ - s0) < kMaxParams ? (np_ - s0) : kMaxParams;
+    PrepParams pp{};
+    pp.mode = 1;
+    pp.tall = ge.tall;
+    pp.rows = (int)P.hb; pp.cols = (int)g->cols;
+    pp.mp = (int)ge.mp; pp.np = (int)ge.np;
+    pp.heads = (int)P.H;
+    pp.src_dtype = g->grad_dtype; pp.mom_dtype = g->mom_dtype;
+    pp.x_bf16 = ge.bf;
+    pp.mu = hp->momentum; pp.nesterov = hp->nesterov ? 1 : 0;
+    pp.param_cols = g->cols;
+    for (int64_t i = 0; i < k; ++i) {
+      pp.grad[i] = g->grad[c0 + s0 + i];
+      pp.mom[i] = g->mom[c0 + s0 + i];
+    }
+    pp.X = ws + L.X0 + (size_t)(s0 * P.H) * ge.mp * ge.np * (size_t)oes;
+    pp.XT = ge.bf ? ws + L.XT0 + (size_t)(s0 * P.H) * ge.mp * ge.np * (size_t)oes : nullptr;
+    pp.X_bs = ge.mp * ge.np;
+    pp.partial = (float*)(ws + L.partial) + s0 * P.H * L.tiles;
+    e = run(MUON_K_PREP, 0, (double)k * P.pelems * (ges + 2 * mes + oes * (ge.bf ? 2 : 1)), s,
+            [&]() { return launch_prep(pp, (int)(k * P.H), s); });
+    if (e != hipSuccess) return hip_fail(e, "momentum kernel");
+  }
+  if ((e = norm_finalize(ge, np_ * P.H, hp->ns.eps, ws, L, s)) != hipSuccess) return hip_fail(e, "norm kernel");
+  // The last update writes O in parameter orientation ([n][rows][cols],
+  // contiguous) into the X buffer the last iteration does not read.
+  void* obuf = ws + ((hp->ns.steps % 2) ? L.X1 : L.X0);
+  *job = NsJob{ge, np_ * P.H, ws, L, FinalOut{obuf, ge.bf ? MUON_BF16 : MUON_F32, g->cols, P.hb * g->cols}};
+  return MUON_OK;
+}
+
+// NorMuon (when on) and the weight update of one pass of one group.
+int finish_group(const GroupPlan& P, const muon_hparams* hp, char* ws, int64_t c0, int64_t np_, const NsJob& job,
+                 hipStream_t s) {
+  const muon_group* g = P.g;
+  const Layout& L = P.L;
+  const bool nm = hp->normuon != 0;
+  const int32_t odt = job.out.dtype;
+  const double oes = odt == MUON_BF16 ? 2 : 4;
+  void* obuf = job.out.C;
   const int64_t fan_out = hp->fan_out ? hp->fan_out : g->rows;
   const int64_t fan_in = hp->fan_in ? hp->fan_in : g->cols;
   const double ratio = (double)fan_out / (double)fan_in;
   const float lr_eff = (float)((double)hp->lr * std::sqrt(ratio > 1.0 ? ratio : 1.0) * (double)hp->extra_scale);
   const float decay = (float)(1.0 - (double)hp->lr * (double)hp->weight_decay);
-  const bool vec = (g->cols % 8) == 0;
-  const int64_t pelems = g->rows * g->cols;
+  hipError_t e;
+  if (nm) {
+    for (int64_t s0 = 0; s0 < np_; s0 += kMaxParams) {
+      const int64_t k = (np_ - s0) < kMaxParams ? (np_ - s0) : kMaxParams;
+      RowStatParams r2{};
+      r2.O = (char*)obuf + (size_t)s0 * P.pelems * (size_t)oes;
+      r2.o_dtype = odt; r2.o_bs = P.pelems; r2.o_rs = g->cols;
+      r2.rows = (int)g->rows; r2.cols = (int)g->cols;
+      r2.beta2 = hp->beta2; r2.eps = hp->norm_eps;
+      r2.d = (float*)(ws + L.d) + s0 * g->rows;
+      r2.ms = (float*)(ws + L.ms) + s0 * g->rows;
+      r2.q = (float*)(ws + L.q) + s0 * g->rows;
+      for (int64_t i = 0; i < k; ++i) r2.v_tab[i] = g->var[c0 + s0 + i];
+      e = run(MUON_K_ROWSTAT, 0, (double)k * (P.pelems * oes + g->rows * 8), s, [&]() { return launch_rowstat(r2, (int)k, s); });
+      if (e != hipSuccess) return hip_fail(e, "row statistics kernel");
+    }
+    RhoParams hpm{(float*)(ws + L.ms), (float*)(ws + L.q), (int)g->rows, (float*)(ws + L.rho)};
+    e = run(MUON_K_RHO, 0, (double)np_ * g->rows * 8, s, [&]() { return launch_rho(hpm, (int)np_, s); });
+    if (e != hipSuccess) return hip_fail(e, "rho kernel");
+  }
+  for (int64_t s0 = 0; s0 < np_; s0 += kMaxParams) {
+    const int64_t k = (np_ - s0) < kMaxParams ? (np_ - s0) : kMaxParams;
+    ApplyParams ap{};
+    ap.mode = 0;
+    ap.O = (char*)obuf + (size_t)s0 * P.pelems * (size_t)oes;
+    ap.o_dtype = odt; ap.o_bs = P.pelems; ap.o_rs = g->cols;
+    ap.rows = (int)g->rows; ap.cols = (int)g->cols;
+    ap.d = nm ? (float*)(ws + L.d) + s0 * g->rows : nullptr;
+    ap.rho = nm ? (float*)(ws + L.rho) + s0 : nullptr;
+    ap.lr_eff = lr_eff; ap.decay = decay;
+    ap.vec = (g->cols % 8) == 0 ? 1 : 0;
+    for (int64_t i = 0; i < k; ++i) {
+      ap.w[i] = g->w_master[c0 + s0 + i];
+      ap.wm[i] = g->model_dtype == MUON_BF16 ? g->w_model[c0 + s0 + i] : nullptr;
+    }
+    const double wb = g->model_dtype == MUON_BF16 ? 10 : 8;
+    e = run(MUON_K_APPLY, 0, (double)k * P.pelems * (oes + wb), s, [&]() { return launch_apply(ap, (int)k, s); });
+    if (e != hipSuccess) return hip_fail(e, "update kernel");
+  }
+  return MUON_OK;
+}
 
-  for (int64_t c0 = 0; c0 < g->n; c0 += pc) {
-    const int64_t np_ = (g->n - c0) < pc ? (g->n - c0) : pc;
-    hipError_t e;
-    // momentum, orientation, norm partials
-    for (int64_t s0 = 0; s0 < np_; s0 += kMaxParams) {
-      const int64_t k = (np_ - s0) < kMaxParams ? (np_ - s0) : kMaxParams;
-      PrepParams pp{};
-      pp.mode = 1;
-      pp.tall = ge.tall;
-      pp.rows = (int)hb; pp.cols = (int)g->cols;
-      pp.mp = (int)ge.mp; pp.np = (int)ge.np;
-      pp.heads = (int)H;
-      pp.src_dtype = g->grad_dtype; pp.mom_dtype = g->mom_dtype;
-      pp.x_bf16 = ge.bf;
-      pp.mu = hp->momentum; pp.nesterov = hp->nesterov ? 1 : 0;
-      pp.param_cols = g->cols;
-      for (int64_t i = 0; i < k; ++i) {
-        pp.grad[i] = g->grad[c0 + s0 + i];
-        pp.mom[i] = g->mom[c0 + s0 + i];
-      }
-      pp.X = ws + L.X0 + (size_t)(s0 * H) * ge.mp * ge.np * (size_t)oes;
-      pp.XT = ge.bf ? ws + L.XT0 + (size_t)(s0 * H) * ge.mp * ge.np * (size_t)oes : nullptr;
-      pp.X_bs = ge.mp * ge.np;
-      pp.partial = (float*)(ws + L.partial) + s0 * H * L.tiles;
-      e = run(MUON_K_PREP, 0, (double)k * pelems * (ges + 2 * mes + oes), s, [&]() { return launch_prep(pp, (int)(k * H), s); });
-      if (e != hipSuccess) return hip_fail(e, "momentum kernel");
+}  // namespace
+
+extern "C" {
+
+int muon_step_groups_workspace_bytes(const muon_group* groups, int64_t ngroups, const muon_hparams* hp,
+                                     size_t* bytes) {
+  if (!bytes) return fail(MUON_ERR_INVALID_ARG, "bytes is NULL");
+  if (!hp) return fail(MUON_ERR_INVALID_ARG, "hparams is NULL");
+  int rc = check_cfg(&hp->ns);
+  if (rc) return rc;
+  if (ngroups < 0 || ngroups > 4096) return fail(MUON_ERR_INVALID_ARG, "ngroups must be in 0..4096");
+  if (ngroups > 0 && !groups) return fail(MUON_ERR_INVALID_ARG, "groups is NULL");
+  for (int64_t i = 0; i < ngroups; ++i) {
+    const muon_group* g = &groups[i];
+    if ((rc = check_dims(g->n, g->rows, g->cols))) return rc;
+    if (g->heads < 1 || (g->rows % g->heads)) return fail(MUON_ERR_INVALID_ARG, "group %lld: rows must divide into heads >= 1", (long long)i);
+  }
+  std::vector<GroupPlan> plans;
+  size_t total = 0;
+  if ((rc = plan_groups(groups, ngroups, hp, plans, &total))) return rc;
+  *bytes = total;
+  return ok();
+}
+
+int muon_step_workspace_bytes(const muon_group* g, const muon_hparams* hp, size_t* bytes) {
+  if (!g) return fail(MUON_ERR_INVALID_ARG, "group is NULL");
+  return muon_step_groups_workspace_bytes(g, 1, hp, bytes);
+}
+
+int muon_step_groups(const muon_group* groups, int64_t ngroups, const muon_hparams* hp, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int rc = check_groups(groups, ngroups, hp);
+  if (rc) return rc;
+  std::vector<GroupPlan> plans;
+  size_t total = 0;
+  if ((rc = plan_groups(groups, ngroups, hp, plans, &total))) return rc;
+  if (total == 0) return ok();
+  if (!workspace) return fail(MUON_ERR_INVALID_ARG, "workspace is NULL");
+  if ((uintptr_t)workspace & 255) return fail(MUON_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < total) return fail(MUON_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", total, workspace_bytes);
+
+  hipStream_t s = (hipStream_t)stream;
+  int64_t passes = 0;
+  for (const GroupPlan& P : plans)
+    if (P.live) passes = std::max<int64_t>(passes, (P.g->n + P.pc - 1) / P.pc);
+  // Pass c of every group runs together: its Newton-Schulz launches cover all
+  // groups at once (a matrix's result does not depend on who shares a launch).
+  for (int64_t c = 0; c < passes; ++c) {
+    std::vector<NsJob> jobs;
+    std::vector<const GroupPlan*> who;
+    for (const GroupPlan& P : plans) {
+      if (!P.live || c * P.pc >= P.g->n) continue;
+      const int64_t c0 = c * P.pc, np_ = std::min<int64_t>(P.pc, P.g->n - c0);
+      NsJob job;
+      if ((rc = stage_group(P, hp, (char*)workspace + P.offset, c0, np_, s, &job))) return rc;
+      jobs.push_back(job);
+      who.push_back(&P);
     }
-    if ((e = norm_finalize(ge, np_ * H, hp->ns.eps, ws, L, s)) != hipSuccess) return hip_fail(e, "norm kernel");
-    // Newton-Schulz; the last update writes O in parameter orientation into
-    // whichever ping-pong buffer is free ([n][rows][cols], contiguous).
-    void* obuf = ws + ((hp->ns.steps % 2) ? L.X1 : L.X0);
-    FinalOut out{obuf, odt, g->cols, hb * g->cols};
-    if ((e = ns_iterations(ge, np_ * H, hp->ns, ws, L, out, s)) != hipSuccess) return hip_fail(e, "Newton-Schulz kernels");
-    if (nm) {
-      RowStatParams rp{};
-      rp.O = obuf; rp.o_dtype = odt; rp.o_bs = pelems; rp.o_rs = g->cols;
-      rp.rows = (int)g->rows; rp.cols = (int)g->cols;
-      rp.beta2 = hp->beta2; rp.eps = hp->norm_eps;
-      rp.d = (float*)(ws + L.d); rp.ms = (float*)(ws + L.ms); rp.q = (float*)(ws + L.q);
-      for (int64_t s0 = 0; s0 < np_; s0 += kMaxParams) {
-        const int64_t k = (np_ - s0) < kMaxParams ? (np_ - s0) : kMaxParams;
-        RowStatParams r2 = rp;
-        r2.O = (char*)obuf + (size_t)s0 * pelems * (size_t)oes;
-        r2.d += s0 * g->rows; r2.ms += s0 * g->rows; r2.q += s0 * g->rows;
-        for (int64_t i = 0; i < k; ++i) r2.v_tab[i] = g->var[c0 + s0 + i];
-        e = run(MUON_K_ROWSTAT, 0, (double)k * (pelems * oes + g->rows * 8), s, [&]() { return launch_rowstat(r2, (int)k, s); });
-        if (e != hipSuccess) return hip_fail(e, "row statistics kernel");
-      }
-      RhoParams hpm{(float*)(ws + L.ms), (float*)(ws + L.q), (int)g->rows, (float*)(ws + L.rho)};
-      e = run(MUON_K_RHO, 0, (double)np_ * g->rows * 8, s, [&]() { return launch_rho(hpm, (int)np_, s); });
-      if (e != hipSuccess) return hip_fail(e, "rho kernel");
-    }
-    for (int64_t s0 = 0; s0 < np_; s0 += kMaxParams) {
-      const int64_t k = (np_ - s0) < kMaxParams ? (np_ - s0) : kMaxParams;
-      ApplyParams ap{};
-      ap.mode = 0;
-      ap.O = (char*)obuf + (size_t)s0 * pelems * (size_t)oes;
-      ap.o_dtype = odt; ap.o_bs = pelems; ap.o_rs = g->cols;
-      ap.rows = (int)g->rows; ap.cols = (int)g->cols;
-      ap.d = nm ? (float*)(ws + L.d) + s0 * g->rows : nullptr;
-      ap.rho = nm ? (float*)(ws + L.rho) + s0 : nullptr;
-      ap.lr_eff = lr_eff; ap.decay = decay;
-      ap.vec = vec ? 1 : 0;
-      for (int64_t i = 0; i < k; ++i) {
-        ap.w[i] = g->w_master[c0 + s0 + i];
-        ap.wm[i] = g->model_dtype == MUON_BF16 ? g->w_model[c0 + s0 + i] : nullptr;
-      }
-      const double wb = g->model_dtype == MUON_BF16 ? 10 : 8;
-      e = run(MUON_K_APPLY, 0, (double)k * pelems * (oes + wb), s, [&]() { return launch_apply(ap, (int)k, s); });
-      if (e != hipSuccess) return hip_fail(e, "update kernel");
+    hipError_t e = ns_iterations(jobs, hp->ns, s);
+    if (e != hipSuccess) return hip_fail(e, "Newton-Schulz kernels");
+    for (size_t k = 0; k < jobs.size(); ++k) {
+      const GroupPlan& P = *who[k];
+      const int64_t c0 = c * P.pc, np_ = std::min<int64_t>(P.pc, P.g->n - c0);
+      if ((rc = finish_group(P, hp, (char*)workspace + P.offset, c0, np_, jobs[k], s))) return rc;
     }
   }
   return ok();
+}
+
+int muon_step_group(const muon_group* g, const muon_hparams* hp, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!g || !hp) return fail(MUON_ERR_INVALID_ARG, "group or hparams is NULL");
+  return muon_step_groups(g, 1, hp, workspace, workspace_bytes, stream);
 }
 
 // ---- launch timing ------------------------------------------------------------

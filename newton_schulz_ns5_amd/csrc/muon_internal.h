@@ -39,6 +39,16 @@ struct GemmParams {
   int32_t alpha_pow, beta_pow;  // alpha_b = alpha * rs[b]^alpha_pow ...
   int32_t batch;
   int32_t tiles_m, tiles_n, tiles_per_batch;
+  double flop, bytes;     // host bookkeeping for launch timing (not read by kernels)
+};
+
+// Several GEMM problems of one kind (same tile edge, same SYRK flag) in one
+// launch: workgroups [tile_start[i], tile_start[i+1]) belong to problem i.
+constexpr int kMaxProblems = 8;
+struct GemmGroup {
+  GemmParams prob[kMaxProblems];
+  int32_t nprob;
+  int32_t tile_start[kMaxProblems + 1];
 };
 
 // ---- load / momentum / orientation / norm partials ------------------------
@@ -95,7 +105,7 @@ struct ApplyParams {
 };
 
 // Launchers (return hipSuccess or the launch error).
-hipError_t launch_gemm_bf16(const GemmParams& p, bool syrk, int tile, hipStream_t s);
+hipError_t launch_gemm_bf16(const GemmGroup& g, bool syrk, int tile, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmParams& p, bool nn, bool syrk, hipStream_t s);
 hipError_t launch_prep(const PrepParams& p, int nb, hipStream_t s);
 hipError_t launch_norm(const NormParams& p, int nb, hipStream_t s);

@@ -239,3 +239,48 @@ def test_normuon_argument_errors():
                                    ctypes.c_void_p(a["v"]), a["vbs"], a["b2"], a["eps"], ws, a["wsb"], None)
     assert call(o=0) == -1 and call(v=0) == -1 and call(od=4) == -2 and call(b2=2.0) == -1
     assert call(ors=3) == -1 and call(vbs=3) == -1 and call(wsb=10) == -3 and call(n=0) == 0
+
+
+def _groups_array(specs):
+    keep, gs = [], []
+    for n, rows, cols, heads in specs:
+        arr = (ctypes.c_void_p * max(n, 1))(*([FAKE] * max(n, 1)))
+        keep.append(arr)
+        g = m.Group()
+        g.n, g.rows, g.cols, g.heads = n, rows, cols, heads
+        g.grad_dtype, g.mom_dtype, g.model_dtype = 1, 1, -1
+        P = ctypes.POINTER(ctypes.c_void_p)
+        g.w_master = g.grad = g.mom = ctypes.cast(arr, P)
+        gs.append(g)
+    return (m.Group * max(len(gs), 1))(*gs), gs, keep
+
+
+def test_step_groups_workspace_is_sum_of_groups():
+    hp = m.hparams()
+    specs = [(2, 4096, 4096, 1), (2, 1024, 4096, 1), (1, 300, 130, 1), (0, 64, 64, 1), (3, 512, 384, 4)]
+    arr, gs, keep = _groups_array(specs)
+    total = m.step_groups_workspace_bytes(gs, hp)
+    each = [m.step_workspace_bytes(g, hp) for g in gs]
+    assert each[3] == 0
+    assert total == sum((b + 255) // 256 * 256 for b in each)
+    assert m.step_groups_workspace_bytes([], hp) == 0
+
+
+def test_step_groups_argument_errors():
+    L = m.lib()
+    hp = m.hparams()
+    arr, gs, keep = _groups_array([(2, 64, 96, 1), (1, 128, 32, 1)])
+    big = ctypes.c_size_t(1 << 40)
+    call = lambda a, n, ws=FAKE, wsb=1 << 40: L.muon_step_groups(a, n, ctypes.byref(hp), ctypes.c_void_p(ws), wsb, None)
+    assert call(arr, -1) == -1
+    assert call(None, 2) == -1
+    assert call(None, 0) == 0                      # nothing to do
+    assert call(arr, 2, wsb=1000) == -3
+    assert call(arr, 2, ws=FAKE + 16) == -1        # workspace alignment
+    # An invalid second group fails the whole call before anything is enqueued.
+    bad, _, keep2 = _groups_array([(2, 64, 96, 1), (1, 128, 32, 3)])
+    assert call(bad, 2) == -1
+    assert "heads" in m.lib().muon_last_error().decode()
+    out = ctypes.c_size_t(0)
+    assert L.muon_step_groups_workspace_bytes(arr, 4097, ctypes.byref(hp), ctypes.byref(out)) == -1
+    del big

@@ -169,6 +169,44 @@ def test_group_size_invariance_bitwise():
     assert torch.equal(w[3], wa[3]) and torch.equal(m[3], ma[3])
 
 
+def test_grouped_step_equals_per_group_bitwise():
+    # muon_step_groups over four shape groups (a wide, a tall, a per-head and
+    # a ragged one, each a different GEMM tile edge or orientation) gives every
+    # parameter exactly the result of its own group's muon_step_group call,
+    # over two steps, with NorMuon and the bf16 model copy.
+    torch = torch_cuda()
+    specs = [((256, 512), 2, 1), ((640, 256), 1, 1), ((512, 384), 2, 4), ((300, 130), 3, 1)]
+
+    def state(seed):
+        out = []
+        for k, (shape, n, h) in enumerate(specs):
+            w = [to_dev(x, "f32") for x in make_state(seed + k, n, shape, "bf16", "bf16")]
+            out.append({
+                "w_master": w,
+                "moms": [torch.zeros(shape, dtype=torch.bfloat16, device="cuda") for _ in range(n)],
+                "variances": [torch.zeros(shape[0], device="cuda") for _ in range(n)],
+                "w_model": [torch.zeros(shape, dtype=torch.bfloat16, device="cuda") for _ in range(n)],
+                "heads": h,
+            })
+        return out
+
+    a, b = state(20), state(20)
+    for step in (1, 2):
+        for k, (shape, n, h) in enumerate(specs):
+            g = [to_dev(x, "bf16") for x in grads_for(20 + k, n, shape, "bf16", step, power=True)]
+            a[k]["grads"] = g
+            b[k]["grads"] = g
+        ns.step_groups(a, normuon=True)
+        for d in b:
+            ns.step_group(d["w_master"], d["grads"], d["moms"], d["variances"], d["w_model"], heads=d["heads"],
+                          normuon=True)
+        torch.cuda.synchronize()
+        for k in range(len(specs)):
+            for key in ("w_master", "moms", "variances", "w_model"):
+                for x, y in zip(a[k][key], b[k][key]):
+                    assert torch.equal(x, y), (step, k, key)
+
+
 def test_normuon_normalize_parity():
     torch = torch_cuda()
     n, rows, cols = 3, 96, 200
