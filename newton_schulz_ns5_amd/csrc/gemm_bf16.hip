@@ -115,7 +115,8 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   constexpr int LDS_BYTES = (NSTAGE * STB > EPI) ? NSTAGE * STB : EPI;
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
   int b, tm, tn;
@@ -136,23 +137,20 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   const int pvo = prow * ldp * 2 + dkc * 16;
   const int qvo = prow * ldq * 2 + dkc * 16;
 
-  auto issue = [&](int t) {  // K slice t -> stage t % NSTAGE
+  // DMA instruction j (0 .. DPT-1) of K slice t into stage t % NSTAGE: the
+  // first DPW fill P rows, the rest Q rows.  Slices past the last one (the
+  // pipeline runs two ahead) re-read the last slice into a stage nobody reads
+  // any more, so every step has the same shape.
+  const int KT = p.K / KS;
+  auto dma = [&](int t, int j) {
     uint8_t* const st = smem + (t % NSTAGE) * STB;
-    const int k0b = t * KS * 2;
-#pragma unroll
-    for (int j = 0; j < DPW; ++j)
+    const int k0b = (t < KT ? t : KT - 1) * KS * 2;
+    if (j < DPW)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, MUON_LDS(st + (wave * RPW + 16 * j) * ROWB), 16, pvo,
                                                16 * j * ldp * 2 + k0b, 0, 0);
-#pragma unroll
-    for (int j = 0; j < DPW; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, MUON_LDS(st + OPB + (wave * RPW + 16 * j) * ROWB), 16, qvo,
-                                               16 * j * ldq * 2 + k0b, 0, 0);
-  };
-  // Wait until at most n stages (of this wave's DMA) are still in flight.
-  auto wait_stages = [&](int n) {
-    if (n >= 2) wait_vmcnt<2 * DPT>();
-    else if (n == 1) wait_vmcnt<DPT>();
-    else wait_vmcnt<0>();
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, MUON_LDS(st + OPB + (wave * RPW + 16 * (j - DPW)) * ROWB), 16,
+                                               qvo, 16 * (j - DPW) * ldq * 2 + k0b, 0, 0);
   };
 
   // MFMA operand layout (32x32x16): lane l supplies row (l % 32) of the A
@@ -162,13 +160,17 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   const int fsw = ((lane & 31) >> 1) & 3;
   const int prd = (wm * WT + (lane & 31)) * ROWB;
   const int qrd = OPB + (wn * WT + (lane & 31)) * ROWB;
-  auto frags = [&](int stage, int ks, bf16x8 (&a)[F], bf16x8 (&q)[F]) {
+  // Fragment u (0 .. 2F-1) of a K half, in the order the MFMAs first need
+  // them: a[0], q[0 .. F-1], a[1 .. F-1].
+  auto frag = [&](int stage, int ks, int u, bf16x8 (&a)[F], bf16x8 (&q)[F]) {
     const uint8_t* st = smem + stage * STB;
     const int so = (((2 * ks + (lane >> 5)) ^ fsw) * 16);
-#pragma unroll
-    for (int f = 0; f < F; ++f) a[f] = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + prd + f * 32 * ROWB + so));
-#pragma unroll
-    for (int f = 0; f < F; ++f) q[f] = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + qrd + f * 32 * ROWB + so));
+    if (u == 0)
+      a[0] = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + prd + so));
+    else if (u <= F)
+      q[u - 1] = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + qrd + (u - 1) * 32 * ROWB + so));
+    else
+      a[u - F] = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + prd + (u - F) * 32 * ROWB + so));
   };
 
   f32x16 acc[F][F];
@@ -179,47 +181,53 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto mfmas = [&](const bf16x8 (&a)[F], const bf16x8 (&q)[F]) {
+  // One K half (16 of the slice's 32): its F^2 MFMAs on (ac, qc), spread over
+  // 2F slots; slot u also reads fragment u of the next half into (an, qn) and,
+  // in even slots, issues one of the DPT/2 DMA instructions of part `part` of
+  // slice `dt`.  Straight-line code, so the compiler waits on exactly the
+  // fragment reads each MFMA needs, and the loads never hold the MFMAs back in
+  // one burst.
+  auto half = [&](int rstage, int rks, bf16x8 (&an)[F], bf16x8 (&qn)[F], const bf16x8 (&ac)[F],
+                  const bf16x8 (&qc)[F], int dt, int part) {
 #pragma unroll
-    for (int i = 0; i < F; ++i)
+    for (int u = 0; u < 2 * F; ++u) {
+      if ((u & 1) == 0 && (u >> 1) < DPT / 2) dma(dt, part * (DPT / 2) + (u >> 1));
+      frag(rstage, rks, u, an, qn);
 #pragma unroll
-      for (int j = 0; j < F; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], q[j], acc[i][j], 0, 0, 0);
+      for (int m = u * (F / 2); m < (u + 1) * (F / 2); ++m)
+        acc[m / F][m % F] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ac[m / F], qc[m % F], acc[m / F][m % F], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
-  // Slice t: DMA issued at step t - 3 (after that step's barrier), waited for
-  // and published by the barrier of step t - 1, multiplied at step t (its
-  // first K half's fragments read right after that barrier).  The barrier of
-  // step t also tells every wave that slice t - 1's stage has been consumed,
-  // so it can be refilled.
-  const int KT = p.K / KS;
-  const int pre = KT < NSTAGE - 1 ? KT : NSTAGE - 1;
-  for (int t = 0; t < pre; ++t) issue(t);
-  wait_stages(pre - 1);
-  __builtin_amdgcn_s_barrier();
+  // Pipeline over the KT >= 4 slices of 32 K.  Slice t's loads are issued in
+  // two parts: P rows in the second half of step t - 3 (after that step's
+  // barrier), Q rows in the first half of step t - 2.  Step t waits for its
+  // own loads of slice t + 1 (DPT loads, slice t + 2's, were issued after
+  // them) and then meets the others at the barrier that publishes slice t + 1
+  // and tells every wave that slice t - 1's stage (read up to the first half
+  // of step t - 1) is free again.
+  //   first half:  MFMAs on K 0..15 of slice t, reads of K 16..31 of slice t
+  //   second half: MFMAs on K 16..31 of slice t, reads of K 0..15 of slice t+1
+  // The last step's second-half reads and loads fetch data nobody uses.
   bf16x8 a0[F], q0[F], a1[F], q1[F];
-  frags(0, 0, a0, q0);
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): both paths into the loop arrive with no reads pending
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) dma(0, j);
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) dma(1, j);
+#pragma unroll
+  for (int j = 0; j < DPT / 2; ++j) dma(2, j);
+  wait_vmcnt<DPT + DPT / 2>();
+  __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int u = 0; u < 2 * F; ++u) frag(0, 0, u, a0, q0);
   __builtin_amdgcn_sched_barrier(0);
   for (int kt = 0; kt < KT; ++kt) {
-    const int st = kt % NSTAGE;
-    frags(st, 1, a1, q1);
+    half(kt % NSTAGE, 1, a1, q1, a0, q0, kt + 2, 1);
+    wait_vmcnt<DPT>();
+    __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(a0, q0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < KT) {
-      const int issued = (kt + NSTAGE - 1 < KT) ? kt + NSTAGE - 1 : KT;
-      wait_stages(issued - (kt + 2));
-      __builtin_amdgcn_s_barrier();
-      if (kt + NSTAGE - 1 < KT) issue(kt + NSTAGE - 1);
-      frags((kt + 1) % NSTAGE, 0, a0, q0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(a1, q1);
-    // The next slice's first fragments were read before these MFMAs; wait for
-    // them here so the loop head does not wait for its own new reads.
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __builtin_amdgcn_sched_barrier(0);
+    half((kt + 1) % NSTAGE, 0, a0, q0, a1, q1, kt + 3, 0);
   }
   __syncthreads();  // every wave is done with the LDS ring before it is reused
 
@@ -280,8 +288,10 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   constexpr int NIT = RH / RPI;      // steps of the row pass
   static_assert(RH * PITCH * 4 <= LDS_BYTES, "epilogue staging must fit");
 
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
+  // The two passes are instantiated separately (compile-time pass index), so
+  // the accumulators are dead after the second pass's staging.
+  auto epilogue_pass = [&](auto pass_c) {
+    constexpr int pass = decltype(pass_c)::value;
     if (wm == pass) {
 #pragma unroll
       for (int i = 0; i < F; ++i)
@@ -358,7 +368,9 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
       }
     }
     __syncthreads();
-  }
+  };
+  epilogue_pass(std::integral_constant<int, 0>{});
+  epilogue_pass(std::integral_constant<int, 1>{});
 }
 
 template <int BT, bool SYRK>
