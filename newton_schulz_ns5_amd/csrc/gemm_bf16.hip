@@ -16,12 +16,12 @@
 // Work decomposition: one workgroup of 256 threads (four wave64s, 2 x 2) per
 // BT x BT output tile (BT = 256 or 128); each wave owns a (BT/2)^2 sub-tile of
 // 32x32 blocks computed with v_mfma_f32_32x32x16_bf16 (fp32 accumulation in
-// AGPRs).  K advances 32 at a time through a ring of four LDS stages filled by
-// direct HBM -> LDS buffer loads (buffer_load_dwordx4 ... lds): no registers
-// hold prefetched data, and about two stages of loads are in flight while a
-// third is multiplied.  Each LDS row holds 32 bf16 (64 bytes) of one operand
-// row; its four 16-byte chunks are XOR-swizzled by bits 1-2 of the row index,
-// so the 16-byte fragment reads of eight consecutive rows hit distinct banks.
+// AGPRs).  K advances 64 at a time: each operand row contributes one 128-byte
+// line per slice, brought by direct HBM -> LDS buffer loads
+// (buffer_load_dwordx4 ... lds) into a ring of five operand slots (160 KiB
+// for BT = 256), about one and a half slices ahead of the multiply.  One
+// barrier per slice.  The loads, the LDS fragment reads and the MFMAs are
+// interleaved in fixed slots, so no burst of loads holds the MFMAs back.
 //
 // Every output tile is computed by the same instruction sequence whatever the
 // batch size or the tile's position, so a matrix's result is bitwise
@@ -38,8 +38,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 #define MUON_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
-constexpr int KS = 32;        // K per LDS stage
-constexpr int NSTAGE = 4;     // LDS ring depth
+constexpr int KS = 64;        // K per slice: one 128-byte line of each operand row
+constexpr int NSLOT = 5;      // LDS ring of operand slots (one operand's rows of one slice each)
 constexpr int ROWB = KS * 2;  // bytes per LDS row
 
 // s_waitcnt with only a vector-memory count (expcnt and lgkmcnt left open).
@@ -55,9 +55,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 // XCD w % 8).  Logical tiles are handed out in rounds of 8 x 32: in each round
 // XCD x takes the 32 consecutive logical tiles [x*32, x*32 + 32), so tiles
 // that share operand panels run together on one XCD's L2 while every XCD
-// moves through the problem list at the same pace.  Within a problem, full
-// tiles are ordered in groups of 4 tile rows (all tile columns of a group
-// before the next group); SYRK tiles row by row over the upper triangle.
+// moves through the problem list at the same pace.  Within a problem, tiles
+// are ordered in bands of 4 tile rows (a band's tile columns one after the
+// other, before the next band), so 32 consecutive tiles read about 12
+// operand panels; SYRK bands cover the upper triangle only.
 template <bool SYRK>
 __device__ __forceinline__ const GemmParams& decode_tile(const GemmGroup& g, int& b, int& tm, int& tn) {
   constexpr int CH = 32;
@@ -75,10 +76,31 @@ __device__ __forceinline__ const GemmParams& decode_tile(const GemmGroup& g, int
   b = local / p.tiles_per_batch;
   int t = local - b * p.tiles_per_batch;
   if constexpr (SYRK) {
+    // Upper-triangle tiles in bands of GM tile rows r0 .. r0 + g - 1; within
+    // a band, column by column from column r0 on, rows r0 .. min(tn, last).
+    constexpr int GM = 4;
     const int T = p.tiles_m;
-    tm = 0;
-    while (t >= T - tm) { t -= T - tm; ++tm; }
-    tn = tm + t;
+    int r0 = 0;
+    for (;;) {
+      const int g = min(T - r0, GM);
+      const int tri = g * (g + 1) / 2;
+      const int size = tri + (T - r0 - g) * g;
+      if (t < size) {
+        if (t < tri) {
+          int c = 0;
+          while (t >= c + 1) { t -= c + 1; ++c; }
+          tn = r0 + c;
+          tm = r0 + t;
+        } else {
+          t -= tri;
+          tn = r0 + g + t / g;
+          tm = r0 + t % g;
+        }
+        break;
+      }
+      t -= size;
+      r0 += g;
+    }
   } else {
     constexpr int GM = 4;
     const int span = GM * p.tiles_n;
@@ -105,14 +127,14 @@ template <int BT, bool SYRK>
 __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup grp) {
   constexpr int WT = BT / 2;          // wave tile edge
   constexpr int F = WT / 32;          // 32x32 MFMA blocks per wave tile edge
-  constexpr int OPB = BT * ROWB;      // bytes of one operand in one stage
-  constexpr int STB = 2 * OPB;        // bytes of one stage
-  constexpr int RPW = BT / 4;         // operand rows loaded by each wave per stage
-  constexpr int DPW = RPW / 16;       // DMA instructions per wave per operand per stage
-  constexpr int DPT = 2 * DPW;        // DMA instructions per wave per stage
+  constexpr int OPB = BT * ROWB;      // bytes of one slot
+  constexpr int RPW = BT / 4;         // operand rows each wave loads per slice
+  constexpr int DPW = RPW / 8;        // DMA instructions per wave per operand slice (8 rows each)
+  constexpr int DQ = DPW / 2;         // DMA instructions per quarter step
+  static_assert(DQ <= F, "one DMA instruction per even slot at most");
   constexpr int RH = BT / 2;          // epilogue: tile rows staged per pass
   constexpr int EPI = RH * (BT + 4) * 4;  // epilogue staging bytes
-  constexpr int LDS_BYTES = (NSTAGE * STB > EPI) ? NSTAGE * STB : EPI;
+  constexpr int LDS_BYTES = (NSLOT * OPB > EPI) ? NSLOT * OPB : EPI;
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -129,48 +151,50 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   const __amdgpu_buffer_rsrc_t prs = make_rsrc(Pg, (int64_t)BT * p.ldp * 2);
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Qg, (int64_t)BT * p.ldq * 2);
 
-  // DMA: instruction j of a wave fills LDS rows wave*RPW + 16 j .. +15 of an
-  // operand; lane l lands at row (l / 4), slot (l % 4) and therefore fetches
-  // the global chunk slot ^ swizzle(row) = (l & 3) ^ ((l >> 3) & 3).
-  const int dkc = (lane & 3) ^ ((lane >> 3) & 3);
-  const int prow = wave * RPW + (lane >> 2);
+  // LDS layout: a slot holds BT rows of 128 bytes (64 K values of one
+  // operand row); its eight 16-byte chunks are XOR-swizzled by the row index
+  // mod 8, so the fragment reads of eight consecutive rows hit distinct banks.
+  // Slice t's P rows live in slot 2t mod 5, its Q rows in slot 2t + 1 mod 5.
+  //
+  // DMA: instruction j of a wave fills rows wave*RPW + 8 j .. +7 of a slot;
+  // lane l lands at row (l / 8), chunk (l % 8) and therefore fetches the
+  // global chunk (l % 8) ^ (row % 8).  Eight lanes cover one 128-byte line.
+  const int dkc = (lane & 7) ^ (lane >> 3);
+  const int prow = wave * RPW + (lane >> 3);
   const int pvo = prow * ldp * 2 + dkc * 16;
   const int qvo = prow * ldq * 2 + dkc * 16;
-
-  // DMA instruction j (0 .. DPT-1) of K slice t into stage t % NSTAGE: the
-  // first DPW fill P rows, the rest Q rows.  Slices past the last one (the
-  // pipeline runs two ahead) re-read the last slice into a stage nobody reads
-  // any more, so every step has the same shape.
   const int KT = p.K / KS;
-  auto dma = [&](int t, int j) {
-    uint8_t* const st = smem + (t % NSTAGE) * STB;
-    const int k0b = (t < KT ? t : KT - 1) * KS * 2;
-    if (j < DPW)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, MUON_LDS(st + (wave * RPW + 16 * j) * ROWB), 16, pvo,
-                                               16 * j * ldp * 2 + k0b, 0, 0);
+  auto slot = [&](int t, int op) { return smem + ((2 * t + op) % NSLOT) * OPB; };
+
+  // DMA instruction j (0 .. DPW-1) of operand op (0: P, 1: Q) of slice t.
+  // Slices past the last one (the pipeline runs ahead) re-read the last
+  // slice into a slot nobody reads any more, so every step has one shape.
+  auto dma = [&](int t, int op, int j) {
+    uint8_t* const dst = slot(t, op) + (wave * RPW + 8 * j) * ROWB;
+    const int k0b = (t < KT ? t : KT - 1) * ROWB;
+    if (op == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, MUON_LDS(dst), 16, pvo, 8 * j * ldp * 2 + k0b, 0, 0);
     else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, MUON_LDS(st + OPB + (wave * RPW + 16 * (j - DPW)) * ROWB), 16,
-                                               qvo, 16 * (j - DPW) * ldq * 2 + k0b, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, MUON_LDS(dst), 16, qvo, 8 * j * ldq * 2 + k0b, 0, 0);
   };
 
   // MFMA operand layout (32x32x16): lane l supplies row (l % 32) of the A
   // block and column (l % 32) of the B block, each with the 8 K values
-  // 8 (l / 32) .. 8 (l / 32) + 7 of the 16-wide K step.  Rows of a block start
-  // at multiples of 32, so a row's swizzle depends on l only.
-  const int fsw = ((lane & 31) >> 1) & 3;
+  // 8 (l / 32) .. 8 (l / 32) + 7 of the 16-wide K step, i.e. chunk
+  // 2 ks + l / 32 of quarter ks.  Blocks start at multiples of 32 rows, so a
+  // row's swizzle is l % 8.
   const int prd = (wm * WT + (lane & 31)) * ROWB;
-  const int qrd = OPB + (wn * WT + (lane & 31)) * ROWB;
-  // Fragment u (0 .. 2F-1) of a K half, in the order the MFMAs first need
-  // them: a[0], q[0 .. F-1], a[1 .. F-1].
-  auto frag = [&](int stage, int ks, int u, bf16x8 (&a)[F], bf16x8 (&q)[F]) {
-    const uint8_t* st = smem + stage * STB;
-    const int so = (((2 * ks + (lane >> 5)) ^ fsw) * 16);
+  const int qrd = (wn * WT + (lane & 31)) * ROWB;
+  // Fragment u (0 .. 2F-1) of quarter ks of slice t, in the order the MFMAs
+  // first need them: a[0], q[0 .. F-1], a[1 .. F-1].
+  auto frag = [&](int t, int ks, int u, bf16x8 (&a)[F], bf16x8 (&q)[F]) {
+    const int so = ((2 * ks + (lane >> 5)) ^ (lane & 7)) * 16;
     if (u == 0)
-      a[0] = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + prd + so));
+      a[0] = __builtin_bit_cast(bf16x8, *(const u32x4*)(slot(t, 0) + prd + so));
     else if (u <= F)
-      q[u - 1] = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + qrd + (u - 1) * 32 * ROWB + so));
+      q[u - 1] = __builtin_bit_cast(bf16x8, *(const u32x4*)(slot(t, 1) + qrd + (u - 1) * 32 * ROWB + so));
     else
-      a[u - F] = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + prd + (u - F) * 32 * ROWB + so));
+      a[u - F] = __builtin_bit_cast(bf16x8, *(const u32x4*)(slot(t, 0) + prd + (u - F) * 32 * ROWB + so));
   };
 
   f32x16 acc[F][F];
@@ -181,18 +205,21 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // One K half (16 of the slice's 32): its F^2 MFMAs on (ac, qc), spread over
-  // 2F slots; slot u also reads fragment u of the next half into (an, qn) and,
-  // in even slots, issues one of the DPT/2 DMA instructions of part `part` of
-  // slice `dt`.  Straight-line code, so the compiler waits on exactly the
-  // fragment reads each MFMA needs, and the loads never hold the MFMAs back in
-  // one burst.
-  auto half = [&](int rstage, int rks, bf16x8 (&an)[F], bf16x8 (&qn)[F], const bf16x8 (&ac)[F],
-                  const bf16x8 (&qc)[F], int dt, int part) {
+  // One quarter of a slice (16 K): its F^2 MFMAs on (ac, qc), spread over 2F
+  // slots; the first F slots also read two fragments each of quarter rks of
+  // slice rt into (an, qn), and even slots issue DMA instructions
+  // j0 .. j0 + DQ - 1 of operand dop of slice dt.  Straight-line code, so the
+  // compiler waits on exactly the fragment reads each MFMA needs, and the
+  // loads never hold the MFMAs back in one burst.
+  auto quarter = [&](int rt, int rks, bf16x8 (&an)[F], bf16x8 (&qn)[F], const bf16x8 (&ac)[F],
+                     const bf16x8 (&qc)[F], int dt, int dop, int j0) {
 #pragma unroll
     for (int u = 0; u < 2 * F; ++u) {
-      if ((u & 1) == 0 && (u >> 1) < DPT / 2) dma(dt, part * (DPT / 2) + (u >> 1));
-      frag(rstage, rks, u, an, qn);
+      if ((u & 1) == 0 && (u >> 1) < DQ) dma(dt, dop, j0 + (u >> 1));
+      if (u < F) {
+        frag(rt, rks, 2 * u, an, qn);
+        frag(rt, rks, 2 * u + 1, an, qn);
+      }
 #pragma unroll
       for (int m = u * (F / 2); m < (u + 1) * (F / 2); ++m)
         acc[m / F][m % F] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ac[m / F], qc[m % F], acc[m / F][m % F], 0, 0, 0);
@@ -200,34 +227,40 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
     }
   };
 
-  // Pipeline over the KT >= 4 slices of 32 K.  Slice t's loads are issued in
-  // two parts: P rows in the second half of step t - 3 (after that step's
-  // barrier), Q rows in the first half of step t - 2.  Step t waits for its
-  // own loads of slice t + 1 (DPT loads, slice t + 2's, were issued after
-  // them) and then meets the others at the barrier that publishes slice t + 1
-  // and tells every wave that slice t - 1's stage (read up to the first half
-  // of step t - 1) is free again.
-  //   first half:  MFMAs on K 0..15 of slice t, reads of K 16..31 of slice t
-  //   second half: MFMAs on K 16..31 of slice t, reads of K 0..15 of slice t+1
-  // The last step's second-half reads and loads fetch data nobody uses.
+  // Pipeline over the KT slices of 64 K.  Step t multiplies slice t in four
+  // quarters q0..q3 and, between q2 and q3, waits for its own loads of slice
+  // t + 1 and meets the other waves at a barrier.  That barrier publishes
+  // slice t + 1 (q3 already reads its first quarter) and, since each wave has
+  // finished its reads of slice t before it (q3's fragments are read in q2),
+  // frees slice t's slots.  Loads, each into slots freed by the barrier before
+  // them:
+  //   q3 of step t - 1, q0 of step t:  Q rows of slice t + 1 (two halves)
+  //   q1, q2 of step t:                P rows of slice t + 2
+  // so at step t's barrier the loads issued after slice t + 1's are the DPW
+  // of P(t + 2).
   bf16x8 a0[F], q0[F], a1[F], q1[F];
 #pragma unroll
-  for (int j = 0; j < DPT; ++j) dma(0, j);
+  for (int j = 0; j < DPW; ++j) dma(0, 0, j);
 #pragma unroll
-  for (int j = 0; j < DPT; ++j) dma(1, j);
+  for (int j = 0; j < DPW; ++j) dma(0, 1, j);
 #pragma unroll
-  for (int j = 0; j < DPT / 2; ++j) dma(2, j);
-  wait_vmcnt<DPT + DPT / 2>();
+  for (int j = 0; j < DPW; ++j) dma(1, 0, j);
+#pragma unroll
+  for (int j = 0; j < DQ; ++j) dma(1, 1, j);
+  wait_vmcnt<DPW + DQ>();
   __builtin_amdgcn_s_barrier();
 #pragma unroll
   for (int u = 0; u < 2 * F; ++u) frag(0, 0, u, a0, q0);
   __builtin_amdgcn_sched_barrier(0);
-  for (int kt = 0; kt < KT; ++kt) {
-    half(kt % NSTAGE, 1, a1, q1, a0, q0, kt + 2, 1);
-    wait_vmcnt<DPT>();
+  for (int t = 0; t < KT; ++t) {
+    quarter(t, 1, a1, q1, a0, q0, t + 1, 1, DQ);
+    quarter(t, 2, a0, q0, a1, q1, t + 2, 0, 0);
+    quarter(t, 3, a1, q1, a0, q0, t + 2, 0, DQ);
+    wait_vmcnt<DPW>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of slice t are done
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    half((kt + 1) % NSTAGE, 0, a0, q0, a1, q1, kt + 3, 0);
+    quarter(t + 1, 0, a0, q0, a1, q1, t + 2, 1, 0);
   }
   __syncthreads();  // every wave is done with the LDS ring before it is reused
 
