@@ -44,6 +44,9 @@
  *    per-parameter tensors of the step entry points must be 16-byte aligned
  *    (as every tensor allocation is).  Workspaces must be 256-byte aligned.
  *  - Zero-sized problems (n == 0, rows == 0 or cols == 0) are valid no-ops.
+ *  - Size limits: rows and cols of one matrix at most 4194176 (2^22 - 128),
+ *    and (rows rounded up to 128) x (cols rounded up to 128) below 2^31;
+ *    larger matrices fail with MUON_ERR_INVALID_ARG.
  *  - Results for one matrix are bitwise independent of how many other
  *    matrices share the call and of its position in the batch.
  */

@@ -180,7 +180,10 @@ int check_cfg(const muon_ns_config* c) {
   return MUON_OK;
 }
 
-constexpr int64_t kMaxDim = (int64_t)1 << 24;  // rows, cols per matrix
+// Rows and columns per matrix: a 256-row operand panel of the padded long
+// side must stay below 2^31 bytes (the GEMMs address panels through buffer
+// descriptors with 32-bit sizes and offsets).
+constexpr int64_t kMaxDim = ((int64_t)1 << 22) - kPadBf16;
 
 int check_dims(int64_t n, int64_t rows, int64_t cols) {
   if (n < 0 || rows < 0 || cols < 0) return fail(MUON_ERR_INVALID_ARG, "negative size (n=%lld rows=%lld cols=%lld)", (long long)n, (long long)rows, (long long)cols);

@@ -122,7 +122,8 @@ def ns_call(**over):
     (dict(n=-1), -1), (dict(rows=-3), -1), (dict(xrs=10), -1), (dict(yrs=63), -1), (dict(xbs=-1), -1),
     (dict(xd=7), -2), (dict(yd=2), -2), (dict(cfg_kw=dict(steps=0)), -1), (dict(cfg_kw=dict(steps=65)), -1),
     (dict(cfg=None), -1), (dict(wsb=100), -3), (dict(n=2, ybs=10), -1), (dict(x=FAKE + 1), -1),
-    (dict(rows=1 << 25), -1),
+    (dict(rows=1 << 25), -1), (dict(rows=128, cols=(1 << 22) - 127, xrs=1 << 22, yrs=1 << 22, xbs=1 << 30,
+                                     ybs=1 << 30), -1),
 ])
 def test_ns_batched_argument_errors(over, code):
     assert ns_call(**over) == code
@@ -284,3 +285,11 @@ def test_step_groups_argument_errors():
     out = ctypes.c_size_t(0)
     assert L.muon_step_groups_workspace_bytes(arr, 4097, ctypes.byref(hp), ctypes.byref(out)) == -1
     del big
+
+
+def test_ns_batched_largest_long_side_accepted():
+    # 128 x (2^22 - 128) is the widest matrix; only the fake workspace fails.
+    c = m.ns_config()
+    assert m.ns_workspace_bytes(1, 128, (1 << 22) - 128, c) > 0
+    with pytest.raises(m.MuonError):
+        m.ns_workspace_bytes(1, 128, (1 << 22) - 127, c)
