@@ -197,6 +197,36 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
       a[u - F] = __builtin_bit_cast(bf16x8, *(const u32x4*)(slot(t, 0) + prd + (u - F) * 32 * ROWB + so));
   };
 
+  const float rsb = p.rs ? p.rs[b] : 1.f;
+  const float alpha = p.alpha * (p.alpha_pow == 2 ? rsb * rsb : (p.alpha_pow == 1 ? rsb : 1.f));
+  const float beta = p.beta * (p.beta_pow == 1 ? rsb : 1.f);
+
+  // beta D with D = Q^T on this tile (p.dq) is added inside the products: in
+  // the quarters whose 16 K values are 16 of this wave's tile rows, block row
+  // bi also takes E Q^T, where E is (beta / alpha) on the matching diagonal
+  // and zero elsewhere, so that alpha (P Q^T + E Q^T) = alpha P Q^T + beta D.
+  // The factor enters as two bf16 terms (hi + lo, within 2^-16 of it).
+  // Fragment eh[h] / el[h] covers the K half h (rows 16h .. 16h + 15) of a
+  // 32-row block: lane l holds row l % 32 and K 8 (l / 32) .. + 7.
+  bf16x8 eh[2], el[2];
+  if (p.dq) {
+    const float e = beta / alpha;
+    const uint32_t hb = f2bf(e);
+    const uint32_t lb = f2bf(e - bf2f((uint16_t)hb));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int pos = (lane & 31) - 16 * h - 8 * (lane >> 5);
+      u32x4 vh, vl;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        vh[w] = (pos == 2 * w ? hb : 0u) | (pos == 2 * w + 1 ? hb << 16 : 0u);
+        vl[w] = (pos == 2 * w ? lb : 0u) | (pos == 2 * w + 1 ? lb << 16 : 0u);
+      }
+      eh[h] = __builtin_bit_cast(bf16x8, vh);
+      el[h] = __builtin_bit_cast(bf16x8, vl);
+    }
+  }
+
   f32x16 acc[F][F];
 #pragma unroll
   for (int i = 0; i < F; ++i)
@@ -211,8 +241,20 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   // j0 .. j0 + DQ - 1 of operand dop of slice dt.  Straight-line code, so the
   // compiler waits on exactly the fragment reads each MFMA needs, and the
   // loads never hold the MFMAs back in one burst.
-  auto quarter = [&](int rt, int rks, bf16x8 (&an)[F], bf16x8 (&qn)[F], const bf16x8 (&ac)[F],
-                     const bf16x8 (&qc)[F], int dt, int dop, int j0) {
+  auto diag_mfmas = [&](auto bi_c, auto h_c, const bf16x8 (&qc)[F]) {
+    constexpr int bi = decltype(bi_c)::value, h = decltype(h_c)::value;
+#pragma unroll
+    for (int j = 0; j < F; ++j) {
+      acc[bi][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(eh[h], qc[j], acc[bi][j], 0, 0, 0);
+      acc[bi][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(el[h], qc[j], acc[bi][j], 0, 0, 0);
+    }
+  };
+  // SD >= 0: the slice multiplied is the SD-th of the tile's own rows, whose
+  // K values 16 cq .. 16 cq + 15 are rows 16 (cq % 2) .. of block row
+  // bi = 2 (SD % (F/2)) + cq / 2 of wave SD / (F/2); that wave adds E Q^T.
+  auto quarter = [&](auto cq_c, auto sd_c, int rt, int rks, bf16x8 (&an)[F], bf16x8 (&qn)[F],
+                     const bf16x8 (&ac)[F], const bf16x8 (&qc)[F], int dt, int dop, int j0) {
+    constexpr int cq = decltype(cq_c)::value, SD = decltype(sd_c)::value;
 #pragma unroll
     for (int u = 0; u < 2 * F; ++u) {
       if ((u & 1) == 0 && (u >> 1) < DQ) dma(dt, dop, j0 + (u >> 1));
@@ -225,7 +267,17 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
         acc[m / F][m % F] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ac[m / F], qc[m % F], acc[m / F][m % F], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (SD >= 0) {
+      constexpr int HW = F / 2;  // slices of one wave's rows
+      if (wm == SD / HW)
+        diag_mfmas(std::integral_constant<int, 2 * (SD % HW) + cq / 2>{}, std::integral_constant<int, cq & 1>{}, qc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
+  using Q0 = std::integral_constant<int, 0>;
+  using Q1 = std::integral_constant<int, 1>;
+  using Q2 = std::integral_constant<int, 2>;
+  using Q3 = std::integral_constant<int, 3>;
 
   // Pipeline over the KT slices of 64 K.  Step t multiplies slice t in four
   // quarters q0..q3 and, between q2 and q3, waits for its own loads of slice
@@ -252,16 +304,33 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
 #pragma unroll
   for (int u = 0; u < 2 * F; ++u) frag(0, 0, u, a0, q0);
   __builtin_amdgcn_sched_barrier(0);
-  for (int t = 0; t < KT; ++t) {
-    quarter(t, 1, a1, q1, a0, q0, t + 1, 1, DQ);
-    quarter(t, 2, a0, q0, a1, q1, t + 2, 0, 0);
-    quarter(t, 3, a1, q1, a0, q0, t + 2, 0, DQ);
+  auto step = [&](int t, auto sd_c) {
+    quarter(Q0{}, sd_c, t, 1, a1, q1, a0, q0, t + 1, 1, DQ);
+    quarter(Q1{}, sd_c, t, 2, a0, q0, a1, q1, t + 2, 0, 0);
+    quarter(Q2{}, sd_c, t, 3, a1, q1, a0, q0, t + 2, 0, DQ);
     wait_vmcnt<DPW>();
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of slice t are done
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    quarter(t + 1, 0, a0, q0, a1, q1, t + 2, 1, 0);
+    quarter(Q3{}, sd_c, t + 1, 0, a0, q0, a1, q1, t + 2, 1, 0);
+  };
+  // The tile's own rows are slices td .. td + PEEL - 1 (K = M here); those
+  // steps are peeled so that the loops carry no branch.
+  constexpr int PEEL = BT / KS;
+  using SN = std::integral_constant<int, -1>;
+  const int td = p.dq ? tm * BT / KS : KT;
+  int t = 0;
+  for (; t < td; ++t) step(t, SN{});
+  if (p.dq) {
+    step(t, std::integral_constant<int, 0>{});
+    step(t + 1, std::integral_constant<int, 1>{});
+    if constexpr (PEEL == 4) {
+      step(t + 2, std::integral_constant<int, 2>{});
+      step(t + 3, std::integral_constant<int, 3>{});
+    }
+    t += PEEL;
   }
+  for (; t < KT; ++t) step(t, SN{});
   __syncthreads();  // every wave is done with the LDS ring before it is reused
 
   // ---- epilogue --------------------------------------------------------------
@@ -270,17 +339,14 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   // passes of BT/2 rows (the waves with wm == pass write theirs) as a
   // row-major fp32 array S with a 16-byte aligned pitch; register indices are
   // compile-time constants.  Then, with 16-byte global accesses:
-  //  - row pass: thread -> (row, 8 consecutive columns); all of the thread's
-  //    D loads are issued first; v = alpha S + beta D is written back to S
+  //  - row pass: thread -> (row, 8 consecutive columns); v = alpha S
+  //    (+ beta D when D is not folded into the products) is written back to S
   //    and stored row-major to C;
   //  - transposed pass: thread -> (column, 8 consecutive rows), stored to
   //    T[j][i .. i+7] (SYRK: the mirrored half of C; update: X'^T).
   // Diagonal SYRK tiles and the ragged edge of a final output fall back to
   // element stores.
   float* const S = reinterpret_cast<float*>(smem);
-  const float rsb = p.rs ? p.rs[b] : 1.f;
-  const float alpha = p.alpha * (p.alpha_pow == 2 ? rsb * rsb : (p.alpha_pow == 1 ? rsb : 1.f));
-  const float beta = p.beta * (p.beta_pow == 1 ? rsb : 1.f);
   const uint16_t* __restrict__ Dg = p.D ? (const uint16_t*)p.D + (int64_t)b * p.sD : nullptr;
   const bool obf = SYRK || p.c_dtype == MUON_BF16;
   const int esz = obf ? 2 : 4;
@@ -343,12 +409,6 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
     {
       const int c8 = (tid % CPR) * 8, r0 = tid / CPR;
       const int j = j0 + c8;
-      u32x4 dreg[NIT];
-      if (Dg) {
-#pragma unroll
-        for (int it = 0; it < NIT; ++it)
-          dreg[it] = *(const u32x4*)(Dg + (int64_t)(i0 + r0 + it * RPI) * p.ldd + j);
-      }
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
         const int rr = r0 + it * RPI;
@@ -358,11 +418,12 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
         float v[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) { v[e] = alpha * s0[e]; v[4 + e] = alpha * s1[e]; }
-        if (Dg) {
+        if (Dg) {  // only when beta D is not folded into the products
+          const u32x4 dv = *(const u32x4*)(Dg + (int64_t)i * p.ldd + j);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            v[2 * e] += beta * __uint_as_float(dreg[it][e] << 16);
-            v[2 * e + 1] += beta * __uint_as_float(dreg[it][e] & 0xffff0000u);
+            v[2 * e] += beta * __uint_as_float(dv[e] << 16);
+            v[2 * e + 1] += beta * __uint_as_float(dv[e] & 0xffff0000u);
           }
         }
 #pragma unroll

@@ -285,11 +285,16 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
         p.flop = B * m * m * n; p.bytes = B * (m * n + m * m) * 2;
         gram.push_back(p);
       }
-      {  // B = c A A + b A
+      {  // B = c A A + b A; A is stored exactly symmetric, so the b A term is
+         // A^T restricted to each tile and is added inside the products
         GemmParams p{};
         p.P = A; p.ldp = g.mp; p.sP = sa;
         p.Q = A; p.ldq = g.mp; p.sQ = sa;
-        p.D = A; p.ldd = g.mp; p.sD = sa;
+        if (cfg.c != 0.f) {
+          p.dq = 1;
+        } else {
+          p.D = A; p.ldd = g.mp; p.sD = sa;
+        }
         p.C = Bm; p.ldc = g.mp; p.sC = sa; p.c_dtype = MUON_BF16;
         p.M = p.N = p.K = (int)g.mp; p.Mreal = p.Nreal = (int)g.mp;
         p.alpha = cfg.c; p.beta = cfg.b;
@@ -297,11 +302,12 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
         p.flop = B * m * m * m; p.bytes = B * 2 * m * m * 2;
         poly.push_back(p);
       }
-      {  // X' = B X + a X (times rs on the first iteration)
+      {  // X' = B X + a X (times rs on the first iteration); X = (X^T)^T holds
+         // the same bf16 values, so a X is added inside the products
         GemmParams p{};
         p.P = Bm; p.ldp = g.mp; p.sP = sa;
         p.Q = XT[c]; p.ldq = g.mp; p.sQ = sx;
-        p.D = X[c]; p.ldd = g.np; p.sD = sx;
+        p.dq = 1;
         p.M = (int)g.mp; p.N = (int)g.np; p.K = (int)g.mp;
         p.alpha = 1.f; p.beta = cfg.a;
         p.rs = first ? rs : nullptr; p.alpha_pow = 1; p.beta_pow = 1;
@@ -317,7 +323,7 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
           p.Ct = XT[c ^ 1]; p.ldct = g.mp; p.sCt = sx;
           p.Mreal = (int)g.mp; p.Nreal = (int)g.np;
         }
-        p.flop = B * 2 * m * m * n; p.bytes = B * (m * m + 4 * m * n) * 2;
+        p.flop = B * 2 * m * m * n; p.bytes = B * (m * m + 3 * m * n) * 2;
         upd.push_back(p);
       }
     }

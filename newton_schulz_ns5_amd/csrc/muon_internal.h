@@ -32,6 +32,8 @@ struct GemmParams {
   void* Ct; int64_t ldct; int64_t sCt;      // transposed result: (i, j) -> Ct[j*ldct + i] (bf16 kernels)
   int32_t c_dtype;        // MUON_BF16 / MUON_F32
   int32_t c_trans;        // fp32 kernels: store C^T into C instead of C
+  int32_t dq;             // bf16 kernels: D = Q^T on every tile (D itself unused, alpha != 0);
+                          // beta D is then added inside the products
   int32_t M, N, K;        // padded problem (multiples of the tile edges)
   int32_t Mreal, Nreal;   // only i < Mreal, j < Nreal are stored
   float alpha, beta;
