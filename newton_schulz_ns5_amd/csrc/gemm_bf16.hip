@@ -152,17 +152,24 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Qg, (int64_t)BT * p.ldq * 2);
 
   // LDS layout: a slot holds BT rows of 128 bytes (64 K values of one
-  // operand row); its eight 16-byte chunks are XOR-swizzled by the row index
-  // mod 8, so the fragment reads of eight consecutive rows hit distinct banks.
+  // operand row); its eight 16-byte chunks are XOR-swizzled by (row / 2) mod
+  // 8.  A 16-byte fragment read is served 16 lanes (256 bytes, all 64 banks)
+  // at a time; its 16 lanes read 16 consecutive rows at one logical chunk,
+  // and the pairs (row parity, swizzle) are then all distinct.
   // Slice t's P rows live in slot 2t mod 5, its Q rows in slot 2t + 1 mod 5.
   //
   // DMA: instruction j of a wave fills rows wave*RPW + 8 j .. +7 of a slot;
   // lane l lands at row (l / 8), chunk (l % 8) and therefore fetches the
-  // global chunk (l % 8) ^ (row % 8).  Eight lanes cover one 128-byte line.
-  const int dkc = (lane & 7) ^ (lane >> 3);
+  // global chunk (l % 8) ^ ((row / 2) % 8), where (row / 2) % 8 =
+  // (4 j + l / 16) % 8.  Eight lanes cover one 128-byte line.
   const int prow = wave * RPW + (lane >> 3);
-  const int pvo = prow * ldp * 2 + dkc * 16;
-  const int qvo = prow * ldq * 2 + dkc * 16;
+  int pvo[2], qvo[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int dkc = (lane & 7) ^ ((4 * par + (lane >> 4)) & 7);
+    pvo[par] = prow * ldp * 2 + dkc * 16;
+    qvo[par] = prow * ldq * 2 + dkc * 16;
+  }
   const int KT = p.K / KS;
   auto slot = [&](int t, int op) { return smem + ((2 * t + op) % NSLOT) * OPB; };
 
@@ -173,22 +180,22 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
     uint8_t* const dst = slot(t, op) + (wave * RPW + 8 * j) * ROWB;
     const int k0b = (t < KT ? t : KT - 1) * ROWB;
     if (op == 0)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, MUON_LDS(dst), 16, pvo, 8 * j * ldp * 2 + k0b, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, MUON_LDS(dst), 16, pvo[j & 1], 8 * j * ldp * 2 + k0b, 0, 0);
     else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, MUON_LDS(dst), 16, qvo, 8 * j * ldq * 2 + k0b, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, MUON_LDS(dst), 16, qvo[j & 1], 8 * j * ldq * 2 + k0b, 0, 0);
   };
 
   // MFMA operand layout (32x32x16): lane l supplies row (l % 32) of the A
   // block and column (l % 32) of the B block, each with the 8 K values
   // 8 (l / 32) .. 8 (l / 32) + 7 of the 16-wide K step, i.e. chunk
   // 2 ks + l / 32 of quarter ks.  Blocks start at multiples of 32 rows, so a
-  // row's swizzle is l % 8.
+  // row's swizzle is ((l % 32) / 2) % 8.
   const int prd = (wm * WT + (lane & 31)) * ROWB;
   const int qrd = (wn * WT + (lane & 31)) * ROWB;
   // Fragment u (0 .. 2F-1) of quarter ks of slice t, in the order the MFMAs
   // first need them: a[0], q[0 .. F-1], a[1 .. F-1].
   auto frag = [&](int t, int ks, int u, bf16x8 (&a)[F], bf16x8 (&q)[F]) {
-    const int so = ((2 * ks + (lane >> 5)) ^ (lane & 7)) * 16;
+    const int so = ((2 * ks + (lane >> 5)) ^ (((lane & 31) >> 1) & 7)) * 16;
     if (u == 0)
       a[0] = __builtin_bit_cast(bf16x8, *(const u32x4*)(slot(t, 0) + prd + so));
     else if (u <= F)

@@ -27,7 +27,8 @@ import numpy as np
 __all__ = [
     "ROLE_GRAD", "ROLE_WEIGHT", "ROLE_U", "ROLE_V", "ROLE_NOISE",
     "generator", "f64_to_bf16_bits", "bf16_bits_to_f64", "bf16_bits_to_f32",
-    "store", "gaussian", "haar", "power_law", "power_law_many",
+    "store", "gaussian", "haar", "power_law", "power_law_many", "power_law_signal",
+    "power_law_from_signal", "power_law_device", "key_seed",
     "LLAMA3_8B_LAYER", "conv_megabatches",
 ]
 
@@ -137,23 +138,52 @@ def power_law(shape, key_uv, key_noise, dtype: str = "bf16", alpha: float = 0.7,
     return power_law_many(shape, key_uv, [key_noise], dtype, alpha, noise)[0]
 
 
+def power_law_signal(shape, key_uv, alpha: float = 0.7) -> np.ndarray:
+    """The low-rank part ``U diag(i^-alpha) V^T`` (float64) of a power-law matrix."""
+    r, c = int(shape[0]), int(shape[1])
+    k = min(r, c)
+    u = haar(r, k, tuple(key_uv) + (ROLE_U,))
+    v = haar(c, k, tuple(key_uv) + (ROLE_V,))
+    s = np.arange(1, k + 1, dtype=np.float64) ** (-alpha)
+    return (u * s[None, :]) @ v.T
+
+
+def power_law_from_signal(signal: np.ndarray, key_noise, dtype: str = "bf16", noise: float = 0.1) -> np.ndarray:
+    """``signal + noise * N(0,1)`` with the noise seeded by ``key_noise``, rounded to ``dtype``."""
+    gnoise = generator(*(tuple(key_noise) + (ROLE_NOISE,)))
+    g = noise * gnoise.standard_normal(size=signal.shape)
+    g += signal
+    return store(g, dtype)
+
+
 def power_law_many(shape, key_uv, keys_noise, dtype: str = "bf16", alpha: float = 0.7,
                    noise: float = 0.1):
     """Several power-law matrices sharing U, V and s, each with its own noise.
 
     Entry i equals ``power_law(shape, key_uv, keys_noise[i], ...)``.
     """
-    r, c = int(shape[0]), int(shape[1])
-    k = min(r, c)
-    u = haar(r, k, tuple(key_uv) + (ROLE_U,))
-    v = haar(c, k, tuple(key_uv) + (ROLE_V,))
-    s = np.arange(1, k + 1, dtype=np.float64) ** (-alpha)
-    signal = (u * s[None, :]) @ v.T
-    del u, v
-    out = []
-    for kn in keys_noise:
-        gnoise = generator(*(tuple(kn) + (ROLE_NOISE,)))
-        g = noise * gnoise.standard_normal(size=(r, c))
-        g += signal
-        out.append(store(g, dtype))
-    return out
+    signal = power_law_signal(shape, key_uv, alpha)
+    return [power_law_from_signal(signal, kn, dtype, noise) for kn in keys_noise]
+
+
+def key_seed(key) -> int:
+    """A 63-bit seed derived from an integer key tuple (for device generators)."""
+    w = np.random.SeedSequence([int(k) for k in key]).generate_state(2, np.uint32)
+    return (int(w[0]) << 31) ^ int(w[1])
+
+
+def power_law_device(signal_f32, key_noise, noise: float = 0.1):
+    """A bf16 power-law matrix drawn on the GPU: ``signal + noise * N(0,1)``.
+
+    ``signal_f32`` is the low-rank part as a float32 CUDA tensor; the noise
+    comes from torch's device generator seeded by ``key_seed(key_noise +
+    (ROLE_NOISE,))`` and the sum is rounded to bfloat16 (nearest even).  This
+    is a different generator from the host one: the same key gives different
+    noise.  Used where host generation of billions of values would dominate.
+    """
+    import torch
+    gen = torch.Generator(device=signal_f32.device)
+    gen.manual_seed(key_seed(tuple(key_noise) + (ROLE_NOISE,)))
+    g = torch.randn(signal_f32.shape, generator=gen, device=signal_f32.device, dtype=torch.float32)
+    g.mul_(noise).add_(signal_f32)
+    return g.to(torch.bfloat16)
