@@ -135,7 +135,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="before the steps, run one plain device copy of this many MiB (for counter calibration)")
+                    help="before the steps, fill and then sum a buffer of this many MiB (known bytes written "
+                         "and read, for calibrating HBM traffic counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -182,12 +183,14 @@ def main():
             raise RuntimeError(f"muon_step_groups failed: {rc} {L.muon_last_error()}")
 
     if args.copy_calibration_mib > 0:
-        src = torch.ones(args.copy_calibration_mib << 19, dtype=torch.int16, device=dev)
-        dst = torch.empty_like(src)
+        # Known traffic for counter calibration: a fill writes exactly this many
+        # MiB, a sum over the same buffer reads them once.
+        cal = torch.empty(args.copy_calibration_mib << 19, dtype=torch.int16, device=dev)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        cal.fill_(1)
+        total = cal.sum()
         torch.cuda.synchronize()
-        del src, dst
+        del cal, total
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
