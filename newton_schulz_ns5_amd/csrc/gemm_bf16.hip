@@ -3,15 +3,15 @@
 // The three products of an iteration ("core.optimizer.layer_sharded_muon",
 // LayerShardedMuon, use_syrk: A = X X^T and B = b A + c A^2 are symmetric and
 // need one triangle only; the update X <- a X + B X is a full product) are
-// all computed here in "NT" form, C = alpha P Q^T + beta D, with both operands
-// stored K-contiguous:
+// all computed here as C = alpha P op(Q) + beta D with P stored K-contiguous:
 //
-//   Gram   A  = alpha X X^T       P = Q = X,          SYRK
-//   Poly   B  = c A A + b A       P = Q = A (A = A^T), SYRK, D = A
-//   Update X' = B X + a X         P = B, Q = X^T,     D = X, writes X' and X'^T
+//   Gram   A  = alpha X X^T       NT: P = Q = X,               SYRK
+//   Poly   B  = c A A + b A       NT: P = Q = A (A = A^T),     SYRK, D = A
+//   Update X' = B X + a X         NN: P = B, Q = X ([K][N]),   D = X
 //
-// The update writes its result both row-major and transposed, so the next
-// update reads X^T without any transpose in its main loop.
+// In the poly and the update the D tile is the transposed Q tile, so beta D
+// is added inside the products.  NN fragments come from the LDS transpose
+// read (ds_read_b64_tr_b16), so the iterate is only ever stored row-major.
 //
 // Work decomposition: one workgroup of 256 threads (four wave64s, 2 x 2) per
 // BT x BT output tile (BT = 256 or 128); each wave owns a (BT/2)^2 sub-tile of
@@ -123,8 +123,39 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, n, 0x00020000);
 }
 
-template <int BT, bool SYRK>
+// The same descriptor as four words, for the assembly loads below.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, int64_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)(uint32_t)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// One 16-byte-per-lane HBM -> LDS load issued as assembly: lane l's 16 bytes
+// from base + voff + soff land at LDS byte address lds + 16 l.  The compiler
+// does not see it as an LDS write, so it does not make later LDS reads wait
+// for every load in flight (it would before each transpose read); the kernel
+// orders these loads itself with explicit vmcnt waits and barriers.
+__device__ __forceinline__ void lds_dma16_asm(i32x4 rsrc, uint32_t lds, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc),
+                 "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "memory", "m0");
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// NN: Q is stored [K][N] (N contiguous) instead of [N][K]; its fragments are
+// read with the LDS transpose read (ds_read_b64_tr_b16).
+template <int BT, bool SYRK, bool NN>
 __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup grp) {
+  static_assert(!(SYRK && NN), "SYRK products are NT");
   constexpr int WT = BT / 2;          // wave tile edge
   constexpr int F = WT / 32;          // 32x32 MFMA blocks per wave tile edge
   constexpr int OPB = BT * ROWB;      // bytes of one slot
@@ -147,9 +178,12 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   const int ldp = __builtin_amdgcn_readfirstlane((int)p.ldp);
   const int ldq = __builtin_amdgcn_readfirstlane((int)p.ldq);
   const uint16_t* Pg = (const uint16_t*)p.P + (int64_t)b * p.sP + (int64_t)tm * BT * p.ldp;
-  const uint16_t* Qg = (const uint16_t*)p.Q + (int64_t)b * p.sQ + (int64_t)tn * BT * p.ldq;
+  const uint16_t* Qg = (const uint16_t*)p.Q + (int64_t)b * p.sQ + (NN ? (int64_t)tn * BT : (int64_t)tn * BT * p.ldq);
+  const int64_t qbytes = (NN ? (int64_t)p.K : (int64_t)BT) * p.ldq * 2;
   const __amdgpu_buffer_rsrc_t prs = make_rsrc(Pg, (int64_t)BT * p.ldp * 2);
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Qg, (int64_t)BT * p.ldq * 2);
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Qg, qbytes);
+  const i32x4 prw = rsrc_words(Pg, (int64_t)BT * p.ldp * 2);
+  const i32x4 qrw = rsrc_words(Qg, qbytes);
 
   // LDS layout: a slot holds BT rows of 128 bytes (64 K values of one
   // operand row); its eight 16-byte chunks are XOR-swizzled by (row / 2) mod
@@ -162,27 +196,54 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   // lane l lands at row (l / 8), chunk (l % 8) and therefore fetches the
   // global chunk (l % 8) ^ ((row / 2) % 8), where (row / 2) % 8 =
   // (4 j + l / 16) % 8.  Eight lanes cover one 128-byte line.
+  //
+  // NN Q slot: 64 K rows of the tile's BT columns, QROWB bytes each, with the
+  // 32-byte blocks of a row XOR-swizzled by 2 (row % 4) (see the transpose
+  // reads).  Wave w fills rows 16 w .. 16 w + 15, QRPI rows per instruction;
+  // lane l lands at row l / QCH, chunk l % QCH.
+  constexpr int QROWB = NN ? BT * 2 : ROWB;
+  constexpr int QCH = QROWB / 16;      // 16-byte chunks per Q slot row
+  constexpr int QRPI = 1024 / QROWB;   // Q slot rows per DMA instruction
   const int prow = wave * RPW + (lane >> 3);
   int pvo[2], qvo[2];
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
     const int dkc = (lane & 7) ^ ((4 * par + (lane >> 4)) & 7);
     pvo[par] = prow * ldp * 2 + dkc * 16;
-    qvo[par] = prow * ldq * 2 + dkc * 16;
+    if constexpr (NN) {
+      const int rl = lane / QCH, cl = lane % QCH;
+      const int key = (par * QRPI + rl) & 3;
+      qvo[par] = rl * ldq * 2 + (2 * ((cl >> 1) ^ (2 * key)) + (cl & 1)) * 16;
+    } else {
+      qvo[par] = prow * ldq * 2 + dkc * 16;
+    }
   }
   const int KT = p.K / KS;
   auto slot = [&](int t, int op) { return smem + ((2 * t + op) % NSLOT) * OPB; };
+  const uint32_t smem_lds =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem);
 
   // DMA instruction j (0 .. DPW-1) of operand op (0: P, 1: Q) of slice t.
   // Slices past the last one (the pipeline runs ahead) re-read the last
   // slice into a slot nobody reads any more, so every step has one shape.
   auto dma = [&](int t, int op, int j) {
-    uint8_t* const dst = slot(t, op) + (wave * RPW + 8 * j) * ROWB;
-    const int k0b = (t < KT ? t : KT - 1) * ROWB;
-    if (op == 0)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, MUON_LDS(dst), 16, pvo[j & 1], 8 * j * ldp * 2 + k0b, 0, 0);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, MUON_LDS(dst), 16, qvo[j & 1], 8 * j * ldq * 2 + k0b, 0, 0);
+    const int tc = t < KT ? t : KT - 1;
+    const int k0b = tc * ROWB;
+    if constexpr (NN) {
+      const uint32_t sl = smem_lds + (uint32_t)(((2 * t + op) % NSLOT) * OPB);
+      if (op == 0) {
+        lds_dma16_asm(prw, sl + (wave * RPW + 8 * j) * ROWB, pvo[j & 1], 8 * j * ldp * 2 + k0b);
+      } else {
+        const uint32_t krow = (uint32_t)tc * KS + wave * 16 + j * QRPI;
+        lds_dma16_asm(qrw, sl + (wave * 16 + j * QRPI) * QROWB, qvo[j & 1], (int)(krow * (uint32_t)ldq * 2u));
+      }
+    } else {
+      uint8_t* const dst = slot(t, op) + (wave * RPW + 8 * j) * ROWB;
+      if (op == 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, MUON_LDS(dst), 16, pvo[j & 1], 8 * j * ldp * 2 + k0b, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, MUON_LDS(dst), 16, qvo[j & 1], 8 * j * ldq * 2 + k0b, 0, 0);
+    }
   };
 
   // MFMA operand layout (32x32x16): lane l supplies row (l % 32) of the A
@@ -192,14 +253,36 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   // row's swizzle is ((l % 32) / 2) % 8.
   const int prd = (wm * WT + (lane & 31)) * ROWB;
   const int qrd = (wn * WT + (lane & 31)) * ROWB;
+  // NN: lane l of 16-lane group g = l / 16 supplies row 8 (g / 2) + (l % 16) / 4
+  // (+ 16 ks + 4 r) and the four columns 4 (l % 4) .. + 3 of the 16-column half
+  // g % 2 of a 32-column block; the transpose read then hands lane l column
+  // l % 32 with the four K values 8 (l / 32) + 4 r .. + 3, the MFMA B layout.
+  // Lanes 0..31 cover four rows and all eight 32-byte blocks of a 256-byte
+  // span under the 2 (row % 4) swizzle: no bank is read twice.
+  const int trow = (8 * (lane >> 5) + ((lane & 15) >> 2)) * QROWB;
+  int tcol[F];
+#pragma unroll
+  for (int f = 0; f < F; ++f)
+    tcol[f] = ((((wn * WT + 32 * f) >> 4) + ((lane >> 4) & 1)) ^ (2 * ((lane & 15) >> 2))) * 32 + (lane & 3) * 8;
+  auto trq = [&](int t, int ks, int f) {
+    const uint8_t* base = slot(t, 1) + 16 * ks * QROWB + trow + tcol[f];
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)MUON_LDS(base));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)MUON_LDS(base + 4 * QROWB));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
   // Fragment u (0 .. 2F-1) of quarter ks of slice t, in the order the MFMAs
   // first need them: a[0], q[0 .. F-1], a[1 .. F-1].
   auto frag = [&](int t, int ks, int u, bf16x8 (&a)[F], bf16x8 (&q)[F]) {
     const int so = ((2 * ks + (lane >> 5)) ^ (((lane & 31) >> 1) & 7)) * 16;
     if (u == 0)
       a[0] = __builtin_bit_cast(bf16x8, *(const u32x4*)(slot(t, 0) + prd + so));
-    else if (u <= F)
-      q[u - 1] = __builtin_bit_cast(bf16x8, *(const u32x4*)(slot(t, 1) + qrd + (u - 1) * 32 * ROWB + so));
+    else if (u <= F) {
+      if constexpr (NN)
+        q[u - 1] = trq(t, ks, u - 1);
+      else
+        q[u - 1] = __builtin_bit_cast(bf16x8, *(const u32x4*)(slot(t, 1) + qrd + (u - 1) * 32 * ROWB + so));
+    }
     else
       a[u - F] = __builtin_bit_cast(bf16x8, *(const u32x4*)(slot(t, 0) + prd + (u - F) * 32 * ROWB + so));
   };
@@ -338,7 +421,11 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
     t += PEEL;
   }
   for (; t < KT; ++t) step(t, SN{});
-  __syncthreads();  // every wave is done with the LDS ring before it is reused
+  // Every wave is done with the LDS ring, and its loads past the last slice
+  // have landed, before the ring is reused (explicit: the NN kernel's loads
+  // are invisible to the compiler).
+  wait_vmcnt<0>();
+  __syncthreads();
 
   // ---- epilogue --------------------------------------------------------------
   // Accumulator register r of a 32x32 block holds row 8 (r / 4) + 4 (l / 32)
@@ -474,18 +561,26 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   epilogue_pass(std::integral_constant<int, 1>{});
 }
 
-template <int BT, bool SYRK>
+template <int BT, bool SYRK, bool NN>
 hipError_t launch_one(const GemmGroup& g, hipStream_t s) {
   const int64_t grid = g.tile_start[g.nprob];
   if (grid <= 0) return hipSuccess;
-  return launch_kernel(gemm_nt_bf16_kernel<BT, SYRK>, dim3((unsigned)grid), g, s);
+  return launch_kernel(gemm_nt_bf16_kernel<BT, SYRK, NN>, dim3((unsigned)grid), g, s);
 }
 
 }  // namespace
 
-hipError_t launch_gemm_bf16(const GemmGroup& g, bool syrk, int tile, hipStream_t s) {
-  if (tile == 256) return syrk ? launch_one<256, true>(g, s) : launch_one<256, false>(g, s);
-  return syrk ? launch_one<128, true>(g, s) : launch_one<128, false>(g, s);
+hipError_t launch_gemm_bf16(const GemmGroup& g, bool syrk, bool nn, int tile, hipStream_t s) {
+  // Every K is a multiple of 128 and at least the tile edge (the pipeline and
+  // the peeled diagonal slices rely on it); SYRK products are NT.
+  for (int i = 0; i < g.nprob; ++i)
+    if (g.prob[i].K % 128 != 0 || g.prob[i].K < tile) return hipErrorInvalidValue;
+  if (syrk && nn) return hipErrorInvalidValue;
+  if (tile == 256)
+    return syrk ? launch_one<256, true, false>(g, s)
+                : (nn ? launch_one<256, false, true>(g, s) : launch_one<256, false, false>(g, s));
+  return syrk ? launch_one<128, true, false>(g, s)
+              : (nn ? launch_one<128, false, true>(g, s) : launch_one<128, false, false>(g, s));
 }
 
 }  // namespace muon

@@ -76,7 +76,7 @@ Geom make_geom(int64_t rows, int64_t cols, int32_t compute) {
 // Workspace of `nb` NS problems (+ per-parameter NorMuon scratch for `np_`
 // parameters of `prow` rows when requested).
 struct Layout {
-  size_t X0, X1, XT0, XT1, A, B, partial, rs, d, ms, q, rho, total;
+  size_t X0, X1, A, B, partial, rs, d, ms, q, rho, total;
   int tiles;
 };
 
@@ -88,10 +88,6 @@ Layout make_layout(const Geom& g, int64_t nb, int64_t nparams, int64_t prow, boo
   L.tiles = (int)((g.mp / kPrepTile) * (g.np / kPrepTile));
   L.X0 = take((size_t)nb * g.mp * g.np * es);
   L.X1 = take((size_t)nb * g.mp * g.np * es);
-  if (g.bf) {  // bf16 mode keeps X^T next to X (the update reads it as its K-contiguous operand)
-    L.XT0 = take((size_t)nb * g.mp * g.np * es);
-    L.XT1 = take((size_t)nb * g.mp * g.np * es);
-  }
   L.A = take((size_t)nb * g.mp * g.mp * es);
   L.B = take((size_t)nb * g.mp * g.mp * es);
   L.partial = take((size_t)nb * L.tiles * 4);
@@ -221,7 +217,7 @@ struct NsJob {
 // Launch one phase (Gram, poly or update) of several jobs: problems with the
 // same tile edge share a launch (at most kMaxProblems each), longest K first
 // so that the long tiles start in the first waves.
-hipError_t launch_phase(std::vector<GemmParams>& probs, bool syrk, int cls, hipStream_t s) {
+hipError_t launch_phase(std::vector<GemmParams>& probs, bool syrk, bool nn, int cls, hipStream_t s) {
   for (int tile : {256, 128}) {
     std::vector<GemmParams*> sel;
     for (auto& p : probs)
@@ -246,7 +242,7 @@ hipError_t launch_phase(std::vector<GemmParams>& probs, bool syrk, int cls, hipS
         fl += grp.prob[i].flop;
         by += grp.prob[i].bytes;
       }
-      hipError_t e = run(cls, fl, by, s, [&]() { return launch_gemm_bf16(grp, syrk, tile, s); });
+      hipError_t e = run(cls, fl, by, s, [&]() { return launch_gemm_bf16(grp, syrk, nn, tile, s); });
       if (e != hipSuccess) return e;
     }
   }
@@ -267,7 +263,6 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
       const double m = (double)g.m, n = (double)g.n, B = (double)J.nb;
       char* ws = J.ws;
       void* X[2] = {ws + J.L.X0, ws + J.L.X1};
-      void* XT[2] = {ws + J.L.XT0, ws + J.L.XT1};
       void* A = ws + J.L.A;
       void* Bm = ws + J.L.B;
       const float* rs = (const float*)(ws + J.L.rs);
@@ -302,11 +297,12 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
         p.flop = B * m * m * m; p.bytes = B * 2 * m * m * 2;
         poly.push_back(p);
       }
-      {  // X' = B X + a X (times rs on the first iteration); X = (X^T)^T holds
-         // the same bf16 values, so a X is added inside the products
+      {  // X' = B X + a X (times rs on the first iteration): NN with Q = X,
+         // whose transposed tile is the D tile, so a X is added inside the
+         // products
         GemmParams p{};
         p.P = Bm; p.ldp = g.mp; p.sP = sa;
-        p.Q = XT[c]; p.ldq = g.mp; p.sQ = sx;
+        p.Q = X[c]; p.ldq = g.np; p.sQ = sx;
         p.dq = 1;
         p.M = (int)g.mp; p.N = (int)g.np; p.K = (int)g.mp;
         p.alpha = 1.f; p.beta = cfg.a;
@@ -320,17 +316,16 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
         } else {
           p.c_dtype = MUON_BF16;
           p.C = X[c ^ 1]; p.ldc = g.np; p.sC = sx;
-          p.Ct = XT[c ^ 1]; p.ldct = g.mp; p.sCt = sx;
           p.Mreal = (int)g.mp; p.Nreal = (int)g.np;
         }
-        p.flop = B * 2 * m * m * n; p.bytes = B * (m * m + 3 * m * n) * 2;
+        p.flop = B * 2 * m * m * n; p.bytes = B * (m * m + 2 * m * n) * 2;
         upd.push_back(p);
       }
     }
     hipError_t e;
-    if ((e = launch_phase(gram, true, MUON_K_GRAM, s)) != hipSuccess) return e;
-    if ((e = launch_phase(poly, true, MUON_K_POLY, s)) != hipSuccess) return e;
-    if ((e = launch_phase(upd, false, MUON_K_UPDATE, s)) != hipSuccess) return e;
+    if ((e = launch_phase(gram, true, false, MUON_K_GRAM, s)) != hipSuccess) return e;
+    if ((e = launch_phase(poly, true, false, MUON_K_POLY, s)) != hipSuccess) return e;
+    if ((e = launch_phase(upd, false, true, MUON_K_UPDATE, s)) != hipSuccess) return e;
     for (auto& c : cur) c ^= 1;
   }
   return hipSuccess;
@@ -526,7 +521,7 @@ int muon_ns_batched(const void* x, int32_t x_dtype, int64_t x_batch_stride, int6
     pp.x = (const char*)x + c0 * x_batch_stride * xe;
     pp.x_bs = x_batch_stride; pp.x_rs = x_row_stride;
     pp.X = ws + L.X0; pp.X_bs = g.mp * g.np;
-    pp.XT = g.bf ? ws + L.XT0 : nullptr;
+    pp.XT = nullptr;
     pp.partial = (float*)(ws + L.partial);
     hipError_t e = run(MUON_K_PREP, 0, (double)nb * rows * cols * (xe + (g.bf ? 2 : 4)), s,
                        [&]() { return launch_prep(pp, (int)nb, s); });
@@ -706,10 +701,10 @@ int stage_group(const GroupPlan& P, const muon_hparams* hp, char* ws, int64_t c0
       pp.mom[i] = g->mom[c0 + s0 + i];
     }
     pp.X = ws + L.X0 + (size_t)(s0 * P.H) * ge.mp * ge.np * (size_t)oes;
-    pp.XT = ge.bf ? ws + L.XT0 + (size_t)(s0 * P.H) * ge.mp * ge.np * (size_t)oes : nullptr;
+    pp.XT = nullptr;
     pp.X_bs = ge.mp * ge.np;
     pp.partial = (float*)(ws + L.partial) + s0 * P.H * L.tiles;
-    e = run(MUON_K_PREP, 0, (double)k * P.pelems * (ges + 2 * mes + oes * (ge.bf ? 2 : 1)), s,
+    e = run(MUON_K_PREP, 0, (double)k * P.pelems * (ges + 2 * mes + oes), s,
             [&]() { return launch_prep(pp, (int)(k * P.H), s); });
     if (e != hipSuccess) return hip_fail(e, "momentum kernel");
   }

@@ -21,7 +21,7 @@ constexpr int kPrepTile = 64;   // tile edge of the load / momentum kernel
 
 // ---- GEMM: C[b] = alpha_b * P[b] * op(Q[b]) + beta_b * D[b] -------------------
 // P is [M][K] row-major.  NT: Q is [N][K] (both operands K-contiguous).
-// NN: Q is [K][N] (fp32 kernels only).  SYRK: only tiles with tile_n >=
+// NN: Q is [K][N].  SYRK: only tiles with tile_n >=
 // tile_m are computed and each value is also written to the mirrored
 // position, so C is exactly symmetric.
 struct GemmParams {
@@ -107,7 +107,7 @@ struct ApplyParams {
 };
 
 // Launchers (return hipSuccess or the launch error).
-hipError_t launch_gemm_bf16(const GemmGroup& g, bool syrk, int tile, hipStream_t s);
+hipError_t launch_gemm_bf16(const GemmGroup& g, bool syrk, bool nn, int tile, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmParams& p, bool nn, bool syrk, hipStream_t s);
 hipError_t launch_prep(const PrepParams& p, int nb, hipStream_t s);
 hipError_t launch_norm(const NormParams& p, int nb, hipStream_t s);
