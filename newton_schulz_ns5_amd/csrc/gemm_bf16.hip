@@ -437,9 +437,10 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   //    (+ beta D when D is not folded into the products) is written back to S
   //    and stored row-major to C;
   //  - transposed pass: thread -> (column, 8 consecutive rows), stored to
-  //    T[j][i .. i+7] (SYRK: the mirrored half of C; update: X'^T).
-  // Diagonal SYRK tiles and the ragged edge of a final output fall back to
-  // element stores.
+  //    T[j][i .. i+7] (SYRK: the mirrored half of C; the final output of a
+  //    tall matrix: X'^T).
+  // Diagonal SYRK tiles, ragged edges, fp32 outputs and an explicit D take a
+  // compact generic path with element stores where needed.
   float* const S = reinterpret_cast<float*>(smem);
   const uint16_t* __restrict__ Dg = p.D ? (const uint16_t*)p.D + (int64_t)b * p.sD : nullptr;
   const bool obf = SYRK || p.c_dtype == MUON_BF16;
@@ -469,7 +470,6 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
         *(f32x4*)(base + idx * 4 + 16) = w1;
       }
     } else {
-#pragma unroll
       for (int e = 0; e < 8; ++e)
         if (e < valid) store_elem(base, idx + e, v[e], obf);
     }
@@ -479,6 +479,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   constexpr int CPR = BT / 8;        // 8-column chunks per row
   constexpr int RPI = 256 / CPR;     // rows per step of the row pass
   constexpr int NIT = RH / RPI;      // steps of the row pass
+  constexpr int R8 = RH / 8;         // 8-row chunks per pass (transposed pass)
   static_assert(RH * PITCH * 4 <= LDS_BYTES, "epilogue staging must fit");
 
   // The two passes are instantiated separately (compile-time pass index), so
@@ -500,10 +501,45 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
     __syncthreads();
     const int i0 = tm * BT + pass * RH;
     const int j0 = tn * BT;
-    {
+    // Almost every tile: all its rows and columns are stored, bf16, no D, off
+    // the SYRK diagonal, aligned rows.  Then both passes store
+    // bf16(alpha S) with 16-byte stores and nothing else; the transposed
+    // pass recomputes alpha S, so its values are bitwise those of the row
+    // pass.
+    const bool fast = obf && !Dg && !diag && i0 + RH <= Mlim && j0 + BT <= Nlim && (!Cg || cvec) && (!Tg || tvec);
+    if (fast) {
+      if (Cg) {
+        const int c8 = (tid % CPR) * 8, r0 = tid / CPR;
+#pragma unroll 4
+        for (int it = 0; it < NIT; ++it) {
+          const int rr = r0 + it * RPI;
+          const float* srow = S + rr * PITCH + c8;
+          const f32x4 s0 = *(const f32x4*)srow, s1 = *(const f32x4*)(srow + 4);
+          u32x4 w;
+          w[0] = pack_bf2(alpha * s0[0], alpha * s0[1]);
+          w[1] = pack_bf2(alpha * s0[2], alpha * s0[3]);
+          w[2] = pack_bf2(alpha * s1[0], alpha * s1[1]);
+          w[3] = pack_bf2(alpha * s1[2], alpha * s1[3]);
+          *(u32x4*)(Cg + ((int64_t)(i0 + rr) * ldc + j0 + c8) * 2) = w;
+        }
+      }
+      if (Tg) {
+#pragma unroll 2
+        for (int idx = tid; idx < BT * R8; idx += 256) {
+          const int jj = idx % BT, i8 = (idx / BT) * 8;
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            w[e] = pack_bf2(alpha * S[(i8 + 2 * e) * PITCH + jj], alpha * S[(i8 + 2 * e + 1) * PITCH + jj]);
+          *(u32x4*)(Tg + ((int64_t)(j0 + jj) * ldt + i0 + i8) * 2) = w;
+        }
+      }
+    } else {
+      // Edges, the SYRK diagonal, fp32 output, an explicit D: element-wise
+      // where needed, through v = alpha S (+ beta D) written back to S.
       const int c8 = (tid % CPR) * 8, r0 = tid / CPR;
       const int j = j0 + c8;
-#pragma unroll
+#pragma unroll 1
       for (int it = 0; it < NIT; ++it) {
         const int rr = r0 + it * RPI;
         const int i = i0 + rr;
@@ -512,7 +548,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
         float v[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) { v[e] = alpha * s0[e]; v[4 + e] = alpha * s1[e]; }
-        if (Dg) {  // only when beta D is not folded into the products
+        if (Dg && i < Mlim && j < Nlim) {  // D is padded like the output: whole chunks are in bounds
           const u32x4 dv = *(const u32x4*)(Dg + (int64_t)i * p.ldd + j);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -526,7 +562,6 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
         *(f32x4*)(srow + 4) = s1;
         if (Cg && i < Mlim) {
           if (diag) {
-#pragma unroll
             for (int e = 0; e < 8; ++e)
               if (i <= j + e) store_elem(Cg, (int64_t)i * ldc + j + e, v[e], obf);
           } else {
@@ -534,23 +569,22 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
           }
         }
       }
-    }
-    if (Tg) {
-      __syncthreads();
-      constexpr int R8 = RH / 8;  // 8-row chunks per pass
-      for (int idx = tid; idx < BT * R8; idx += 256) {
-        const int jj = idx % BT, i8 = (idx / BT) * 8;
-        const int j = j0 + jj, i = i0 + i8;
-        float v[8];
+      if (Tg) {
+        __syncthreads();
+#pragma unroll 1
+        for (int idx = tid; idx < BT * R8; idx += 256) {
+          const int jj = idx % BT, i8 = (idx / BT) * 8;
+          const int jt = j0 + jj, it8 = i0 + i8;
+          float v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = S[(i8 + e) * PITCH + jj];
-        if (j < Nlim) {
-          if (diag) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (i + e < j) store_elem(Tg, (int64_t)j * ldt + i + e, v[e], obf);
-          } else {
-            store8(Tg, (int64_t)j * ldt + i, v, Mlim - i, tvec);
+          for (int e = 0; e < 8; ++e) v[e] = S[(i8 + e) * PITCH + jj];
+          if (jt < Nlim) {
+            if (diag) {
+              for (int e = 0; e < 8; ++e)
+                if (it8 + e < jt) store_elem(Tg, (int64_t)jt * ldt + it8 + e, v[e], obf);
+            } else {
+              store8(Tg, (int64_t)jt * ldt + it8, v, Mlim - it8, tvec);
+            }
           }
         }
       }
