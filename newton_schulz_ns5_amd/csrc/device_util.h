@@ -12,17 +12,18 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// float -> bf16, round to nearest even; NaN stays NaN (quiet).
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// float -> bf16 pair, round to nearest even, NaN kept (quiet): one
+// v_cvt_pk_bf16_f32.  On gfx950 it gives the same bits as rounding the fp32
+// pattern in integer arithmetic (add 0x7fff plus the kept lsb, set the quiet
+// bit of a NaN), checked over ties, denormals, overflow and NaNs.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
-}
+__device__ __forceinline__ uint16_t f2bf(float f) { return (uint16_t)pack_bf2(f, 0.f); }
 
 // Sum over the 64 lanes of a wavefront with an xor butterfly.  Every lane
 // ends with the same, bitwise identical value (each pairwise step adds the
