@@ -501,12 +501,14 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
     __syncthreads();
     const int i0 = tm * BT + pass * RH;
     const int j0 = tn * BT;
-    // Almost every tile: all its rows and columns are stored, bf16, no D, off
-    // the SYRK diagonal, aligned rows.  Then both passes store
-    // bf16(alpha S) with 16-byte stores and nothing else; the transposed
-    // pass recomputes alpha S, so its values are bitwise those of the row
-    // pass.
-    const bool fast = obf && !Dg && !diag && i0 + RH <= Mlim && j0 + BT <= Nlim && (!Cg || cvec) && (!Tg || tvec);
+    // Almost every tile: all its rows and columns are stored, bf16, no D,
+    // aligned rows.  Then both passes store bf16(alpha S) with 16-byte stores;
+    // the transposed pass recomputes alpha S, so its values are bitwise
+    // those of the row pass.  On a SYRK diagonal tile the row pass stores
+    // the chunks on or above the diagonal (element stores where the diagonal
+    // crosses a chunk) and the transposed pass mirrors the strictly upper
+    // part, so the stored matrix is exactly symmetric.
+    const bool fast = obf && !Dg && i0 + RH <= Mlim && j0 + BT <= Nlim && (!Cg || cvec) && (!Tg || tvec);
     if (fast) {
       if (Cg) {
         const int c8 = (tid % CPR) * 8, r0 = tid / CPR;
@@ -520,18 +522,32 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
           w[1] = pack_bf2(alpha * s0[2], alpha * s0[3]);
           w[2] = pack_bf2(alpha * s1[0], alpha * s1[1]);
           w[3] = pack_bf2(alpha * s1[2], alpha * s1[3]);
-          *(u32x4*)(Cg + ((int64_t)(i0 + rr) * ldc + j0 + c8) * 2) = w;
+          uint8_t* const dst = Cg + ((int64_t)(i0 + rr) * ldc + j0 + c8) * 2;
+          const int lo = pass * RH + rr - c8;  // columns c8 + e with e >= lo are on or above the diagonal
+          if (!diag || lo <= 0) {
+            *(u32x4*)dst = w;
+          } else if (lo < 8) {
+            for (int e = lo; e < 8; ++e) ((uint16_t*)dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+          }
         }
       }
       if (Tg) {
 #pragma unroll 2
         for (int idx = tid; idx < BT * R8; idx += 256) {
           const int jj = idx % BT, i8 = (idx / BT) * 8;
+          // mirrored rows i8 + e (tile rows pass * RH + i8 + e) strictly below column jj
+          const int hi = diag ? jj - (pass * RH + i8) : 8;
+          if (hi <= 0) continue;
           u32x4 w;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             w[e] = pack_bf2(alpha * S[(i8 + 2 * e) * PITCH + jj], alpha * S[(i8 + 2 * e + 1) * PITCH + jj]);
-          *(u32x4*)(Tg + ((int64_t)(j0 + jj) * ldt + i0 + i8) * 2) = w;
+          uint8_t* const dst = Tg + ((int64_t)(j0 + jj) * ldt + i0 + i8) * 2;
+          if (hi >= 8) {
+            *(u32x4*)dst = w;
+          } else {
+            for (int e = 0; e < hi; ++e) ((uint16_t*)dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+          }
         }
       }
     } else {
