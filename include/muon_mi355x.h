@@ -44,6 +44,12 @@
  *    per-parameter tensors of the step entry points must be 16-byte aligned
  *    (as every tensor allocation is).  Workspaces must be 256-byte aligned.
  *  - Zero-sized problems (n == 0, rows == 0 or cols == 0) are valid no-ops.
+ *  - With launch timing off (the default) a call only launches kernels on
+ *    `stream`: no allocation, no memset, no synchronization.  A call can
+ *    therefore be captured into a HIP graph and replayed (the pointers and
+ *    scalars are fixed at capture; the data they point to may change between
+ *    replays).  Calls made while timing is on record events and must not be
+ *    captured.
  *  - Size limits: rows and cols of one matrix at most 4194176 (2^22 - 128),
  *    and (rows rounded up to 128) x (cols rounded up to 128) below 2^31;
  *    larger matrices fail with MUON_ERR_INVALID_ARG.

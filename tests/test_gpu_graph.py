@@ -1,0 +1,84 @@
+"""A whole optimizer step captured in a HIP graph.
+
+The library only enqueues kernels on the caller's stream (no allocation, no
+memset, no synchronization while launch timing is off), so a
+``muon_step_groups`` call can be captured once and replayed.  The graph is
+replayed three times, each time after new gradients are written into its
+static input tensors and after eager steps of an identical copy of the state,
+and every replay is compared bitwise with the eager result.
+"""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import to_dev, torch_cuda
+
+import newton_schulz_ns5_amd as ns
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [((256, 512), 2, 1), ((384, 128), 1, 1), ((512, 256), 2, 4)]   # (shape, n, heads)
+
+
+def make_states(torch, seed):
+    out = []
+    for k, (shape, n, heads) in enumerate(SHAPES):
+        w = [to_dev(synth.gaussian(shape, (seed, k, i, 0, synth.ROLE_WEIGHT), "f32", std=0.02), "f32")
+             for i in range(n)]
+        out.append({
+            "w_master": w,
+            "moms": [torch.zeros(shape, dtype=torch.bfloat16, device="cuda") for _ in range(n)],
+            "variances": [torch.zeros(shape[0], device="cuda") for _ in range(n)],
+            "w_model": [t.to(torch.bfloat16) for t in w],
+            "heads": heads,
+        })
+    return out
+
+
+def grads(seed, step):
+    return [[synth.power_law(shape, (seed, k, 0), (seed, k, i, step)) for i in range(n)]
+            for k, (shape, n, _) in enumerate(SHAPES)]
+
+
+def test_step_groups_graph_replay_matches_eager():
+    torch = torch_cuda()
+    hp = ns.hparams(normuon=True, ns=ns.ns_config(compute_dtype="bf16"))
+    eager = make_states(torch, 31)
+    graphed = make_states(torch, 31)
+    static_g = [[torch.empty(shape, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+                for shape, n, _ in SHAPES]
+    for st, g in zip(graphed, static_g):
+        st["grads"] = g
+    need = ns.step_groups_workspace_bytes([ns._make_group(st["w_master"], st["grads"], st["moms"],
+                                                          st["variances"], st["w_model"], st["heads"])[0]
+                                           for st in graphed], hp)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    # The captured call must not be the first use of the library in the process.
+    ns.lib()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            ns.step_groups(graphed, hp=hp, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    # Capture enqueues nothing: the graphed state is still the initial one.
+    for a, b in zip(eager, graphed):
+        for x, y in zip(a["w_master"], b["w_master"]):
+            assert torch.equal(x, y)
+    for step in (1, 2, 3):
+        gs = grads(31, step)
+        for k in range(len(SHAPES)):
+            for i, g in enumerate(gs[k]):
+                static_g[k][i].copy_(to_dev(g, "bf16"))
+            eager[k]["grads"] = [to_dev(g, "bf16") for g in gs[k]]
+        ns.step_groups(eager, hp=hp)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, (a, b) in enumerate(zip(eager, graphed)):
+            for key in ("w_master", "moms", "variances", "w_model"):
+                for x, y in zip(a[key], b[key]):
+                    assert torch.equal(x, y), (step, k, key)
