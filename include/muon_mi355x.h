@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 1
+#define MUON_ABI_VERSION 2
 /* Layout of the caller-owned optimizer state: momentum has the parameter's
  * shape and dtype; the NorMuon variance is one fp32 value per output channel
  * ([ConvFix] "What it does"). */
@@ -91,21 +91,26 @@ extern "C" {
  * orthogonalized through its transpose and returned in its own orientation.
  * compute_dtype MUON_BF16: X, A, B are stored in bf16 between kernels and all
  * products accumulate in fp32 on bf16 MFMA; MUON_F32: everything is fp32
- * (fp32 MFMA). */
+ * (fp32 MFMA).
+ * schedule 1 runs iteration k with coeffs[k] instead of (a, b, c): a
+ * per-iteration coefficient schedule (the Polar-Express-style schedules
+ * [ConvFix] mentions; the pages give no values). */
+#define MUON_NS_MAX_STEPS 64
 typedef struct muon_ns_config {
-  int32_t steps;          /* iterations, 1..64 (5) */
+  int32_t steps;          /* iterations, 1..MUON_NS_MAX_STEPS (5) */
   float a, b, c;          /* (3.4445, -4.7750, 2.0315) */
   float eps;              /* added to the Frobenius norm (1e-7) */
   int32_t compute_dtype;  /* MUON_BF16 or MUON_F32 */
-  int32_t reserved;       /* must be 0 */
+  int32_t schedule;       /* 0: (a, b, c) in every iteration; 1: coeffs[k] in iteration k */
   int64_t max_batch;      /* most matrices (or parameters, for muon_step_group)
                              processed at once; 0 = all.  Bounds the workspace
                              like ns_batch_size ([LSMuon] _run_ns); results do
                              not depend on it. */
+  float coeffs[MUON_NS_MAX_STEPS][3];  /* per-iteration (a, b, c); entries past `steps` unused */
 } muon_ns_config;
 
-/* Fills *cfg with steps 5, the quintic coefficients above, eps 1e-7,
- * compute_dtype MUON_BF16, max_batch 0. */
+/* Fills *cfg with steps 5, the quintic coefficients above (also in every row
+ * of coeffs), schedule 0, eps 1e-7, compute_dtype MUON_BF16, max_batch 0. */
 void muon_ns_default_config(muon_ns_config* cfg);
 
 int muon_abi_version(void);

@@ -63,14 +63,33 @@ def state_layout_version():
 
 
 def ns_config(steps=5, coeffs=QUINTIC, eps=1e-7, compute_dtype="bf16", max_batch=0):
+    """Newton-Schulz configuration.  ``coeffs`` is one (a, b, c) triple for every
+    iteration, or a sequence of ``steps`` triples (a per-iteration schedule)."""
     c = NSConfig()
     lib().muon_ns_default_config(ctypes.byref(c))
     c.steps = int(steps)
-    c.a, c.b, c.c = (float(v) for v in coeffs)
+    rows = [tuple(float(v) for v in t) for t in coeffs] if _is_schedule(coeffs) else None
+    if rows is None:
+        c.a, c.b, c.c = (float(v) for v in coeffs)
+    else:
+        if len(rows) != c.steps or any(len(r) != 3 for r in rows) or c.steps > _lib.NS_MAX_STEPS:
+            raise MuonError(_lib.MUON_ERR_INVALID_ARG, "a schedule needs one (a, b, c) per iteration")
+        c.schedule = 1
+        c.a, c.b, c.c = rows[0]
+        for k, r in enumerate(rows):
+            for j in range(3):
+                c.coeffs[k][j] = r[j]
     c.eps = float(eps)
     c.compute_dtype = _cdt(compute_dtype)
     c.max_batch = int(max_batch)
     return c
+
+
+def _is_schedule(coeffs):
+    try:
+        return len(coeffs) > 0 and hasattr(coeffs[0], "__len__")
+    except TypeError:
+        return False
 
 
 def hparams(lr=0.05, momentum=0.95, nesterov=True, weight_decay=0.0, extra_scale=1.0, normuon=False,

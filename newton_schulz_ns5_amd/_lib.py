@@ -27,9 +27,13 @@ c_i32, c_i64, c_f32, c_f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, cty
 c_vp, c_sz = ctypes.c_void_p, ctypes.c_size_t
 
 
+NS_MAX_STEPS = 64
+
+
 class NSConfig(ctypes.Structure):
     _fields_ = [("steps", c_i32), ("a", c_f32), ("b", c_f32), ("c", c_f32), ("eps", c_f32),
-                ("compute_dtype", c_i32), ("reserved", c_i32), ("max_batch", c_i64)]
+                ("compute_dtype", c_i32), ("schedule", c_i32), ("max_batch", c_i64),
+                ("coeffs", (c_f32 * 3) * NS_MAX_STEPS)]
 
 
 class Group(ctypes.Structure):

@@ -167,12 +167,16 @@ hipError_t drain_pending() {
 // ---- validation helpers ------------------------------------------------------
 int check_cfg(const muon_ns_config* c) {
   if (!c) return fail(MUON_ERR_INVALID_ARG, "ns config is NULL");
-  if (c->steps < 1 || c->steps > 64) return fail(MUON_ERR_INVALID_ARG, "steps must be in 1..64 (got %d)", c->steps);
+  if (c->steps < 1 || c->steps > MUON_NS_MAX_STEPS) return fail(MUON_ERR_INVALID_ARG, "steps must be in 1..MUON_NS_MAX_STEPS (got %d)", c->steps);
   if (!dtype_ok(c->compute_dtype)) return fail(MUON_ERR_UNSUPPORTED, "compute_dtype %d is not MUON_BF16 or MUON_F32", c->compute_dtype);
-  if (c->reserved != 0) return fail(MUON_ERR_INVALID_ARG, "reserved field must be 0");
+  if (c->schedule != 0 && c->schedule != 1) return fail(MUON_ERR_INVALID_ARG, "schedule must be 0 or 1 (got %d)", c->schedule);
   if (c->max_batch < 0) return fail(MUON_ERR_INVALID_ARG, "max_batch must be >= 0");
   if (!std::isfinite(c->a) || !std::isfinite(c->b) || !std::isfinite(c->c) || !std::isfinite(c->eps) || c->eps < 0)
     return fail(MUON_ERR_INVALID_ARG, "coefficients must be finite and eps >= 0");
+  if (c->schedule)
+    for (int k = 0; k < c->steps; ++k)
+      for (int j = 0; j < 3; ++j)
+        if (!std::isfinite(c->coeffs[k][j])) return fail(MUON_ERR_INVALID_ARG, "coeffs[%d][%d] is not finite", k, j);
   return MUON_OK;
 }
 
@@ -252,10 +256,18 @@ hipError_t launch_phase(std::vector<GemmParams>& probs, bool syrk, bool nn, int 
 // bf16 mode: every product is NT.  X and X^T ping-pong between two buffer
 // pairs; the update writes both (or, on the last iteration, the output in
 // parameter orientation).
+// (a, b, c) of iteration `it`.
+struct Coeffs { float a, b, c; };
+Coeffs coeffs_of(const muon_ns_config& cfg, int it) {
+  if (cfg.schedule) return {cfg.coeffs[it][0], cfg.coeffs[it][1], cfg.coeffs[it][2]};
+  return {cfg.a, cfg.b, cfg.c};
+}
+
 hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_config& cfg, hipStream_t s) {
   std::vector<int> cur(jobs.size(), 0);
   for (int it = 0; it < cfg.steps; ++it) {
     const bool first = it == 0, last = it == cfg.steps - 1;
+    const Coeffs cf = coeffs_of(cfg, it);
     std::vector<GemmParams> gram, poly, upd;
     for (size_t k = 0; k < jobs.size(); ++k) {
       const NsJob& J = jobs[k];
@@ -285,14 +297,14 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
         GemmParams p{};
         p.P = A; p.ldp = g.mp; p.sP = sa;
         p.Q = A; p.ldq = g.mp; p.sQ = sa;
-        if (cfg.c != 0.f) {
+        if (cf.c != 0.f) {
           p.dq = 1;
         } else {
           p.D = A; p.ldd = g.mp; p.sD = sa;
         }
         p.C = Bm; p.ldc = g.mp; p.sC = sa; p.c_dtype = MUON_BF16;
         p.M = p.N = p.K = (int)g.mp; p.Mreal = p.Nreal = (int)g.mp;
-        p.alpha = cfg.c; p.beta = cfg.b;
+        p.alpha = cf.c; p.beta = cf.b;
         p.batch = (int)J.nb;
         p.flop = B * m * m * m; p.bytes = B * 2 * m * m * 2;
         poly.push_back(p);
@@ -305,7 +317,7 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
         p.Q = X[c]; p.ldq = g.np; p.sQ = sx;
         p.dq = 1;
         p.M = (int)g.mp; p.N = (int)g.np; p.K = (int)g.mp;
-        p.alpha = 1.f; p.beta = cfg.a;
+        p.alpha = 1.f; p.beta = cf.a;
         p.rs = first ? rs : nullptr; p.alpha_pow = 1; p.beta_pow = 1;
         p.batch = (int)J.nb;
         if (last) {
@@ -345,6 +357,7 @@ hipError_t ns_iterations_f32(const Geom& g, int64_t nb, const muon_ns_config& cf
   const int64_t sx = g.mp * g.np, sa = g.mp * g.mp;
   for (int it = 0; it < cfg.steps; ++it) {
     const bool first = it == 0, last = it == cfg.steps - 1;
+    const Coeffs cf = coeffs_of(cfg, it);
     hipError_t e;
     {  // A = X X^T (times rs^2 on the first iteration, which folds in the normalization)
       GemmParams p{};
@@ -365,7 +378,7 @@ hipError_t ns_iterations_f32(const Geom& g, int64_t nb, const muon_ns_config& cf
       p.D = A; p.ldd = g.mp; p.sD = sa;
       p.C = Bm; p.ldc = g.mp; p.sC = sa; p.c_dtype = wdt;
       p.M = p.N = p.K = (int)g.mp; p.Mreal = p.Nreal = (int)g.mp;
-      p.alpha = cfg.c; p.beta = cfg.b;
+      p.alpha = cf.c; p.beta = cf.b;
       p.batch = (int)nb;
       e = gemm_f32(p, false, true, MUON_K_POLY, B * m * m * m, B * 2 * m * m * es, s);
       if (e != hipSuccess) return e;
@@ -376,7 +389,7 @@ hipError_t ns_iterations_f32(const Geom& g, int64_t nb, const muon_ns_config& cf
       p.Q = xin; p.ldq = g.np; p.sQ = sx;
       p.D = xin; p.ldd = g.np; p.sD = sx;
       p.M = (int)g.mp; p.N = (int)g.np; p.K = (int)g.mp;
-      p.alpha = 1.f; p.beta = cfg.a;
+      p.alpha = 1.f; p.beta = cf.a;
       p.rs = first ? rs : nullptr; p.alpha_pow = 1; p.beta_pow = 1;
       p.batch = (int)nb;
       if (last) {
@@ -435,6 +448,11 @@ void muon_ns_default_config(muon_ns_config* cfg) {
   cfg->eps = 1e-7f;
   cfg->compute_dtype = MUON_BF16;
   cfg->max_batch = 0;
+  for (int k = 0; k < MUON_NS_MAX_STEPS; ++k) {
+    cfg->coeffs[k][0] = cfg->a;
+    cfg->coeffs[k][1] = cfg->b;
+    cfg->coeffs[k][2] = cfg->c;
+  }
 }
 
 void muon_default_hparams(muon_hparams* hp) {

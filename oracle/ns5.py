@@ -9,6 +9,11 @@ A = X X^T and B = b A + c A^2, after which X <- a X + B X.  The coefficients
 (a, b, c) = (3.4445, -4.7750, 2.0315) are the quintic ones of the workload
 definition and are used unchanged in all five iterations.
 
+A per-iteration schedule (one (a, b, c) triple per iteration, as the
+Polar-Express-style schedules that "Fix convolution flattening in megabatches
+and NorMuon normalization" mentions; the pages print none) runs iteration k
+with the k-th triple.
+
 Readings where the pages are silent:
 * eps is added to the norm: X0 = G / (||G||_F + eps).
 * A matrix with more rows than columns is transposed first and transposed back
@@ -25,17 +30,26 @@ def frobenius_normalize(g, eps=1e-7):
     return g / (np.sqrt(np.sum(g * g)) + eps)
 
 
+def schedule(coeffs, steps):
+    """The (a, b, c) of each iteration: one triple for all, or one per iteration."""
+    t = np.asarray(coeffs, dtype=np.float64)
+    if t.shape == (3,):
+        return [tuple(float(v) for v in t)] * int(steps)
+    if t.shape == (int(steps), 3):
+        return [tuple(float(v) for v in row) for row in t]
+    raise ValueError("coeffs must be (a, b, c) or one (a, b, c) per iteration")
+
+
 def newton_schulz5(g, steps=5, coeffs=QUINTIC, eps=1e-7):
     """Orthogonalize one matrix.  float64 in, float64 out, same shape."""
     g = np.asarray(g, dtype=np.float64)
     if g.ndim != 2:
         raise ValueError("newton_schulz5 takes one 2-D matrix")
-    a, b, c = (float(t) for t in coeffs)
     x = frobenius_normalize(g, eps)
     tall = x.shape[0] > x.shape[1]
     if tall:
         x = np.ascontiguousarray(x.T)
-    for _ in range(int(steps)):
+    for a, b, c in schedule(coeffs, steps):
         gram = x @ x.T                       # A = X X^T
         poly = b * gram + c * (gram @ gram)  # B = b A + c A^2
         x = a * x + poly @ x                 # X <- a X + B X

@@ -48,7 +48,8 @@ int main(void) {
   printf("muon_group %zu\n", sizeof(muon_group));
   printf("muon_hparams %zu\n", sizeof(muon_hparams));
   F(muon_ns_config, steps); F(muon_ns_config, a); F(muon_ns_config, b); F(muon_ns_config, c);
-  F(muon_ns_config, eps); F(muon_ns_config, compute_dtype); F(muon_ns_config, reserved); F(muon_ns_config, max_batch);
+  F(muon_ns_config, eps); F(muon_ns_config, compute_dtype); F(muon_ns_config, schedule); F(muon_ns_config, max_batch);
+  F(muon_ns_config, coeffs);
   F(muon_group, n); F(muon_group, rows); F(muon_group, cols); F(muon_group, heads); F(muon_group, grad_dtype);
   F(muon_group, mom_dtype); F(muon_group, model_dtype); F(muon_group, reserved); F(muon_group, w_master);
   F(muon_group, w_model); F(muon_group, grad); F(muon_group, mom); F(muon_group, var);
@@ -86,7 +87,7 @@ def test_one_hip_runtime_per_process():
 
 def test_versions_and_status_strings():
     L = m.lib()
-    assert L.muon_abi_version() == 1 and L.muon_state_layout_version() == 1
+    assert L.muon_abi_version() == 2 and L.muon_state_layout_version() == 1
     for code, word in [(0, b"ok"), (-1, b"invalid"), (-2, b"unsupported"), (-3, b"workspace"), (-4, b"HIP")]:
         assert word in L.muon_status_string(code)
     assert L.muon_kernel_class_name(4) == b"update"
@@ -135,8 +136,24 @@ def test_ns_batched_unsupported_compute_dtype():
     c.compute_dtype = 5
     assert ns_call(cfg=c) == -2
     c = m.ns_config()
-    c.reserved = 1
+    c.schedule = 2
     assert ns_call(cfg=c) == -1
+
+
+def test_ns_config_schedule_fields():
+    sched = [(3.4445, -4.775, 2.0315)] * 4 + [(1.875, -1.25, 0.375)]
+    c = m.ns_config(coeffs=sched)
+    assert c.schedule == 1 and c.steps == 5
+    assert abs(c.coeffs[4][0] - 1.875) < 1e-7 and abs(c.coeffs[0][2] - 2.0315) < 1e-6
+    d = m.ns_config()
+    assert d.schedule == 0 and abs(d.coeffs[63][1] + 4.775) < 1e-6   # defaults fill every row
+    c.coeffs[2][1] = float("nan")
+    assert ns_call(cfg=c) == -1
+    c.coeffs[2][1] = -4.775
+    c.coeffs[7][0] = float("inf")                                      # past `steps`: unused
+    assert m.ns_workspace_bytes(2, 64, 96, c) > 0
+    with pytest.raises(m.MuonError):
+        m.ns_config(coeffs=sched[:3])
 
 
 @pytest.mark.parametrize("over", [dict(n=0), dict(rows=0), dict(cols=0), dict(n=0, x=0, y=0, ws=0)])

@@ -173,3 +173,31 @@ def test_strided_row_views():
     ref = ns.ns_batched(view.contiguous())
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
+
+
+# ---- per-iteration coefficient schedules ------------------------------------
+SCHEDULE = [oracle.QUINTIC] * 4 + [(15 / 8, -10 / 8, 3 / 8)]   # four quintic steps, then the classical polynomial
+
+
+@pytest.mark.parametrize("compute", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(2, 300, 520), (1, 384, 256)])
+def test_schedule_parity(shape, compute):
+    torch = torch_cuda()
+    dt = "bf16" if compute == "bf16" else "f32"
+    x = synth.gaussian(shape, (21, shape[1], shape[2], 1, 0), dt)
+    out = ns.ns_batched(to_dev(x, dt), steps=5, coeffs=SCHEDULE, compute_dtype=compute)
+    torch.cuda.synchronize()
+    got, xin = to_f64(out), storage_f64(x, dt)
+    err = max(rel_fro(got[i], oracle.newton_schulz5(xin[i], steps=5, coeffs=SCHEDULE)) for i in range(shape[0]))
+    assert err <= TOL[compute], err
+    # and it is not the constant-coefficient result
+    assert rel_fro(got[0], oracle.newton_schulz5(xin[0])) > 0.05
+
+
+def test_constant_schedule_is_bitwise_the_scalar_path():
+    torch = torch_cuda()
+    xt = to_dev(synth.gaussian((2, 256, 640), (22, 0, 0, 1, 0), "bf16"), "bf16")
+    a = ns.ns_batched(xt)
+    b = ns.ns_batched(xt, steps=5, coeffs=[oracle.QUINTIC] * 5)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

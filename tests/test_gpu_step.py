@@ -230,3 +230,18 @@ def test_empty_group_is_noop():
     ns.step_group(w, [torch.zeros((0, 16), dtype=torch.bfloat16, device="cuda")],
                   [torch.zeros((0, 16), dtype=torch.bfloat16, device="cuda")])
     torch.cuda.synchronize()
+
+
+def test_step_with_coefficient_schedule():
+    # A per-iteration schedule reaches the step through the hparams' ns config.
+    torch = torch_cuda()
+    sched = [oracle.QUINTIC] * 4 + [(15 / 8, -10 / 8, 3 / 8)]
+    shape = (256, 384)
+    g = grads_for(12, 1, shape, "bf16", 1, power=True)[0]
+    w0 = make_state(12, 1, shape, "bf16", "bf16")[0]
+    W, M = [to_dev(w0, "f32")], [torch.zeros(shape, dtype=torch.bfloat16, device="cuda")]
+    ns.step_group(W, [to_dev(g, "bf16")], M, ns=ns.ns_config(steps=5, coeffs=sched))
+    torch.cuda.synchronize()
+    hp = oracle.MuonHParams(coeffs=sched, mom_dtype="bf16")
+    r = oracle.muon_step(w0.astype(np.float64), storage_f64(g, "bf16"), np.zeros(shape), np.zeros(shape[0]), hp)
+    assert rel_fro(to_f64(W[0]) - w0, r["w"] - w0) <= TOL["bf16"]

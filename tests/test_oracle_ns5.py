@@ -179,3 +179,58 @@ def test_per_head_with_one_head_is_plain_ns():
 def test_per_head_rejects_uneven_heads():
     with pytest.raises(ValueError):
         ns5_per_head(np.ones((10, 4)), 3)
+
+
+# ---- per-iteration coefficient schedules ------------------------------------
+CLASSICAL = (15 / 8, -10 / 8, 3 / 8)   # p(s) = (15 s - 10 s^3 + 3 s^5) / 8: p(1) = 1, p'(1) = 0
+
+
+def _phi(coeffs, s):
+    a, b, c = coeffs
+    return a * s + b * s ** 3 + c * s ** 5
+
+
+def test_schedule_of_identical_rows_equals_constant_coefficients():
+    g = np.random.default_rng(11).standard_normal((24, 40))
+    assert np.array_equal(oracle.newton_schulz5(g, coeffs=[oracle.QUINTIC] * 5), oracle.newton_schulz5(g))
+
+
+def test_schedule_svd_closed_form():
+    # NS with (a_k, b_k, c_k) maps every singular value s of G/(||G||+eps)
+    # through phi_K o ... o phi_1 and keeps the singular vectors.
+    rng = np.random.default_rng(12)
+    g = rng.standard_normal((30, 50))
+    sched = [oracle.QUINTIC] * 3 + [CLASSICAL] * 2
+    u, sv, vt = np.linalg.svd(g, full_matrices=False)
+    s = sv / (np.sqrt(np.sum(g * g)) + 1e-7)
+    for co in sched:
+        s = _phi(co, s)
+    want = (u * s[None, :]) @ vt
+    got = oracle.newton_schulz5(g, steps=5, coeffs=sched)
+    assert np.max(np.abs(got - want)) < 1e-12
+
+
+def test_schedule_order_matters():
+    g = np.random.default_rng(13).standard_normal((16, 32))
+    sched = [oracle.QUINTIC, oracle.QUINTIC, CLASSICAL]
+    rev = sched[::-1]
+    assert np.max(np.abs(oracle.newton_schulz5(g, steps=3, coeffs=sched)
+                         - oracle.newton_schulz5(g, steps=3, coeffs=rev))) > 1e-3
+
+
+def test_classical_tail_converges_to_the_polar_factor():
+    # Quintic steps bring every singular value near 1; the classical
+    # polynomial (fixed point 1, zero derivative there) then converges to the
+    # exact polar factor U V^T of G.
+    rng = np.random.default_rng(14)
+    u, _ = np.linalg.qr(rng.standard_normal((20, 20)))
+    v, _ = np.linalg.qr(rng.standard_normal((36, 20)))
+    g = (u * np.linspace(0.2, 1.0, 20)[None, :]) @ v.T
+    sched = [oracle.QUINTIC] * 5 + [CLASSICAL] * 6
+    got = oracle.newton_schulz5(g, steps=11, coeffs=sched)
+    assert np.max(np.abs(got - u @ v.T)) < 1e-10
+
+
+def test_schedule_shape_is_checked():
+    with pytest.raises(ValueError):
+        oracle.newton_schulz5(np.eye(4), steps=5, coeffs=[oracle.QUINTIC] * 4)
