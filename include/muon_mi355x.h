@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 2
+#define MUON_ABI_VERSION 3
 /* Layout of the caller-owned optimizer state: momentum has the parameter's
  * shape and dtype; the NorMuon variance is one fp32 value per output channel
  * ([ConvFix] "What it does"). */
@@ -191,6 +191,11 @@ typedef struct muon_group {
   const void* const* grad; /* n x grad_dtype [rows][cols] */
   void* const* mom;        /* n x mom_dtype [rows][cols], updated in place */
   float* const* var;       /* n x fp32 [rows] NorMuon variance, updated in place; NULL without NorMuon */
+  int64_t nsplit;          /* 0, or the number of row blocks (heads must then be 1) */
+  const int64_t* split_rows; /* nsplit block heights (host, read during the call), > 0, summing to rows:
+                                NS runs on each block [r0, r0 + h) of every parameter (a fused
+                                q/k/v weight split on its rows); momentum, NorMuon and the update
+                                act on the whole parameter */
 } muon_group;
 
 /* Step hyper-parameters.  [LSMuon] LayerShardedMuon: lr, momentum,

@@ -194,7 +194,7 @@ def _ptr_array(ts):
     return arr
 
 
-def _make_group(w_master, grads, moms, variances=None, w_model=None, heads=1):
+def _make_group(w_master, grads, moms, variances=None, w_model=None, heads=1, split_rows=None):
     n = len(w_master)
     if not (len(grads) == len(moms) == n):
         raise MuonError(_lib.MUON_ERR_INVALID_ARG, "w_master, grads and moms must have the same length")
@@ -220,6 +220,13 @@ def _make_group(w_master, grads, moms, variances=None, w_model=None, heads=1):
     if w_model:
         keep.append(_ptr_array(w_model))
         g.w_model = ctypes.cast(keep[-1], ctypes.POINTER(ctypes.c_void_p))
+    if split_rows:
+        if len(shape) != 2:
+            # Row blocks are cut on dim -2, which is the row axis of 2-D weights only.
+            raise MuonError(_lib.MUON_ERR_INVALID_ARG, "split_rows needs 2-D parameters")
+        keep.append((ctypes.c_int64 * len(split_rows))(*[int(h) for h in split_rows]))
+        g.nsplit = len(split_rows)
+        g.split_rows = ctypes.cast(keep[-1], ctypes.POINTER(ctypes.c_int64))
     return g, keep
 
 
@@ -229,10 +236,16 @@ def step_workspace_bytes(group, hp):
     return out.value
 
 
-def step_group(w_master, grads, moms, variances=None, w_model=None, *, heads=1, hp=None, workspace=None, **kw):
-    """One Muon / NorMuon step for a list of same-shape parameters (see muon_step_group)."""
+def step_group(w_master, grads, moms, variances=None, w_model=None, *, heads=1, split_rows=None, hp=None,
+               workspace=None, **kw):
+    """One Muon / NorMuon step for a list of same-shape parameters (see muon_step_group).
+
+    ``split_rows`` (a list of block heights summing to the row count) runs
+    Newton-Schulz on each row block of every parameter on its own, e.g. the q,
+    k and v blocks of a fused projection weight.
+    """
     hp = hp if hp is not None else hparams(**kw)
-    g, keep = _make_group(w_master, grads, moms, variances, w_model, heads)
+    g, keep = _make_group(w_master, grads, moms, variances, w_model, heads, split_rows)
     need = step_workspace_bytes(g, hp)
     ws = workspace if workspace is not None else _workspace(w_master[0].device, need)
     _lib.check(lib().muon_step_group(ctypes.byref(g), ctypes.byref(hp), _ptr(ws), ws.numel(),
@@ -253,12 +266,12 @@ def step_groups(groups, *, hp=None, workspace=None, **kw):
 
     ``groups`` is a list of dicts with the arguments of :func:`step_group`:
     ``w_master``, ``grads``, ``moms`` and optionally ``variances``, ``w_model``,
-    ``heads``.  Every parameter comes out bitwise as it would from its own
+    ``heads``, ``split_rows``.  Every parameter comes out bitwise as it would from its own
     ``step_group`` call.
     """
     hp = hp if hp is not None else hparams(**kw)
     made = [_make_group(d["w_master"], d["grads"], d["moms"], d.get("variances"), d.get("w_model"),
-                        d.get("heads", 1)) for d in groups]
+                        d.get("heads", 1), d.get("split_rows")) for d in groups]
     if not made:
         return None
     arr = (Group * len(made))(*[g for g, _ in made])
@@ -274,7 +287,9 @@ def step_groups(groups, *, hp=None, workspace=None, **kw):
 class MuonNS5:
     """Muon / NorMuon over a list of matrix-shaped parameters.
 
-    Parameters are grouped by (flattened shape, dtype); each group's fp32
+    ``heads`` and ``split_rows`` map ``id(param)`` to a head count or to a list
+    of row-block heights (a fused q/k/v weight); parameters are grouped by
+    (flattened shape, dtype, heads, split); each group's fp32
     master weights, momentum and NorMuon variance are held here, and one
     ``step_groups`` call runs the step of every group on the current stream.
     After the step the bf16 model parameters hold RNE(master).
@@ -282,17 +297,19 @@ class MuonNS5:
 
     def __init__(self, params, lr=0.05, momentum=0.95, nesterov=True, weight_decay=0.0, extra_scale=1.0,
                  normuon=False, beta2=0.95, norm_eps=1e-8, ns_steps=5, coeffs=QUINTIC, ns_eps=1e-7,
-                 compute_dtype="bf16", mom_dtype=None, max_batch=0, heads=None):
+                 compute_dtype="bf16", mom_dtype=None, max_batch=0, heads=None, split_rows=None):
         torch = _torch()
         self.params = [p for p in params]
         heads = heads or {}
+        split_rows = split_rows or {}
         self.hp = hparams(lr, momentum, nesterov, weight_decay, extra_scale, normuon, beta2, norm_eps,
                           ns=ns_config(ns_steps, coeffs, ns_eps, compute_dtype, max_batch))
         self.groups = OrderedDict()
         for p in self.params:
             if p.dim() < 2:
                 raise MuonError(_lib.MUON_ERR_INVALID_ARG, "MuonNS5 takes matrix-shaped (2-D+) parameters")
-            key = (tuple(p.shape), p.dtype, int(heads.get(id(p), 1)))
+            sp = split_rows.get(id(p))
+            key = (tuple(p.shape), p.dtype, int(heads.get(id(p), 1)), tuple(int(h) for h in sp) if sp else None)
             self.groups.setdefault(key, []).append(p)
         self.state = {}
         for key, ps in self.groups.items():
@@ -313,7 +330,7 @@ class MuonNS5:
     def step(self):
         torch = _torch()
         todo = []
-        for (shape, dt, h), ps in self.groups.items():
+        for (shape, dt, h, sp), ps in self.groups.items():
             live = [p for p in ps if p.grad is not None]
             if not live:
                 continue
@@ -325,6 +342,7 @@ class MuonNS5:
                 "variances": [s["var"] for s in st] if self.hp.normuon else None,
                 "w_model": [p.data for p in live] if dt == torch.bfloat16 else None,
                 "heads": h,
+                "split_rows": list(sp) if sp else None,
             })
         step_groups(todo, hp=self.hp)
 

@@ -40,7 +40,8 @@ class Group(ctypes.Structure):
     _fields_ = [("n", c_i64), ("rows", c_i64), ("cols", c_i64), ("heads", c_i64),
                 ("grad_dtype", c_i32), ("mom_dtype", c_i32), ("model_dtype", c_i32), ("reserved", c_i32),
                 ("w_master", ctypes.POINTER(c_vp)), ("w_model", ctypes.POINTER(c_vp)),
-                ("grad", ctypes.POINTER(c_vp)), ("mom", ctypes.POINTER(c_vp)), ("var", ctypes.POINTER(c_vp))]
+                ("grad", ctypes.POINTER(c_vp)), ("mom", ctypes.POINTER(c_vp)), ("var", ctypes.POINTER(c_vp)),
+                ("nsplit", c_i64), ("split_rows", ctypes.POINTER(c_i64))]
 
 
 class HParams(ctypes.Structure):

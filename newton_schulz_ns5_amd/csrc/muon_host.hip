@@ -73,14 +73,13 @@ Geom make_geom(int64_t rows, int64_t cols, int32_t compute) {
   return g;
 }
 
-// Workspace of `nb` NS problems (+ per-parameter NorMuon scratch for `np_`
-// parameters of `prow` rows when requested).
+// Workspace of `nb` NS problems.
 struct Layout {
-  size_t X0, X1, A, B, partial, rs, d, ms, q, rho, total;
+  size_t X0, X1, A, B, partial, rs, total;
   int tiles;
 };
 
-Layout make_layout(const Geom& g, int64_t nb, int64_t nparams, int64_t prow, bool normuon) {
+Layout make_layout(const Geom& g, int64_t nb) {
   Layout L{};
   const size_t es = g.bf ? 2 : 4;
   size_t off = 0;
@@ -92,12 +91,6 @@ Layout make_layout(const Geom& g, int64_t nb, int64_t nparams, int64_t prow, boo
   L.B = take((size_t)nb * g.mp * g.mp * es);
   L.partial = take((size_t)nb * L.tiles * 4);
   L.rs = take((size_t)nb * 4);
-  if (normuon) {
-    L.d = take((size_t)nparams * prow * 4);
-    L.ms = take((size_t)nparams * prow * 4);
-    L.q = take((size_t)nparams * prow * 4);
-    L.rho = take((size_t)nparams * 4);
-  }
   L.total = off;
   return L;
 }
@@ -492,7 +485,7 @@ int muon_ns_workspace_bytes(int64_t n, int64_t rows, int64_t cols, const muon_ns
   if (!bytes) return fail(MUON_ERR_INVALID_ARG, "bytes is NULL");
   if (n == 0 || rows == 0 || cols == 0) { *bytes = 0; return ok(); }
   const Geom g = make_geom(rows, cols, cfg->compute_dtype);
-  *bytes = make_layout(g, chunk_of(n, cfg->max_batch), 0, 0, false).total;
+  *bytes = make_layout(g, chunk_of(n, cfg->max_batch)).total;
   return ok();
 }
 
@@ -518,7 +511,7 @@ int muon_ns_batched(const void* x, int32_t x_dtype, int64_t x_batch_stride, int6
   }
   const Geom g = make_geom(rows, cols, cfg->compute_dtype);
   const int64_t chunk = chunk_of(n, cfg->max_batch);
-  const Layout L = make_layout(g, chunk, 0, 0, false);
+  const Layout L = make_layout(g, chunk);
   if (!workspace) return fail(MUON_ERR_INVALID_ARG, "workspace is NULL");
   if ((uintptr_t)workspace & 255) return fail(MUON_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   if (workspace_bytes < L.total) return fail(MUON_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", L.total, workspace_bytes);
@@ -607,13 +600,31 @@ int normuon_normalize(void* o, int32_t o_dtype, int64_t o_batch_stride, int64_t 
   return ok();
 }
 
+// Sizes, heads and row splits of one group.
+static int check_group_shape(const muon_group* g) {
+  int rc = check_dims(g->n, g->rows, g->cols);
+  if (rc) return rc;
+  if (g->heads < 1) return fail(MUON_ERR_INVALID_ARG, "heads must be >= 1");
+  if (g->rows % g->heads) return fail(MUON_ERR_INVALID_ARG, "rows (%lld) not divisible by heads (%lld)", (long long)g->rows, (long long)g->heads);
+  if (g->nsplit < 0 || g->nsplit > 4096) return fail(MUON_ERR_INVALID_ARG, "nsplit must be in 0..4096");
+  if (g->nsplit > 0) {
+    if (!g->split_rows) return fail(MUON_ERR_INVALID_ARG, "split_rows is NULL");
+    if (g->heads != 1) return fail(MUON_ERR_INVALID_ARG, "row splits need heads == 1");
+    int64_t sum = 0;
+    for (int64_t k = 0; k < g->nsplit; ++k) {
+      if (g->split_rows[k] <= 0) return fail(MUON_ERR_INVALID_ARG, "split_rows[%lld] must be > 0", (long long)k);
+      sum += g->split_rows[k];
+    }
+    if (sum != g->rows) return fail(MUON_ERR_INVALID_ARG, "split_rows sum to %lld, rows is %lld", (long long)sum, (long long)g->rows);
+  }
+  return MUON_OK;
+}
+
 static int check_group(const muon_group* g, const muon_hparams* hp) {
   if (!g || !hp) return fail(MUON_ERR_INVALID_ARG, "group or hparams is NULL");
   int rc = check_cfg(&hp->ns);
   if (rc) return rc;
-  if ((rc = check_dims(g->n, g->rows, g->cols))) return rc;
-  if (g->heads < 1) return fail(MUON_ERR_INVALID_ARG, "heads must be >= 1");
-  if (g->rows % g->heads) return fail(MUON_ERR_INVALID_ARG, "rows (%lld) not divisible by heads (%lld)", (long long)g->rows, (long long)g->heads);
+  if ((rc = check_group_shape(g))) return rc;
   if (!dtype_ok(g->grad_dtype) || !dtype_ok(g->mom_dtype)) return fail(MUON_ERR_UNSUPPORTED, "grad/mom dtype must be MUON_F32 or MUON_BF16");
   if (g->model_dtype != -1 && g->model_dtype != MUON_BF16) return fail(MUON_ERR_UNSUPPORTED, "model_dtype must be MUON_BF16 or -1");
   if (g->reserved != 0) return fail(MUON_ERR_INVALID_ARG, "reserved field must be 0");
@@ -641,14 +652,25 @@ static int check_group(const muon_group* g, const muon_hparams* hp) {
 
 namespace {
 
+// One row block of a group: rows [r0, r0 + h) of every parameter, split into
+// H heads of hb rows for Newton-Schulz.
+struct Block {
+  int64_t r0, h, H, hb;
+  Geom ge;
+  Layout L;
+  size_t off;              // of the block's region within the group's region
+};
+
 // Where each group of a step call lives in the workspace and how it is cut
 // into passes of at most pc parameters.
 struct GroupPlan {
   const muon_group* g;
   bool live;               // non-empty group
-  int64_t H, hb, pc, pelems;
-  Geom ge;
-  Layout L;
+  bool split;              // row blocks: O is assembled in its own buffer
+  int64_t pc, pelems;
+  std::vector<Block> blocks;
+  size_t obuf_off;         // split groups: O [pc][rows][cols]
+  size_t nm_d, nm_ms, nm_q, nm_rho;  // NorMuon scratch: [pc][rows] x 3, [pc]
   size_t offset;           // of the group's region in the workspace
 };
 
@@ -665,15 +687,37 @@ int plan_groups(const muon_group* groups, int64_t ng, const muon_hparams* hp, st
     P.g = g;
     P.live = !(g->n == 0 || g->rows == 0 || g->cols == 0);
     if (P.live) {
-      P.H = g->heads;
-      P.hb = g->rows / P.H;
-      P.ge = make_geom(P.hb, g->cols, hp->ns.compute_dtype);
+      P.split = g->nsplit > 0;
       P.pc = chunk_of(g->n, hp->ns.max_batch);
       P.pelems = g->rows * g->cols;
-      P.L = make_layout(P.ge, P.pc * P.H, P.pc, g->rows, hp->normuon != 0);
+      size_t goff = 0;
+      auto take = [&](size_t bytes) { size_t at = goff; goff = align256(goff + bytes); return at; };
+      int64_t r0 = 0;
+      const int64_t nb = P.split ? g->nsplit : 1;
+      for (int64_t k = 0; k < nb; ++k) {
+        Block B{};
+        B.r0 = r0;
+        B.h = P.split ? g->split_rows[k] : g->rows;
+        B.H = P.split ? 1 : g->heads;
+        B.hb = B.h / B.H;
+        B.ge = make_geom(B.hb, g->cols, hp->ns.compute_dtype);
+        B.L = make_layout(B.ge, P.pc * B.H);
+        B.off = take(B.L.total);
+        if (P.pc * B.H > 65535)
+          return fail(MUON_ERR_INVALID_ARG, "group %lld: parameters x heads per pass above 65535; set ns.max_batch", (long long)i);
+        P.blocks.push_back(B);
+        r0 += B.h;
+      }
+      const size_t oes = hp->ns.compute_dtype == MUON_BF16 ? 2 : 4;
+      if (P.split) P.obuf_off = take((size_t)P.pc * P.pelems * oes);
+      if (hp->normuon) {
+        P.nm_d = take((size_t)P.pc * g->rows * 4);
+        P.nm_ms = take((size_t)P.pc * g->rows * 4);
+        P.nm_q = take((size_t)P.pc * g->rows * 4);
+        P.nm_rho = take((size_t)P.pc * 4);
+      }
       P.offset = off;
-      off = align256(off + P.L.total);
-      if (P.pc * P.H > 65535) return fail(MUON_ERR_INVALID_ARG, "group %lld: parameters x heads per pass above 65535; set ns.max_batch", (long long)i);
+      off = align256(off + goff);
     }
     plans.push_back(P);
   }
@@ -693,56 +737,68 @@ int check_groups(const muon_group* groups, int64_t ng, const muon_hparams* hp) {
 }
 
 // Momentum (+ orientation and norm partials) and the norm finalize of one pass
-// of one group; returns the Newton-Schulz job of the pass.
+// of one group: one Newton-Schulz job per row block, appended to `jobs`;
+// *obuf receives where the pass's O [np_][rows][cols] is assembled.
 int stage_group(const GroupPlan& P, const muon_hparams* hp, char* ws, int64_t c0, int64_t np_, hipStream_t s,
-                NsJob* job) {
+                std::vector<NsJob>& jobs, void** obuf) {
   const muon_group* g = P.g;
-  const Geom& ge = P.ge;
-  const Layout& L = P.L;
-  const double oes = ge.bf ? 2 : 4;
   const double ges = (double)esize(g->grad_dtype), mes = (double)esize(g->mom_dtype);
   hipError_t e;
-  for (int64_t s0 = 0; s0 < np_; s0 += kMaxParams) {
-    const int64_t k = (np_ - s0) < kMaxParams ? (np_ - s0) : kMaxParams;
-    PrepParams pp{};
-    pp.mode = 1;
-    pp.tall = ge.tall;
-    pp.rows = (int)P.hb; pp.cols = (int)g->cols;
-    pp.mp = (int)ge.mp; pp.np = (int)ge.np;
-    pp.heads = (int)P.H;
-    pp.src_dtype = g->grad_dtype; pp.mom_dtype = g->mom_dtype;
-    pp.x_bf16 = ge.bf;
-    pp.mu = hp->momentum; pp.nesterov = hp->nesterov ? 1 : 0;
-    pp.param_cols = g->cols;
-    for (int64_t i = 0; i < k; ++i) {
-      pp.grad[i] = g->grad[c0 + s0 + i];
-      pp.mom[i] = g->mom[c0 + s0 + i];
+  for (const Block& B : P.blocks) {
+    const Geom& ge = B.ge;
+    const Layout& L = B.L;
+    char* const bws = ws + B.off;
+    const double oes = ge.bf ? 2 : 4;
+    for (int64_t s0 = 0; s0 < np_; s0 += kMaxParams) {
+      const int64_t k = (np_ - s0) < kMaxParams ? (np_ - s0) : kMaxParams;
+      PrepParams pp{};
+      pp.mode = 1;
+      pp.tall = ge.tall;
+      pp.rows = (int)B.hb; pp.cols = (int)g->cols;
+      pp.mp = (int)ge.mp; pp.np = (int)ge.np;
+      pp.heads = (int)B.H;
+      pp.src_dtype = g->grad_dtype; pp.mom_dtype = g->mom_dtype;
+      pp.x_bf16 = ge.bf;
+      pp.mu = hp->momentum; pp.nesterov = hp->nesterov ? 1 : 0;
+      pp.param_cols = g->cols;
+      for (int64_t i = 0; i < k; ++i) {
+        pp.grad[i] = (const char*)g->grad[c0 + s0 + i] + (size_t)(B.r0 * g->cols) * (size_t)ges;
+        pp.mom[i] = (char*)g->mom[c0 + s0 + i] + (size_t)(B.r0 * g->cols) * (size_t)mes;
+      }
+      pp.X = bws + L.X0 + (size_t)(s0 * B.H) * ge.mp * ge.np * (size_t)oes;
+      pp.XT = nullptr;
+      pp.X_bs = ge.mp * ge.np;
+      pp.partial = (float*)(bws + L.partial) + s0 * B.H * L.tiles;
+      e = run(MUON_K_PREP, 0, (double)k * B.h * g->cols * (ges + 2 * mes + oes), s,
+              [&]() { return launch_prep(pp, (int)(k * B.H), s); });
+      if (e != hipSuccess) return hip_fail(e, "momentum kernel");
     }
-    pp.X = ws + L.X0 + (size_t)(s0 * P.H) * ge.mp * ge.np * (size_t)oes;
-    pp.XT = nullptr;
-    pp.X_bs = ge.mp * ge.np;
-    pp.partial = (float*)(ws + L.partial) + s0 * P.H * L.tiles;
-    e = run(MUON_K_PREP, 0, (double)k * P.pelems * (ges + 2 * mes + oes), s,
-            [&]() { return launch_prep(pp, (int)(k * P.H), s); });
-    if (e != hipSuccess) return hip_fail(e, "momentum kernel");
+    if ((e = norm_finalize(ge, np_ * B.H, hp->ns.eps, bws, L, s)) != hipSuccess) return hip_fail(e, "norm kernel");
+    // The last update writes O in parameter orientation ([n][rows][cols],
+    // contiguous): a whole group into the X buffer its last iteration does not
+    // read, row blocks into the group's O buffer at their row offset.
+    const int32_t odt = ge.bf ? MUON_BF16 : MUON_F32;
+    FinalOut out;
+    if (P.split) {
+      out = FinalOut{ws + P.obuf_off + (size_t)(B.r0 * g->cols) * (size_t)oes, odt, g->cols, P.pelems};
+      *obuf = ws + P.obuf_off;
+    } else {
+      void* o = bws + ((hp->ns.steps % 2) ? L.X1 : L.X0);
+      out = FinalOut{o, odt, g->cols, B.hb * g->cols};
+      *obuf = o;
+    }
+    jobs.push_back(NsJob{ge, np_ * B.H, bws, L, out});
   }
-  if ((e = norm_finalize(ge, np_ * P.H, hp->ns.eps, ws, L, s)) != hipSuccess) return hip_fail(e, "norm kernel");
-  // The last update writes O in parameter orientation ([n][rows][cols],
-  // contiguous) into the X buffer the last iteration does not read.
-  void* obuf = ws + ((hp->ns.steps % 2) ? L.X1 : L.X0);
-  *job = NsJob{ge, np_ * P.H, ws, L, FinalOut{obuf, ge.bf ? MUON_BF16 : MUON_F32, g->cols, P.hb * g->cols}};
   return MUON_OK;
 }
 
 // NorMuon (when on) and the weight update of one pass of one group.
-int finish_group(const GroupPlan& P, const muon_hparams* hp, char* ws, int64_t c0, int64_t np_, const NsJob& job,
+int finish_group(const GroupPlan& P, const muon_hparams* hp, char* ws, int64_t c0, int64_t np_, void* obuf,
                  hipStream_t s) {
   const muon_group* g = P.g;
-  const Layout& L = P.L;
   const bool nm = hp->normuon != 0;
-  const int32_t odt = job.out.dtype;
+  const int32_t odt = hp->ns.compute_dtype == MUON_BF16 ? MUON_BF16 : MUON_F32;
   const double oes = odt == MUON_BF16 ? 2 : 4;
-  void* obuf = job.out.C;
   const int64_t fan_out = hp->fan_out ? hp->fan_out : g->rows;
   const int64_t fan_in = hp->fan_in ? hp->fan_in : g->cols;
   const double ratio = (double)fan_out / (double)fan_in;
@@ -757,14 +813,14 @@ int finish_group(const GroupPlan& P, const muon_hparams* hp, char* ws, int64_t c
       r2.o_dtype = odt; r2.o_bs = P.pelems; r2.o_rs = g->cols;
       r2.rows = (int)g->rows; r2.cols = (int)g->cols;
       r2.beta2 = hp->beta2; r2.eps = hp->norm_eps;
-      r2.d = (float*)(ws + L.d) + s0 * g->rows;
-      r2.ms = (float*)(ws + L.ms) + s0 * g->rows;
-      r2.q = (float*)(ws + L.q) + s0 * g->rows;
+      r2.d = (float*)(ws + P.nm_d) + s0 * g->rows;
+      r2.ms = (float*)(ws + P.nm_ms) + s0 * g->rows;
+      r2.q = (float*)(ws + P.nm_q) + s0 * g->rows;
       for (int64_t i = 0; i < k; ++i) r2.v_tab[i] = g->var[c0 + s0 + i];
       e = run(MUON_K_ROWSTAT, 0, (double)k * (P.pelems * oes + g->rows * 8), s, [&]() { return launch_rowstat(r2, (int)k, s); });
       if (e != hipSuccess) return hip_fail(e, "row statistics kernel");
     }
-    RhoParams hpm{(float*)(ws + L.ms), (float*)(ws + L.q), (int)g->rows, (float*)(ws + L.rho)};
+    RhoParams hpm{(float*)(ws + P.nm_ms), (float*)(ws + P.nm_q), (int)g->rows, (float*)(ws + P.nm_rho)};
     e = run(MUON_K_RHO, 0, (double)np_ * g->rows * 8, s, [&]() { return launch_rho(hpm, (int)np_, s); });
     if (e != hipSuccess) return hip_fail(e, "rho kernel");
   }
@@ -775,8 +831,8 @@ int finish_group(const GroupPlan& P, const muon_hparams* hp, char* ws, int64_t c
     ap.O = (char*)obuf + (size_t)s0 * P.pelems * (size_t)oes;
     ap.o_dtype = odt; ap.o_bs = P.pelems; ap.o_rs = g->cols;
     ap.rows = (int)g->rows; ap.cols = (int)g->cols;
-    ap.d = nm ? (float*)(ws + L.d) + s0 * g->rows : nullptr;
-    ap.rho = nm ? (float*)(ws + L.rho) + s0 : nullptr;
+    ap.d = nm ? (float*)(ws + P.nm_d) + s0 * g->rows : nullptr;
+    ap.rho = nm ? (float*)(ws + P.nm_rho) + s0 : nullptr;
     ap.lr_eff = lr_eff; ap.decay = decay;
     ap.vec = (g->cols % 8) == 0 ? 1 : 0;
     for (int64_t i = 0; i < k; ++i) {
@@ -803,9 +859,7 @@ int muon_step_groups_workspace_bytes(const muon_group* groups, int64_t ngroups, 
   if (ngroups < 0 || ngroups > 4096) return fail(MUON_ERR_INVALID_ARG, "ngroups must be in 0..4096");
   if (ngroups > 0 && !groups) return fail(MUON_ERR_INVALID_ARG, "groups is NULL");
   for (int64_t i = 0; i < ngroups; ++i) {
-    const muon_group* g = &groups[i];
-    if ((rc = check_dims(g->n, g->rows, g->cols))) return rc;
-    if (g->heads < 1 || (g->rows % g->heads)) return fail(MUON_ERR_INVALID_ARG, "group %lld: rows must divide into heads >= 1", (long long)i);
+    if ((rc = check_group_shape(&groups[i]))) return rc;
   }
   std::vector<GroupPlan> plans;
   size_t total = 0;
@@ -839,21 +893,20 @@ int muon_step_groups(const muon_group* groups, int64_t ngroups, const muon_hpara
   // groups at once (a matrix's result does not depend on who shares a launch).
   for (int64_t c = 0; c < passes; ++c) {
     std::vector<NsJob> jobs;
-    std::vector<const GroupPlan*> who;
+    std::vector<std::pair<const GroupPlan*, void*>> who;
     for (const GroupPlan& P : plans) {
       if (!P.live || c * P.pc >= P.g->n) continue;
       const int64_t c0 = c * P.pc, np_ = std::min<int64_t>(P.pc, P.g->n - c0);
-      NsJob job;
-      if ((rc = stage_group(P, hp, (char*)workspace + P.offset, c0, np_, s, &job))) return rc;
-      jobs.push_back(job);
-      who.push_back(&P);
+      void* obuf = nullptr;
+      if ((rc = stage_group(P, hp, (char*)workspace + P.offset, c0, np_, s, jobs, &obuf))) return rc;
+      who.emplace_back(&P, obuf);
     }
     hipError_t e = ns_iterations(jobs, hp->ns, s);
     if (e != hipSuccess) return hip_fail(e, "Newton-Schulz kernels");
-    for (size_t k = 0; k < jobs.size(); ++k) {
-      const GroupPlan& P = *who[k];
+    for (const auto& [pp, obuf] : who) {
+      const GroupPlan& P = *pp;
       const int64_t c0 = c * P.pc, np_ = std::min<int64_t>(P.pc, P.g->n - c0);
-      if ((rc = finish_group(P, hp, (char*)workspace + P.offset, c0, np_, jobs[k], s))) return rc;
+      if ((rc = finish_group(P, hp, (char*)workspace + P.offset, c0, np_, obuf, s))) return rc;
     }
   }
   return ok();

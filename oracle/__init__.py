@@ -21,11 +21,12 @@ Sources (pages are cited by title and section):
 * "Fix convolution flattening in megabatches and NorMuon normalization" (dion
   pull request): "Problem and fix" (megabatch [N, out, prod(rest)], fan_out=out,
   fan_in=prod(rest)), "Adjacent bug" and "What it does" (one NorMuon variance
-  per output channel on the flattened matrix, norm-preserving rescale).
+  per output channel on the flattened matrix, norm-preserving rescale);
+  "Design" (review): split_sizes row blocks cut on dim -2 before Newton-Schulz.
 
 Parity status per function (see also the test suite):
 
-* newton_schulz5, ns5_megabatch, ns5_per_head, flatten_param: pinned (SVD
+* newton_schulz5, ns5_megabatch, ns5_per_head, ns5_row_split, flatten_param: pinned (SVD
   closed form, scalar fixed points, invariances, the shard-vs-whole figures
   printed on the AutoTP page).
 * nesterov_momentum: pinned by the two-step closed form.
@@ -37,7 +38,7 @@ Parity status per function (see also the test suite):
 """
 from .bf16 import round_bf16, round_f32  # noqa: F401
 from .ns5 import (  # noqa: F401
-    QUINTIC, newton_schulz5, ns5_megabatch, ns5_per_head, frobenius_normalize,
+    QUINTIC, newton_schulz5, ns5_megabatch, ns5_per_head, ns5_row_split, frobenius_normalize,
 )
 from .muon import (  # noqa: F401
     flatten_param, nesterov_momentum, normuon, spectral_lr, muon_step, MuonHParams,

@@ -12,7 +12,7 @@ from dataclasses import dataclass
 import numpy as np
 
 from .bf16 import round_bf16, round_f32
-from .ns5 import QUINTIC, newton_schulz5, ns5_per_head
+from .ns5 import QUINTIC, newton_schulz5, ns5_per_head, ns5_row_split
 
 
 def flatten_param(p):
@@ -87,6 +87,7 @@ class MuonHParams:
     coeffs: tuple = QUINTIC
     ns_eps: float = 1e-7
     heads: int = 1
+    split_rows: tuple = None    # row-block heights of a fused weight (heads must be 1)
     normuon: bool = False
     beta2: float = 0.95
     norm_eps: float = 1e-8
@@ -101,7 +102,12 @@ def muon_step(w, g, m, v=None, hp=MuonHParams()):
     """One optimizer step of one parameter, all arithmetic in float64.
 
     w: fp32 master weight values [out, *rest]; g: gradient; m: momentum;
-    v: NorMuon variance [out] (required when hp.normuon).  Inputs are the
+    v: NorMuon variance [out] (required when hp.normuon).  With
+    hp.split_rows only Newton-Schulz runs per row block; momentum, NorMuon
+    (its norm-preserving rescale included) and the spectral scale act on the
+    whole parameter, whose shape is the one the lr adjustment uses ("Fix
+    convolution flattening...", "Problem and fix").  This whole-parameter
+    scope is a reading: the pages do not say.  Inputs are the
     exact stored values widened to float64.
 
     Returns a dict with the stored results (w rounded to fp32, m rounded to
@@ -118,6 +124,10 @@ def muon_step(w, g, m, v=None, hp=MuonHParams()):
     kw = dict(steps=hp.ns_steps, coeffs=hp.coeffs, eps=hp.ns_eps)
     if out == 0 or fan_in == 0:
         o = np.zeros_like(u)
+    elif hp.split_rows:
+        if hp.heads != 1:
+            raise ValueError("row splits take heads == 1")
+        o = ns5_row_split(u, hp.split_rows, **kw)
     elif hp.heads > 1:
         o = ns5_per_head(u, hp.heads, **kw)
     else:

@@ -87,3 +87,27 @@ def ns5_per_head(p, heads, **kw):
         res[h * hb:(h + 1) * hb] = newton_schulz5(
             np.array(p[h * hb:(h + 1) * hb], copy=True, order="C"), **kw)
     return res
+
+
+def ns5_row_split(p, split_rows, **kw):
+    """Row-split Newton-Schulz: block k = rows [r_k, r_k + h_k) with the
+    heights h_k in order, each block orthogonalized on its own.
+
+    "Fix convolution flattening in megabatches and NorMuon normalization",
+    "Design" (review): a split_sizes list cuts a parameter into row blocks on
+    dim -2 before Newton-Schulz; "core.optimizer.layer_sharded_muon",
+    LayerShardedMuon (split_qkv, qkv_split_shapes) applies it to fused q/k/v
+    weights.  Reading taken: the heights are listed top to bottom and must
+    cover the rows exactly.
+    """
+    p = np.asarray(p, dtype=np.float64)
+    hs = [int(h) for h in split_rows]
+    if any(h <= 0 for h in hs) or sum(hs) != p.shape[0]:
+        raise ValueError("split_rows must be positive and sum to the row count")
+    res = np.empty_like(p)
+    r0 = 0
+    for h in hs:
+        res[r0:r0 + h] = newton_schulz5(np.array(p[r0:r0 + h], copy=True, order="C"), **kw)
+        r0 += h
+    return res
+

@@ -53,6 +53,7 @@ int main(void) {
   F(muon_group, n); F(muon_group, rows); F(muon_group, cols); F(muon_group, heads); F(muon_group, grad_dtype);
   F(muon_group, mom_dtype); F(muon_group, model_dtype); F(muon_group, reserved); F(muon_group, w_master);
   F(muon_group, w_model); F(muon_group, grad); F(muon_group, mom); F(muon_group, var);
+  F(muon_group, nsplit); F(muon_group, split_rows);
   F(muon_hparams, lr); F(muon_hparams, momentum); F(muon_hparams, nesterov); F(muon_hparams, weight_decay);
   F(muon_hparams, extra_scale); F(muon_hparams, normuon); F(muon_hparams, beta2); F(muon_hparams, norm_eps);
   F(muon_hparams, fan_out); F(muon_hparams, fan_in); F(muon_hparams, ns);
@@ -87,7 +88,7 @@ def test_one_hip_runtime_per_process():
 
 def test_versions_and_status_strings():
     L = m.lib()
-    assert L.muon_abi_version() == 2 and L.muon_state_layout_version() == 1
+    assert L.muon_abi_version() == 3 and L.muon_state_layout_version() == 1
     for code, word in [(0, b"ok"), (-1, b"invalid"), (-2, b"unsupported"), (-3, b"workspace"), (-4, b"HIP")]:
         assert word in L.muon_status_string(code)
     assert L.muon_kernel_class_name(4) == b"update"
@@ -192,6 +193,11 @@ def group_call(hp=None, **over):
     g.n, g.rows, g.cols, g.heads = n, over.pop("rows", 64), over.pop("cols", 96), over.pop("heads", 1)
     g.grad_dtype, g.mom_dtype, g.model_dtype = over.pop("gd", 1), over.pop("md", 1), over.pop("mdl", -1)
     g.reserved = over.pop("reserved", 0)
+    split = over.pop("split", None)
+    if split is not None:
+        keep_split = (ctypes.c_int64 * max(len(split), 1))(*split)
+        g.nsplit = over.pop("nsplit", len(split))
+        g.split_rows = None if over.pop("split_null", False) else ctypes.cast(keep_split, ctypes.POINTER(ctypes.c_int64))
     P = ctypes.POINTER(ctypes.c_void_p)
     g.w_master = ctypes.cast(arrs["w"], P) if arrs["w"] is not None else None
     g.grad = ctypes.cast(arrs["g"], P) if arrs["g"] is not None else None
@@ -212,6 +218,10 @@ def group_call(hp=None, **over):
     (dict(arrays={"w": (ctypes.c_void_p * 2)(FAKE, 0)}), -1),
     (dict(arrays={"g": (ctypes.c_void_p * 2)(FAKE, FAKE + 8)}), -1),
     (dict(wsb=1000), -3), (dict(ws=0), -1), (dict(rows=-1), -1),
+    # row splits: heights must be positive and sum to rows; heads must be 1
+    (dict(split=[32, 16]), -1), (dict(split=[64, 0]), -1), (dict(split=[80, -16]), -1),
+    (dict(split=[32, 32], heads=2), -1), (dict(split=[32, 32], split_null=True), -1),
+    (dict(split=[32, 32], nsplit=-1), -1), (dict(split=[32, 32], wsb=1000), -3),
 ])
 def test_step_group_argument_errors(kw, code):
     assert group_call(**kw) == code
@@ -245,6 +255,42 @@ def test_step_workspace_scales_with_heads_and_batch():
     assert per_head < whole     # 32 Gram matrices of 128^2 instead of one 4096^2
     hp2 = m.hparams(ns=m.ns_config(max_batch=1))
     assert m.step_workspace_bytes(g, hp2) < whole
+
+
+def _split_group(n, rows, cols, hs, keep):
+    arr = (ctypes.c_void_p * n)(*([FAKE] * n))
+    g = m.Group()
+    g.n, g.rows, g.cols, g.heads = n, rows, cols, 1
+    g.grad_dtype, g.mom_dtype, g.model_dtype = 1, 1, -1
+    P = ctypes.POINTER(ctypes.c_void_p)
+    g.w_master = g.grad = g.mom = ctypes.cast(arr, P)
+    keep.append(arr)
+    if hs:
+        h = (ctypes.c_int64 * len(hs))(*hs)
+        keep.append(h)
+        g.nsplit, g.split_rows = len(hs), ctypes.cast(h, ctypes.POINTER(ctypes.c_int64))
+    return g
+
+
+@pytest.mark.parametrize("compute", ["bf16", "f32"])
+def test_split_workspace_is_blocks_plus_output(compute):
+    # A fused [q; k; v] weight (4096 + 1024 + 1024 rows): one region per row
+    # block, sized as the block alone, plus the assembled output [n][rows][cols].
+    hp = m.hparams(ns=m.ns_config(compute_dtype=compute))
+    keep = []
+    n, cols, hs = 3, 4096, [4096, 1024, 1024]
+    fused = m.step_workspace_bytes(_split_group(n, sum(hs), cols, hs, keep), hp)
+    blocks = sum((m.step_workspace_bytes(_split_group(n, h, cols, None, keep), hp) + 255) // 256 * 256 for h in hs)
+    es = 2 if compute == "bf16" else 4
+    assert fused == blocks + (n * sum(hs) * cols * es + 255) // 256 * 256
+
+
+def test_split_of_one_block_matches_the_plain_group_plus_output():
+    hp = m.hparams()
+    keep = []
+    plain = m.step_workspace_bytes(_split_group(2, 300, 130, None, keep), hp)
+    one = m.step_workspace_bytes(_split_group(2, 300, 130, [300], keep), hp)
+    assert one == (plain + 255) // 256 * 256 + (2 * 300 * 130 * 2 + 255) // 256 * 256
 
 
 def test_normuon_argument_errors():

@@ -40,7 +40,7 @@ def grads_for(cfg, n, shape, gdt, step, power=False):
 
 
 def run_steps(shape, n, gdt, mdt, compute, steps=2, normuon=False, heads=1, model_copy=False, power=False,
-              cfg_id=7, lr=0.05, wd=0.0, check=None):
+              cfg_id=7, lr=0.05, wd=0.0, check=None, split_rows=None):
     torch = torch_cuda()
     w0 = make_state(cfg_id, n, shape, gdt, mdt)
     tdt = {"bf16": torch.bfloat16, "f32": torch.float32}
@@ -52,15 +52,16 @@ def run_steps(shape, n, gdt, mdt, compute, steps=2, normuon=False, heads=1, mode
     ow = [w.astype(np.float64) for w in w0]
     om = [np.zeros(shape) for _ in range(n)]
     ov = [np.zeros(shape[0]) for _ in range(n)]
-    hp = oracle.MuonHParams(lr=lr, weight_decay=wd, heads=heads, normuon=normuon, mom_dtype=mdt)
+    hp = oracle.MuonHParams(lr=lr, weight_decay=wd, heads=heads, normuon=normuon, mom_dtype=mdt,
+                            split_rows=tuple(split_rows) if split_rows else None)
     tol = TOL[compute]
     check = list(range(n)) if check is None else check
     for step in range(1, steps + 1):
         g = grads_for(cfg_id, n, shape, gdt, step, power)
         G = [to_dev(x, gdt) for x in g]
         before = [to_f64(w) for w in W]
-        ns.step_group(W, G, M, V, WM, heads=heads, lr=lr, weight_decay=wd, normuon=normuon,
-                      ns=ns.ns_config(compute_dtype=compute))
+        ns.step_group(W, G, M, V, WM, heads=heads, split_rows=split_rows, lr=lr, weight_decay=wd,
+                      normuon=normuon, ns=ns.ns_config(compute_dtype=compute))
         torch.cuda.synchronize()
         for i in check:
             r = oracle.muon_step(ow[i], storage_f64(g[i], gdt), om[i], ov[i], hp)
@@ -120,6 +121,53 @@ def test_conv_p1_shapes_tail():
 
 def test_per_head_step():
     run_steps((256, 384), 2, "bf16", "bf16", "bf16", steps=2, heads=4)
+
+
+@pytest.mark.parametrize("normuon", [False, True])
+def test_split_qkv_step(normuon):
+    # A fused [q; k; v] weight of 384 x 256 split into 256 + 64 + 64 rows (the
+    # 4:1:1 grouped-query ratio of the Llama-3-8B attention), two steps; the
+    # scale sqrt(384 / 256) comes from the whole parameter.
+    run_steps((384, 256), 2, "bf16", "bf16", "bf16", steps=2, normuon=normuon, power=True, model_copy=True,
+              split_rows=[256, 64, 64])
+
+
+def test_split_ragged_blocks_f32():
+    # Blocks of 100, 37 and 3 rows (wide, wide, wide; the last a 3 x 96 sliver)
+    # in fp32 compute.
+    run_steps((140, 96), 2, "f32", "f32", "f32", steps=2, normuon=True, split_rows=[100, 37, 3])
+
+
+def test_split_tall_blocks():
+    # Blocks taller than wide take the transposed orientation inside the split.
+    run_steps((448, 128), 1, "bf16", "bf16", "bf16", steps=2, split_rows=[320, 128])
+
+
+def test_split_blocks_step_like_their_own_groups_bitwise():
+    # Without NorMuon a row block of a split parameter steps bitwise like the
+    # same rows stepped as a parameter of their own, given the same lr scale
+    # (fan_out / fan_in pinned to the whole parameter's).
+    torch = torch_cuda()
+    shape, hs, n = (384, 512), [256, 64, 64], 2
+    g = [to_dev(x, "bf16") for x in grads_for(9, n, shape, "bf16", 1, power=True)]
+    w = [to_dev(x, "f32") for x in make_state(9, n, shape, "bf16", "bf16")]
+    m = [torch.zeros(shape, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+    hp = dict(fan_out=shape[0], fan_in=shape[1])
+    parts = []
+    r0 = 0
+    for h in hs:
+        parts.append({"w_master": [x[r0:r0 + h].clone() for x in w], "grads": [x[r0:r0 + h].contiguous() for x in g],
+                      "moms": [x[r0:r0 + h].clone() for x in m]})
+        r0 += h
+    ns.step_groups([{"w_master": w, "grads": g, "moms": m, "split_rows": hs}], **hp)
+    ns.step_groups(parts, **hp)
+    torch.cuda.synchronize()
+    r0 = 0
+    for k, h in enumerate(hs):
+        for i in range(n):
+            assert torch.equal(w[i][r0:r0 + h], parts[k]["w_master"][i]), (k, i)
+            assert torch.equal(m[i][r0:r0 + h], parts[k]["moms"][i]), (k, i)
+        r0 += h
 
 
 def test_weight_decay_and_gate_shape_lr():

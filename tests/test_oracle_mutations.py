@@ -124,3 +124,45 @@ def test_normuon_unmutated_passes():
 @pytest.mark.parametrize("mutation", NORMUON_MUTANTS)
 def test_normuon_mutant_is_caught(mutation):
     assert not normuon_pins_pass(lambda o, v: normuon_variant(o, v, mutation))
+
+
+# ---- row-split geometry -----------------------------------------------------
+def split_variant(p, hs, mutation=None):
+    p = np.asarray(p, dtype=np.float64)
+    if mutation == "reversed_heights":
+        hs = list(hs)[::-1]
+    whole = np.sqrt(np.sum(p * p)) + 1e-7
+    res = np.empty_like(p)
+    r0 = 0
+    for h in hs:
+        blk = p[r0:r0 + h]
+        if mutation == "whole_norm":
+            # every block scaled by the whole matrix's norm instead of its own
+            res[r0:r0 + h] = ns_variant(blk / whole, "no_normalize")
+        else:
+            res[r0:r0 + h] = ns_variant(blk)
+        r0 += h
+    return res
+
+
+def split_pins_pass(fn):
+    rng = np.random.default_rng(1)
+    hs = [5, 3, 9, 1]
+    p = rng.standard_normal((sum(hs), 7))
+    out = fn(p, hs)
+    r0 = 0
+    for h in hs:
+        if rel(out[r0:r0 + h], svd_closed_form(p[r0:r0 + h])) > 1e-12:
+            return False
+        r0 += h
+    return True
+
+
+def test_split_unmutated_passes():
+    assert split_pins_pass(lambda p, hs: split_variant(p, hs))
+    assert split_pins_pass(oracle.ns5_row_split)
+
+
+@pytest.mark.parametrize("mutation", ["reversed_heights", "whole_norm"])
+def test_split_mutant_is_caught(mutation):
+    assert not split_pins_pass(lambda p, hs: split_variant(p, hs, mutation))

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import newton_schulz5, ns5_megabatch, ns5_per_head
+from oracle import newton_schulz5, ns5_megabatch, ns5_per_head, ns5_row_split
 
 A, B, C = oracle.QUINTIC
 
@@ -179,6 +179,48 @@ def test_per_head_with_one_head_is_plain_ns():
 def test_per_head_rejects_uneven_heads():
     with pytest.raises(ValueError):
         ns5_per_head(np.ones((10, 4)), 3)
+
+
+# ---- row-split geometry (fused q/k/v weights) --------------------------------
+# "Fix convolution flattening...", "Design": split_sizes row blocks on dim -2.
+def test_row_split_blocks_follow_their_own_svd_closed_form():
+    # Blocks of unequal height, tall and wide, at very different scales: each
+    # block is normalized by its own norm and orthogonalized alone.
+    rng = np.random.default_rng(40)
+    hs = [5, 3, 9, 1]
+    p = rng.standard_normal((sum(hs), 7)) * np.repeat([1.0, 1e3, 1e-2, 5.0], hs)[:, None]
+    out = ns5_row_split(p, hs)
+    r0 = 0
+    for h in hs:
+        assert rel(out[r0:r0 + h], svd_closed_form(p[r0:r0 + h])) < 1e-12, h
+        r0 += h
+
+
+def test_row_split_differs_from_whole_matrix():
+    p = np.random.default_rng(41).standard_normal((12, 16))
+    assert rel(ns5_row_split(p, [4, 8]), newton_schulz5(p)) > 0.1
+
+
+def test_row_split_blocks_are_independent_bitwise():
+    rng = np.random.default_rng(42)
+    p = rng.standard_normal((10, 6))
+    q = p.copy()
+    q[4:] = rng.standard_normal((6, 6))          # change the second block only
+    a, b = ns5_row_split(p, [4, 6]), ns5_row_split(q, [4, 6])
+    assert np.array_equal(a[:4], b[:4])
+    assert not np.array_equal(a[4:], b[4:])
+
+
+def test_row_split_of_equal_heights_is_per_head():
+    p = np.random.default_rng(43).standard_normal((24, 10))
+    assert np.array_equal(ns5_row_split(p, [6, 6, 6, 6]), ns5_per_head(p, 4))
+    assert np.array_equal(ns5_row_split(p, [24]), newton_schulz5(p))
+
+
+@pytest.mark.parametrize("hs", [[5, 4], [10, 0, 0], [11, -1], []])
+def test_row_split_rejects_bad_heights(hs):
+    with pytest.raises(ValueError):
+        ns5_row_split(np.ones((10, 4)), hs)
 
 
 # ---- per-iteration coefficient schedules ------------------------------------

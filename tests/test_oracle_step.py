@@ -7,7 +7,9 @@ Closed forms used:
   1 / sqrt(beta2 (1 - beta2) ms1 + (1 - beta2) ms2) before the rescale;
 * update: W1 - W0 = -lr * sqrt(max(1, out / F)) * O_hat (+ decoupled decay);
 * a convolution [out, *rest] steps exactly like the [out, prod(rest)] matrix
-  ("Fix convolution flattening...", "What it does": exact-equivalence oracle).
+  ("Fix convolution flattening...", "What it does": exact-equivalence oracle);
+* a row-split (fused q/k/v) weight: each block's own SVD closed form, with
+  the scale and NorMuon over the whole parameter.
 """
 import json
 import os
@@ -18,6 +20,7 @@ import pytest
 import synth
 from oracle import (MuonHParams, flatten_param, muon_step, nesterov_momentum, newton_schulz5,
                     normuon, ns5_megabatch, round_bf16, round_f32, spectral_lr)
+from test_oracle_ns5 import svd_closed_form
 
 MU = 0.95
 
@@ -113,6 +116,32 @@ def test_one_step_update_closed_form(shape, normuon_on):
     lr_eff = 0.05 * np.sqrt(max(1.0, out / f))
     expect = round_f32(flatten_param(w) - lr_eff * o).reshape(shape)
     assert np.array_equal(r["w"], expect)
+
+
+@pytest.mark.parametrize("normuon_on", [False, True])
+def test_row_split_step_closed_form(normuon_on):
+    # A fused [q; k; v] weight of 24 x 8 with blocks 16, 4, 4: Newton-Schulz
+    # per block (each block's SVD), the spectral scale and NorMuon on the
+    # whole parameter (24 / 8: lr * sqrt(3)).
+    rng = np.random.default_rng(8)
+    hs = (16, 4, 4)
+    w = round_f32(0.02 * rng.standard_normal((24, 8)))
+    g = rng.standard_normal((24, 8))
+    hp = MuonHParams(lr=0.05, normuon=normuon_on, split_rows=hs, mom_dtype="f32")
+    r = muon_step(w, g, np.zeros((24, 8)), np.zeros(24), hp)
+    u = (1 + MU) * g
+    o = np.concatenate([svd_closed_form(u[0:16]), svd_closed_form(u[16:20]), svd_closed_form(u[20:24])])
+    assert rel(r["o"], o) < 1e-12
+    if normuon_on:
+        assert abs(np.linalg.norm(r["o_hat"]) - np.linalg.norm(r["o"])) < 1e-12 * np.linalg.norm(r["o"])
+        o, _ = normuon(o, np.zeros(24))
+    expect = flatten_param(w) - 0.05 * np.sqrt(3.0) * o
+    assert np.all(np.abs(r["w"] - expect) <= 2.0 ** -24 * np.abs(expect) + 1e-12)   # one fp32 rounding
+
+
+def test_row_split_needs_one_head():
+    with pytest.raises(ValueError):
+        muon_step(np.zeros((8, 4)), np.ones((8, 4)), np.zeros((8, 4)), hp=MuonHParams(heads=2, split_rows=(4, 4)))
 
 
 def test_decoupled_weight_decay():
