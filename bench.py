@@ -254,7 +254,7 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "update GEMM X' = B X + a X, all seven matrices per launch (gemm_nt_bf16_kernel<256, false>)",
+            "kernel": "update GEMM X' = B X + a X, all seven matrices per launch (gemm_nt_bf16_kernel<256, false, true>)",
             "achieved": round(upd_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
