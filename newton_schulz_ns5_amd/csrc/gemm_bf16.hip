@@ -430,9 +430,11 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   // ---- epilogue --------------------------------------------------------------
   // Accumulator register r of a 32x32 block holds row 8 (r / 4) + 4 (l / 32)
   // + (r % 4) and column l % 32.  The tile is staged through LDS in two
-  // passes of BT/2 rows (the waves with wm == pass write theirs) as a
-  // row-major fp32 array S with a 16-byte aligned pitch; register indices are
-  // compile-time constants.  Then, with 16-byte global accesses:
+  // passes of BT/2 rows as a row-major fp32 array S with a 16-byte aligned
+  // pitch; register indices are compile-time constants.  Pass p stages block
+  // rows F/2 p .. F/2 p + F/2 - 1 of all four waves, so every wave writes in
+  // every pass: staged row s is tile row WT (s / HWT) + HWT p + s % HWT.
+  // Then, with 16-byte global accesses:
   //  - row pass: thread -> (row, 8 consecutive columns); v = alpha S
   //    (+ beta D when D is not folded into the products) is written back to S
   //    and stored row-major to C;
@@ -476,6 +478,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   };
 
   constexpr int PITCH = BT + 4;      // floats per staged row
+  constexpr int HWT = WT / 2;        // rows of one wave's quadrant staged per pass
   constexpr int CPR = BT / 8;        // 8-column chunks per row
   constexpr int RPI = 256 / CPR;     // rows per step of the row pass
   constexpr int NIT = RH / RPI;      // steps of the row pass
@@ -486,20 +489,20 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   // the accumulators are dead after the second pass's staging.
   auto epilogue_pass = [&](auto pass_c) {
     constexpr int pass = decltype(pass_c)::value;
-    if (wm == pass) {
 #pragma unroll
-      for (int i = 0; i < F; ++i)
+    for (int ii = 0; ii < F / 2; ++ii)
 #pragma unroll
-        for (int j = 0; j < F; ++j)
+      for (int j = 0; j < F; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-            const int col = wn * WT + j * 32 + (lane & 31);
-            S[row * PITCH + col] = acc[i][j][r];
-          }
-    }
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * HWT + ii * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const int col = wn * WT + j * 32 + (lane & 31);
+          S[row * PITCH + col] = acc[pass * (F / 2) + ii][j][r];
+        }
     __syncthreads();
-    const int i0 = tm * BT + pass * RH;
+    // tile row of staged row s (8-row chunks never straddle a quadrant band)
+    auto trow = [&](int s) { return (s / HWT) * WT + pass * HWT + (s % HWT); };
+    const int i0 = tm * BT;
     const int j0 = tn * BT;
     // Almost every tile: all its rows and columns are stored, bf16, no D,
     // aligned rows.  Then both passes store bf16(alpha S) with 16-byte stores;
@@ -508,7 +511,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
     // the chunks on or above the diagonal (element stores where the diagonal
     // crosses a chunk) and the transposed pass mirrors the strictly upper
     // part, so the stored matrix is exactly symmetric.
-    const bool fast = obf && !Dg && i0 + RH <= Mlim && j0 + BT <= Nlim && (!Cg || cvec) && (!Tg || tvec);
+    const bool fast = obf && !Dg && i0 + BT <= Mlim && j0 + BT <= Nlim && (!Cg || cvec) && (!Tg || tvec);
     if (fast) {
       if (Cg) {
         const int c8 = (tid % CPR) * 8, r0 = tid / CPR;
@@ -522,8 +525,9 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
           w[1] = pack_bf2(alpha * s0[2], alpha * s0[3]);
           w[2] = pack_bf2(alpha * s1[0], alpha * s1[1]);
           w[3] = pack_bf2(alpha * s1[2], alpha * s1[3]);
-          uint8_t* const dst = Cg + ((int64_t)(i0 + rr) * ldc + j0 + c8) * 2;
-          const int lo = pass * RH + rr - c8;  // columns c8 + e with e >= lo are on or above the diagonal
+          const int tr = trow(rr);
+          uint8_t* const dst = Cg + ((int64_t)(i0 + tr) * ldc + j0 + c8) * 2;
+          const int lo = tr - c8;  // columns c8 + e with e >= lo are on or above the diagonal
           if (!diag || lo <= 0) {
             *(u32x4*)dst = w;
           } else if (lo < 8) {
@@ -535,14 +539,15 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
 #pragma unroll 2
         for (int idx = tid; idx < BT * R8; idx += 256) {
           const int jj = idx % BT, i8 = (idx / BT) * 8;
-          // mirrored rows i8 + e (tile rows pass * RH + i8 + e) strictly below column jj
-          const int hi = diag ? jj - (pass * RH + i8) : 8;
+          // mirrored rows i8 + e (tile rows trow(i8) + e) strictly below column jj
+          const int ti = trow(i8);
+          const int hi = diag ? jj - ti : 8;
           if (hi <= 0) continue;
           u32x4 w;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             w[e] = pack_bf2(alpha * S[(i8 + 2 * e) * PITCH + jj], alpha * S[(i8 + 2 * e + 1) * PITCH + jj]);
-          uint8_t* const dst = Tg + ((int64_t)(j0 + jj) * ldt + i0 + i8) * 2;
+          uint8_t* const dst = Tg + ((int64_t)(j0 + jj) * ldt + i0 + ti) * 2;
           if (hi >= 8) {
             *(u32x4*)dst = w;
           } else {
@@ -558,7 +563,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
 #pragma unroll 1
       for (int it = 0; it < NIT; ++it) {
         const int rr = r0 + it * RPI;
-        const int i = i0 + rr;
+        const int i = i0 + trow(rr);
         float* srow = S + rr * PITCH + c8;
         f32x4 s0 = *(const f32x4*)srow, s1 = *(const f32x4*)(srow + 4);
         float v[8];
@@ -590,7 +595,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
 #pragma unroll 1
         for (int idx = tid; idx < BT * R8; idx += 256) {
           const int jj = idx % BT, i8 = (idx / BT) * 8;
-          const int jt = j0 + jj, it8 = i0 + i8;
+          const int jt = j0 + jj, it8 = i0 + trow(i8);
           float v[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = S[(i8 + e) * PITCH + jj];

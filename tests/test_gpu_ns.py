@@ -201,3 +201,35 @@ def test_constant_schedule_is_bitwise_the_scalar_path():
     b = ns.ns_batched(xt, steps=5, coeffs=[oracle.QUINTIC] * 5)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# ---- coefficients with c = 0 ---------------------------------------------------
+# With c = 0 the polynomial step is B = b A: the kernel then adds b A as an
+# explicit D operand in the epilogue instead of inside the products.  The cubic
+# Newton-Schulz iteration (a, b, c) = (3/2, -1/2, 0) is the textbook case.
+CUBIC = (1.5, -0.5, 0.0)
+
+
+@pytest.mark.parametrize("compute", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(2, 300, 520), (1, 256, 256), (1, 640, 384)])
+def test_cubic_coefficients_parity(shape, compute):
+    torch = torch_cuda()
+    dt = "bf16" if compute == "bf16" else "f32"
+    x = synth.gaussian(shape, (23, shape[1], shape[2], 1, 0), dt)
+    out = ns.ns_batched(to_dev(x, dt), steps=5, coeffs=CUBIC, compute_dtype=compute)
+    torch.cuda.synchronize()
+    got, xin = to_f64(out), storage_f64(x, dt)
+    err = max(rel_fro(got[i], oracle.newton_schulz5(xin[i], steps=5, coeffs=CUBIC)) for i in range(shape[0]))
+    assert err <= TOL[compute], err
+
+
+def test_schedule_mixing_zero_and_nonzero_c():
+    # Iterations with c = 0 (explicit D) and c != 0 (D inside the products) in one call.
+    torch = torch_cuda()
+    sched = [oracle.QUINTIC, CUBIC, oracle.QUINTIC, CUBIC, (15 / 8, -10 / 8, 3 / 8)]
+    x = synth.gaussian((2, 512, 768), (24, 0, 0, 1, 0), "bf16")
+    out = ns.ns_batched(to_dev(x, "bf16"), steps=5, coeffs=sched)
+    torch.cuda.synchronize()
+    got, xin = to_f64(out), storage_f64(x, "bf16")
+    err = max(rel_fro(got[i], oracle.newton_schulz5(xin[i], steps=5, coeffs=sched)) for i in range(2))
+    assert err <= TOL["bf16"], err
