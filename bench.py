@@ -11,8 +11,14 @@ matrices of the workload definition (U diag(i^-0.7) V^T + 0.1 N(0,1)), bf16;
 master weights fp32 N(0, 0.02^2); momentum bf16; all resident in HBM before
 timing starts.
 
+With --layers L > 1 a step covers L such layers in the same one call (the
+model-wide step: 32 layers are the 224 matrices of Llama-3-8B); the gradients
+of every layer then come from the device generator (the same power-law signal
+per shape, torch's generator for the noise), since host generation of 7e9
+values would take minutes.
+
 Prints one JSON line.  `value` is Newton-Schulz orthogonalizations per second
-(7 per step).  `roofline` covers the dominant kernel (the X <- a X + B X
+(7 L per step).  `roofline` covers the dominant kernel (the X <- a X + B X
 update GEMM) from HIP events recorded around each of its launches inside the
 timed region; `cpu_baseline` times the float64 oracle on a bounded sample.
 """
@@ -58,6 +64,27 @@ def make_layer_inputs():
             weights[n] = synth.gaussian(shape, (WORKLOAD_ID, 0, index[n], 0, synth.ROLE_WEIGHT), "f32", std=0.02)
         print(f"[bench] generated {'+'.join(names)} {shape} in {time.perf_counter() - t:.1f} s",
               file=sys.stderr, flush=True)
+    return grads, weights
+
+
+def make_model_inputs(layers, dev):
+    """Device-generated inputs of `layers` layers (layer l, matrix i: the
+    shape's signal plus noise keyed (workload 5, l, i, step 1); weights
+    N(0, 0.02^2) from the device generator keyed (5, l, i, 0, weight))."""
+    import torch
+    import synth
+    index = {name: i for i, (name, _) in enumerate(LAYER)}
+    grads, weights = {}, {}
+    for shape, names in groups_of_layer():
+        sig = torch.from_numpy(synth.power_law_signal(shape, (WORKLOAD_ID, 0, index[names[0]]))
+                               .astype(np.float32)).to(dev)
+        for l in range(layers):
+            for n in names:
+                grads[(l, n)] = synth.power_law_device(sig, (5, l, index[n], 1))
+                gen = torch.Generator(device=dev)
+                gen.manual_seed(synth.key_seed((5, l, index[n], 0, synth.ROLE_WEIGHT)))
+                weights[(l, n)] = 0.02 * torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+        del sig
     return grads, weights
 
 
@@ -134,6 +161,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--layers", type=int, default=1,
+                    help="Llama-3-8B layers per step (1: the layer workload; 32: the whole model)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the steps, fill and then sum a buffer of this many MiB (known bytes written "
                          "and read, for calibrating HBM traffic counters)")
@@ -152,14 +181,26 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
 
+    if args.layers < 1 or args.layers > 64:
+        print("--layers must be in 1..64", file=sys.stderr)
+        sys.exit(2)
     t_gen = time.perf_counter()
-    grads, weights = make_layer_inputs()
+    if args.layers == 1:
+        grads, weights = make_layer_inputs()
+    else:
+        dgrads, dweights = make_model_inputs(args.layers, dev)
     print(f"[bench] inputs generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
 
     groups = []
     for shape, names in groups_of_layer():
-        G = [torch.from_numpy(grads[n].view(np.int16)).view(torch.bfloat16).to(dev) for n in names]
-        W = [torch.from_numpy(weights[n]).to(dev) for n in names]
+        if args.layers == 1:
+            G = [torch.from_numpy(grads[n].view(np.int16)).view(torch.bfloat16).to(dev) for n in names]
+            W = [torch.from_numpy(weights[n]).to(dev) for n in names]
+        else:
+            keys = [(l, n) for l in range(args.layers) for n in names]
+            G = [dgrads[k] for k in keys]
+            W = [dweights[k] for k in keys]
+            names = [f"{n}{l}" for l, n in keys]
         M = [torch.zeros(shape, dtype=torch.bfloat16, device=dev) for _ in names]
         V = [torch.zeros(shape[0], dtype=torch.float32, device=dev) for _ in names]
         WM = [w.to(torch.bfloat16) for w in W]
@@ -219,9 +260,10 @@ def main():
     upd_avg_ms = upd["ms"] / max(upd["launches"], 1)
     upd_tflops = upd["flop"] / (upd["ms"] * 1e-3) / 1e12 if upd["ms"] > 0 else 0.0
 
-    fl_L = sum(ns_flops(*s)[0] for _, s in LAYER)
-    fl_E = sum(ns_flops(*s)[1] for _, s in LAYER)
-    value = len(LAYER) / (ms_per_step * 1e-3)
+    nmat = len(LAYER) * args.layers
+    fl_L = args.layers * sum(ns_flops(*s)[0] for _, s in LAYER)
+    fl_E = args.layers * sum(ns_flops(*s)[1] for _, s in LAYER)
+    value = nmat / (ms_per_step * 1e-3)
     tf_L = fl_L / (ms_per_step * 1e-3) / 1e12
     tf_E = fl_E / (ms_per_step * 1e-3) / 1e12
     per_class = {k: {"launches": v["launches"], "avg_us": round(1e3 * v["ms"] / max(v["launches"], 1), 2),
@@ -241,8 +283,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "llama3-8b-layer-muon-normuon-step",
-            "matrices": len(LAYER),
+            "workload": ("llama3-8b-layer-muon-normuon-step" if args.layers == 1
+                         else f"llama3-8b-{args.layers}-layer-muon-normuon-step"),
+            "matrices": nmat,
             "groups": [f"{len(gr['names'])}x{gr['shape'][0]}x{gr['shape'][1]}" for gr in groups],
             "ns_iterations": 5,
             "ns_compute": "bf16 storage, fp32 accumulate (MFMA)",
@@ -254,18 +297,20 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "update GEMM X' = B X + a X, all seven matrices per launch (gemm_nt_bf16_kernel<256, false, true>)",
+            "kernel": f"update GEMM X' = B X + a X, all {nmat} matrices per launch (gemm_nt_bf16_kernel<256, false, true>)",
             "achieved": round(upd_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(upd_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic_for("update"),
+            "traffic": traffic_for("update") if args.layers == 1 else None,
             "launches": upd["launches"],
             "avg_launch_us": round(upd_avg_ms * 1e3, 2),
             "flop_per_launch": upd["flop"] / max(upd["launches"], 1),
         },
     }
     if not args.no_cpu_baseline:
+        if args.layers != 1:
+            grads, weights = make_layer_inputs()
         print("[bench] timing the oracle on the CPU", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(grads, weights, args.cpu_seconds)
     print(json.dumps(out), flush=True)
