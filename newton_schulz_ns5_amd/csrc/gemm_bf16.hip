@@ -628,14 +628,12 @@ hipError_t launch_one(const GemmGroup& g, hipStream_t s) {
 hipError_t launch_gemm_bf16(const GemmGroup& g, bool syrk, bool nn, int tile, hipStream_t s) {
   // Every K is a multiple of 128 and at least the tile edge (the pipeline and
   // the peeled diagonal slices rely on it); SYRK products are NT.
+  // Products are either symmetric NT (Gram, polynomial) or NN (update).
   for (int i = 0; i < g.nprob; ++i)
     if (g.prob[i].K % 128 != 0 || g.prob[i].K < tile) return hipErrorInvalidValue;
-  if (syrk && nn) return hipErrorInvalidValue;
-  if (tile == 256)
-    return syrk ? launch_one<256, true, false>(g, s)
-                : (nn ? launch_one<256, false, true>(g, s) : launch_one<256, false, false>(g, s));
-  return syrk ? launch_one<128, true, false>(g, s)
-              : (nn ? launch_one<128, false, true>(g, s) : launch_one<128, false, false>(g, s));
+  if (syrk == nn) return hipErrorInvalidValue;
+  if (tile == 256) return syrk ? launch_one<256, true, false>(g, s) : launch_one<256, false, true>(g, s);
+  return syrk ? launch_one<128, true, false>(g, s) : launch_one<128, false, true>(g, s);
 }
 
 }  // namespace muon

@@ -107,6 +107,7 @@ struct ApplyParams {
 };
 
 // Launchers (return hipSuccess or the launch error).
+// bf16: symmetric NT products (syrk) or NN products (nn), exactly one of the two.
 hipError_t launch_gemm_bf16(const GemmGroup& g, bool syrk, bool nn, int tile, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmParams& p, bool nn, bool syrk, hipStream_t s);
 hipError_t launch_prep(const PrepParams& p, int nb, hipStream_t s);
