@@ -266,9 +266,19 @@ def main():
     value = nmat / (ms_per_step * 1e-3)
     tf_L = fl_L / (ms_per_step * 1e-3) / 1e12
     tf_E = fl_E / (ms_per_step * 1e-3) / 1e12
-    per_class = {k: {"launches": v["launches"], "avg_us": round(1e3 * v["ms"] / max(v["launches"], 1), 2),
-                     "share": round(v["ms"] / max(sum(x["ms"] for x in prof.values()), 1e-9), 4)}
-                 for k, v in prof.items()}
+    # Per kernel class: launches, mean launch time, share of kernel time, and the
+    # rate of its algorithmic work (GB/s of algorithmic bytes for the memory-bound
+    # classes, TFLOP/s for the GEMMs).
+    per_class = {}
+    for k, v in prof.items():
+        sec = v["ms"] * 1e-3
+        e = {"launches": v["launches"], "avg_us": round(1e3 * v["ms"] / max(v["launches"], 1), 2),
+             "share": round(v["ms"] / max(sum(x["ms"] for x in prof.values()), 1e-9), 4)}
+        if sec > 0 and v["flop"] > 0:
+            e["tflops"] = round(v["flop"] / sec / 1e12, 1)
+        elif sec > 0 and v["bytes"] > 0:
+            e["gbps"] = round(v["bytes"] / sec / 1e9, 1)
+        per_class[k] = e
     out = {
         "metric": METRIC,
         "value": round(value, 3),

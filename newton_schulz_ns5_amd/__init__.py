@@ -284,6 +284,17 @@ def step_groups(groups, *, hp=None, workspace=None, **kw):
     return None
 
 
+def _check_scalars(hp):
+    """The scalar hyperparameter checks of muon_step_groups, run early."""
+    vals = (hp.lr, hp.momentum, hp.weight_decay, hp.extra_scale)
+    if not all(math.isfinite(v) for v in vals):
+        raise MuonError(_lib.MUON_ERR_INVALID_ARG, "lr, momentum, weight_decay and extra_scale must be finite")
+    if hp.normuon and not (0.0 <= hp.beta2 <= 1.0 and 0.0 <= hp.norm_eps < math.inf):
+        raise MuonError(_lib.MUON_ERR_INVALID_ARG, "beta2 must be in [0,1] and norm_eps >= 0")
+    if hp.fan_out < 0 or hp.fan_in < 0:
+        raise MuonError(_lib.MUON_ERR_INVALID_ARG, "fan_out/fan_in must be >= 0")
+
+
 class MuonNS5:
     """Muon / NorMuon over a list of matrix-shaped parameters.
 
@@ -326,6 +337,16 @@ class MuonNS5:
                     "mom": torch.zeros(p.shape, dtype=md, device=p.device),
                     "var": torch.zeros(p.shape[0], dtype=torch.float32, device=p.device) if normuon else None,
                 }
+        # Reject bad geometry (heads, row splits) and hyperparameters here, not
+        # at the first step: the workspace query checks every group's shape
+        # and the Newton-Schulz configuration without touching device memory.
+        _check_scalars(self.hp)
+        made = []
+        for (shape, dt, h, sp), ps in self.groups.items():
+            masters = [self.state[id(p)]["master"] for p in ps]
+            made.append(_make_group(masters, masters, [self.state[id(p)]["mom"] for p in ps], None, None, h,
+                                    list(sp) if sp else None))
+        self.workspace_bytes = step_groups_workspace_bytes([g for g, _ in made], self.hp) if made else 0
 
     def step(self):
         torch = _torch()

@@ -170,6 +170,27 @@ def test_split_blocks_step_like_their_own_groups_bitwise():
         r0 += h
 
 
+def test_split_step_is_independent_of_max_batch_bitwise():
+    # Three fused [q; k; v] weights stepped in passes of 2 (max_batch) or all at
+    # once, with NorMuon: bitwise the same.
+    torch = torch_cuda()
+    shape, hs, n = (384, 256), [256, 64, 64], 3
+    g = [to_dev(x, "bf16") for x in grads_for(10, n, shape, "bf16", 1, power=True)]
+
+    def state():
+        return {"w_master": [to_dev(x, "f32") for x in make_state(10, n, shape, "bf16", "bf16")],
+                "grads": g, "moms": [torch.zeros(shape, dtype=torch.bfloat16, device="cuda") for _ in range(n)],
+                "variances": [torch.zeros(shape[0], device="cuda") for _ in range(n)], "split_rows": hs}
+
+    a, b = state(), state()
+    ns.step_groups([a], normuon=True)
+    ns.step_groups([b], normuon=True, ns=ns.ns_config(max_batch=2))
+    torch.cuda.synchronize()
+    for key in ("w_master", "moms", "variances"):
+        for x, y in zip(a[key], b[key]):
+            assert torch.equal(x, y), key
+
+
 def test_weight_decay_and_gate_shape_lr():
     # fan_out / fan_in = 3.5 > 1 scales lr by sqrt(3.5).
     run_steps((448, 128), 1, "bf16", "bf16", "bf16", steps=1, wd=0.1)
@@ -293,3 +314,45 @@ def test_step_with_coefficient_schedule():
     hp = oracle.MuonHParams(coeffs=sched, mom_dtype="bf16")
     r = oracle.muon_step(w0.astype(np.float64), storage_f64(g, "bf16"), np.zeros(shape), np.zeros(shape[0]), hp)
     assert rel_fro(to_f64(W[0]) - w0, r["w"] - w0) <= TOL["bf16"]
+
+
+def test_muon_ns5_optimizer_two_steps():
+    # The optimizer class end to end: bf16 and fp32 weights, a convolution, a
+    # per-head weight and a fused [q; k; v] weight in one MuonNS5, NorMuon on,
+    # two steps with .grad set; every parameter against its own oracle step.
+    torch = torch_cuda()
+    specs = [((256, 384), torch.bfloat16, 1, None), ((128, 256), torch.float32, 1, None),
+             ((8, 4, 3, 3), torch.bfloat16, 1, None), ((256, 384), torch.bfloat16, 4, None),
+             ((384, 256), torch.bfloat16, 1, (256, 64, 64))]
+    ps, ostate, hps = [], [], []
+    for k, (shape, dt, h, sp) in enumerate(specs):
+        w0 = synth.gaussian(shape, (30, k, 0, 0, synth.ROLE_WEIGHT), "f32", std=0.02)
+        p = torch.nn.Parameter(to_dev(w0, "f32").to(dt))
+        ps.append(p)
+        wq = to_f64(p.data.float())          # the master starts from the parameter's stored value
+        mdt = "bf16" if dt == torch.bfloat16 else "f32"
+        ostate.append({"w": wq, "m": np.zeros(shape), "v": np.zeros(shape[0])})
+        hps.append(oracle.MuonHParams(lr=0.05, normuon=True, heads=h, split_rows=sp, mom_dtype=mdt))
+    opt = ns.MuonNS5(ps, lr=0.05, normuon=True, heads={id(ps[3]): 4}, split_rows={id(ps[4]): [256, 64, 64]})
+    for step in (1, 2):
+        gbits = []
+        for k, (shape, dt, h, sp) in enumerate(specs):
+            r, c = shape[0], int(np.prod(shape[1:]))
+            g = synth.power_law((r, c), (30, k, 1), (30, k, 1, step), "bf16").reshape(shape)
+            gbits.append(g)
+            ps[k].grad = to_dev(g, "bf16").to(specs[k][1])
+        before = [to_f64(opt.state[id(p)]["master"]) for p in ps]
+        opt.step()
+        torch.cuda.synchronize()
+        for k, p in enumerate(ps):
+            gin = storage_f64(gbits[k], "bf16")
+            r = oracle.muon_step(ostate[k]["w"], gin, ostate[k]["m"], ostate[k]["v"], hps[k])
+            master = to_f64(opt.state[id(p)]["master"])
+            err = rel_fro(master - before[k], r["w"] - ostate[k]["w"])
+            assert err <= TOL["bf16"], (step, k, err)
+            if p.dtype == torch.bfloat16:
+                got = p.data.cpu().view(torch.int16).numpy().view(np.uint16)
+                assert np.array_equal(got, synth.f64_to_bf16_bits(master)), (step, k)
+            else:
+                assert p.data.data_ptr() == opt.state[id(p)]["master"].data_ptr()
+            ostate[k].update(w=r["w"], m=r["m"], v=r["v"])

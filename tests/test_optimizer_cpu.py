@@ -1,0 +1,46 @@
+"""MuonNS5 rejects bad geometry and hyperparameters when it is built, before
+any step (on the CPU: the checks run the library's workspace query, which
+touches no device memory)."""
+import math
+
+import pytest
+import torch
+
+import newton_schulz_ns5_amd as ns
+
+
+def params(*shapes, dtype=torch.bfloat16):
+    return [torch.nn.Parameter(torch.zeros(s, dtype=dtype)) for s in shapes]
+
+
+def test_valid_configuration_reports_its_workspace():
+    ps = params((256, 384), (384, 256), (8, 4, 3, 3))
+    opt = ns.MuonNS5(ps, normuon=True, heads={id(ps[0]): 4}, split_rows={id(ps[1]): [256, 64, 64]})
+    assert opt.workspace_bytes > 0
+    assert len(opt.groups) == 3
+
+
+@pytest.mark.parametrize("kw", [
+    dict(heads=lambda ps: {id(ps[0]): 5}),                    # 256 rows do not split into 5 heads
+    dict(split_rows=lambda ps: {id(ps[0]): [200, 50]}),       # heights sum to 250, not 256
+    dict(split_rows=lambda ps: {id(ps[0]): [256, 0]}),        # empty block
+    dict(split_rows=lambda ps: {id(ps[1]): [4, 4]}),          # row splits are for 2-D weights
+    dict(heads=lambda ps: {id(ps[0]): 2}, split_rows=lambda ps: {id(ps[0]): [128, 128]}),
+])
+def test_bad_geometry_is_rejected_at_construction(kw):
+    ps = params((256, 384), (8, 4, 3, 3))
+    args = {k: v(ps) for k, v in kw.items()}
+    with pytest.raises(ns.MuonError):
+        ns.MuonNS5(ps, **args)
+
+
+@pytest.mark.parametrize("kw", [dict(lr=math.nan), dict(momentum=math.inf), dict(normuon=True, beta2=1.5),
+                                dict(normuon=True, norm_eps=-1.0), dict(ns_steps=0), dict(ns_eps=-1.0)])
+def test_bad_hyperparameters_are_rejected_at_construction(kw):
+    with pytest.raises(ns.MuonError):
+        ns.MuonNS5(params((64, 96)), **kw)
+
+
+def test_vectors_are_rejected():
+    with pytest.raises(ns.MuonError):
+        ns.MuonNS5(params((64,)))
