@@ -233,6 +233,8 @@ hipError_t launch_phase(std::vector<GemmParams>& probs, bool syrk, bool nn, int 
         grp.prob[grp.nprob++] = p;
         tiles += (int64_t)p.batch * p.tiles_per_batch;
       }
+      // Tile indices are 32-bit in the kernel (and a grid holds < 2^31 workgroups).
+      if (tiles > INT32_MAX) return hipErrorInvalidValue;
       grp.tile_start[grp.nprob] = (int32_t)tiles;
       double fl = 0, by = 0;  // algorithmic FLOPs and bytes of this launch
       for (int i = 0; i < grp.nprob; ++i) {
