@@ -156,23 +156,6 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams p) {
       }
     }
   }
-  if (p.XT) {
-    // Transposed copy: XT[oj0 + orow][oi0 + oc0 .. +16] = X[oi0 + oc0 + e][oj0 + orow].
-    const int orow = tid >> 2, oc0 = (tid & 3) * 16;
-    float v[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) v[e] = p.tall ? T[orow][oc0 + e] : T[oc0 + e][orow];
-    const int64_t xoff = (int64_t)bz * p.X_bs + (int64_t)(oj0 + orow) * p.mp + oi0 + oc0;
-    u32x4 a, b;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      a[w] = pack_bf2(v[2 * w], v[2 * w + 1]);
-      b[w] = pack_bf2(v[8 + 2 * w], v[8 + 2 * w + 1]);
-    }
-    u32x4* dst = (u32x4*)((uint16_t*)p.XT + xoff);
-    dst[0] = a;
-    dst[1] = b;
-  }
   const float tot = block_sum(s, red);
   if (tid == 0) {
     const int tiles = gridDim.x * gridDim.y;

@@ -202,7 +202,7 @@ hipError_t gemm_f32(GemmParams& p, bool nn, bool syrk, int cls, double flop, dou
 }
 
 // One pass of Newton-Schulz over nb same-shape matrices already loaded (X0,
-// X0^T, norm scales) into their own workspace region.
+// norm scales) into their own workspace region.
 struct NsJob {
   Geom g;
   int64_t nb;
@@ -248,9 +248,6 @@ hipError_t launch_phase(std::vector<GemmParams>& probs, bool syrk, bool nn, int 
   return hipSuccess;
 }
 
-// bf16 mode: every product is NT.  X and X^T ping-pong between two buffer
-// pairs; the update writes both (or, on the last iteration, the output in
-// parameter orientation).
 // (a, b, c) of iteration `it`.
 struct Coeffs { float a, b, c; };
 Coeffs coeffs_of(const muon_ns_config& cfg, int it) {
@@ -258,6 +255,9 @@ Coeffs coeffs_of(const muon_ns_config& cfg, int it) {
   return {cfg.a, cfg.b, cfg.c};
 }
 
+// bf16 mode: Gram and poly are symmetric NT products, the update is NN and
+// reads X row-major.  X ping-pongs between two buffers; the last update
+// writes the output in parameter orientation instead.
 hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_config& cfg, hipStream_t s) {
   std::vector<int> cur(jobs.size(), 0);
   for (int it = 0; it < cfg.steps; ++it) {
@@ -534,7 +534,6 @@ int muon_ns_batched(const void* x, int32_t x_dtype, int64_t x_batch_stride, int6
     pp.x = (const char*)x + c0 * x_batch_stride * xe;
     pp.x_bs = x_batch_stride; pp.x_rs = x_row_stride;
     pp.X = ws + L.X0; pp.X_bs = g.mp * g.np;
-    pp.XT = nullptr;
     pp.partial = (float*)(ws + L.partial);
     hipError_t e = run(MUON_K_PREP, 0, (double)nb * rows * cols * (xe + (g.bf ? 2 : 4)), s,
                        [&]() { return launch_prep(pp, (int)nb, s); });
@@ -768,7 +767,6 @@ int stage_group(const GroupPlan& P, const muon_hparams* hp, char* ws, int64_t c0
         pp.mom[i] = (char*)g->mom[c0 + s0 + i] + (size_t)(B.r0 * g->cols) * (size_t)mes;
       }
       pp.X = bws + L.X0 + (size_t)(s0 * B.H) * ge.mp * ge.np * (size_t)oes;
-      pp.XT = nullptr;
       pp.X_bs = ge.mp * ge.np;
       pp.partial = (float*)(bws + L.partial) + s0 * B.H * L.tiles;
       e = run(MUON_K_PREP, 0, (double)k * B.h * g->cols * (ges + 2 * mes + oes), s,

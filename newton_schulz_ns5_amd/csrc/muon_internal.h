@@ -63,7 +63,6 @@ struct PrepParams {
   int32_t src_dtype;      // x (mode 0) or grad (mode 1)
   int32_t mom_dtype;      // mode 1
   int32_t x_bf16;         // X0 storage dtype is bf16
-  void* XT;               // bf16 mode: X0^T [b][np][mp] as well (null otherwise)
   float mu; int32_t nesterov;
   const void* x; int64_t x_bs, x_rs;          // mode 0
   int64_t param_cols;                          // mode 1: row stride of a parameter
