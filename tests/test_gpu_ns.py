@@ -233,3 +233,21 @@ def test_schedule_mixing_zero_and_nonzero_c():
     got, xin = to_f64(out), storage_f64(x, "bf16")
     err = max(rel_fro(got[i], oracle.newton_schulz5(xin[i], steps=5, coeffs=sched)) for i in range(2))
     assert err <= TOL["bf16"], err
+
+
+# ---- the largest long side ------------------------------------------------------
+def test_largest_long_side_parity():
+    # (2^22 - 128) x 128, the longest side the library takes (a 256-row
+    # operand panel of it is just under 2^31 bytes, the buffer-descriptor
+    # limit), stored tall so that the load transposes it and the last update
+    # writes the transposed output.  One matrix against the float64 oracle
+    # (about 1.4 TFLOP of float64 work).
+    torch = torch_cuda()
+    n = (1 << 22) - 128
+    x = synth.gaussian((n, 128), (25, 1, 0, 1, 0), "bf16")
+    out = ns.ns_batched(to_dev(x, "bf16"))
+    torch.cuda.synchronize()
+    got = to_f64(out)
+    del out
+    err = rel_fro(got, oracle.newton_schulz5(storage_f64(x, "bf16")))
+    assert err <= TOL["bf16"], err
