@@ -104,12 +104,17 @@ def hparams(lr=0.05, momentum=0.95, nesterov=True, weight_decay=0.0, extra_scale
 
 
 # ---- workspace (caller-owned device memory; the library never allocates) ----
+# One cached buffer per (device, stream): calls enqueued on one stream run in
+# order and may share it; calls on different streams may overlap, so each
+# stream gets its own.  A buffer is allocated on (and, when it grows, released
+# to torch's caching allocator from) the stream that uses it.
 _WS = {}
 
 
 def _workspace(device, nbytes):
     torch = _torch()
-    key = (device.type, device.index)
+    stream = torch.cuda.current_stream(device)
+    key = (device.type, device.index, stream.cuda_stream)
     buf = _WS.get(key)
     if buf is None or buf.numel() < nbytes:
         _WS.pop(key, None)

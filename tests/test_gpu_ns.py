@@ -251,3 +251,26 @@ def test_largest_long_side_parity():
     del out
     err = rel_fro(got, oracle.newton_schulz5(storage_f64(x, "bf16")))
     assert err <= TOL["bf16"], err
+
+
+def test_two_streams_get_their_own_workspace():
+    # Calls enqueued on two streams at once, each with the binding's cached
+    # workspace, give what the same calls give one after the other.
+    torch = torch_cuda()
+    xa = to_dev(synth.gaussian((4, 512, 768), (26, 0, 0, 1, 0), "bf16"), "bf16")
+    xb = to_dev(synth.gaussian((4, 512, 768), (26, 1, 0, 1, 0), "bf16"), "bf16")
+    ra, rb = ns.ns_batched(xa), ns.ns_batched(xb)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            ya = ns.ns_batched(xa)
+        with torch.cuda.stream(s2):
+            yb = ns.ns_batched(xb)
+        outs.append((ya, yb))
+    torch.cuda.synchronize()
+    for ya, yb in outs:
+        assert torch.equal(ya, ra) and torch.equal(yb, rb)
