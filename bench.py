@@ -135,23 +135,213 @@ def cpu_baseline(grads, weights, target_seconds=20.0):
                       f"({dt:.1f} s), scaled by dense NS FLOPs ({f_sample:.3e} of {f_layer:.3e}) to the 7-matrix layer"}
 
 
+def source_digest():
+    """sha256 over the library's HIP sources (kernels and the host code that lays
+    out their operands), in file-name order."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "newton_schulz_ns5_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        h.update(name.encode())
+        h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()
+
+
 def traffic_for(kernel_name):
     """HBM bytes per launch from the committed counter summary (profiles/traffic.json),
-    used only while the GEMM source still has the hash the counters were taken with."""
+    used only while the library's sources still have the digest the counters were
+    taken with."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
         info = json.load(open(path))
-        src = os.path.join(ROOT, "newton_schulz_ns5_amd", "csrc", "gemm_bf16.hip")
-        import hashlib
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        digest = source_digest()
         rec = info.get(kernel_name)
         if rec and rec.get("source_sha256") == digest:
             return rec.get("bytes_per_launch")
     except Exception:
         return None
     return None
+
+
+def timed_steps(step_fn, steps, warmup):
+    """Warm up, then time `steps` calls of step_fn on the current stream with
+    HIP events (per-launch library timing on); returns ms per step and the
+    library's per-class launch totals."""
+    import torch
+    import newton_schulz_ns5_amd as ns
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        step_fn()
+    torch.cuda.synchronize()
+    ns.profile_reset()
+    ns.profile_enable(True)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        step_fn()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ns.profile_enable(False)
+    return ev0.elapsed_time(ev1) / steps, {k: ns.profile_query(k) for k in ns.KERNEL_CLASSES}
+
+
+def class_table(prof):
+    """Per kernel class: launches, mean launch time, share of kernel time and the
+    rate of its algorithmic work (TFLOP/s for the GEMMs, GB/s for the rest)."""
+    per_class = {}
+    total = max(sum(x["ms"] for x in prof.values()), 1e-9)
+    for k, v in prof.items():
+        sec = v["ms"] * 1e-3
+        e = {"launches": v["launches"], "avg_us": round(1e3 * v["ms"] / max(v["launches"], 1), 2),
+             "share": round(v["ms"] / total, 4)}
+        if sec > 0 and v["flop"] > 0:
+            e["tflops"] = round(v["flop"] / sec / 1e12, 1)
+            e["gbps"] = round(v["bytes"] / sec / 1e9, 1)
+        elif sec > 0 and v["bytes"] > 0:
+            e["gbps"] = round(v["bytes"] / sec / 1e9, 1)
+        per_class[k] = e
+    return per_class
+
+
+def side_workload(args, dev):
+    """The per-head and conv-megabatch workloads: one JSON line in the same
+    format as the layer workload.  Their Newton-Schulz GEMMs have m = 128..512,
+    so the roofline names the GEMM class with the largest share of time and
+    takes HBM as its bound when its algorithmic FLOP per byte is below the
+    ridge (2516.6 TFLOP/s over 8 TB/s)."""
+    import ctypes
+    import torch
+    import newton_schulz_ns5_amd as ns
+    import oracle
+    import synth
+    L = ns.lib()
+    sptr = lambda: ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    if args.workload == "heads":
+        # q_proj 4096 x 4096 as 32 heads of 128 rows, k_proj 1024 x 4096 as 8; N(0,1) bf16; NS only.
+        parts = []
+        for i, (rows, heads) in enumerate(((4096, 32), (1024, 8))):
+            x = synth.gaussian((rows, 4096), (3, 0, i, 1, synth.ROLE_GRAD), "bf16")
+            xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev).view(heads, rows // heads, 4096)
+            yt = torch.empty_like(xt)
+            cfg = ns.ns_config(compute_dtype="bf16")
+            ws = torch.empty(ns.ns_workspace_bytes(heads, rows // heads, 4096, cfg), dtype=torch.uint8, device=dev)
+            parts.append((xt, yt, cfg, ws, x))
+
+        def step_fn():
+            for xt, yt, cfg, ws, _ in parts:
+                n, r, c = xt.shape
+                rc = L.muon_ns_batched(ctypes.c_void_p(xt.data_ptr()), ns.MUON_BF16, xt.stride(0), xt.stride(1),
+                                       ctypes.c_void_p(yt.data_ptr()), ns.MUON_BF16, yt.stride(0), yt.stride(1),
+                                       n, r, c, ctypes.byref(cfg), ctypes.c_void_p(ws.data_ptr()), ws.numel(), sptr())
+                if rc != 0:
+                    raise RuntimeError(f"muon_ns_batched failed: {rc} {L.muon_last_error()}")
+        shapes = [(32, 128, 4096), (8, 128, 4096)]
+        workload = "llama3-8b-q-k-per-head-ns5"
+        extra = {"heads": ["q 32x128x4096", "k 8x128x4096"], "normuon": False, "step": "Newton-Schulz only"}
+
+        def cpu_leg():
+            t0, done = time.perf_counter(), 0
+            x = synth.bf16_bits_to_f64(parts[0][4])
+            while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0) and done < 32:
+                oracle.newton_schulz5(x[128 * done:128 * (done + 1)])
+                done += 1
+            dt = time.perf_counter() - t0
+            return done / dt, f"float64 numpy oracle, Newton-Schulz of {done} q heads (128 x 4096) in {dt:.1f} s"
+    else:
+        groups, shapes = [], []
+        for gi, (name, n, pshape) in enumerate(synth.conv_megabatches()):
+            rows, cols = pshape[0], int(np.prod(pshape[1:]))
+            gs = synth.power_law_many((rows, cols), (4, gi, 0), [(4, gi, i, 1) for i in range(n)], "bf16")
+            G = [torch.from_numpy(g.view(np.int16)).view(torch.bfloat16).to(dev).view(pshape) for g in gs]
+            W = [torch.from_numpy(synth.gaussian((rows, cols), (4, gi, i, 0, synth.ROLE_WEIGHT), "f32", std=0.02))
+                 .to(dev).view(pshape) for i in range(n)]
+            M = [torch.zeros(pshape, dtype=torch.bfloat16, device=dev) for _ in range(n)]
+            V = [torch.zeros(rows, dtype=torch.float32, device=dev) for _ in range(n)]
+            WM = [w.to(torch.bfloat16) for w in W]
+            groups.append(ns._make_group(W, G, M, V, WM, heads=1))
+            shapes.append((n, rows, cols))
+            if gi == 0:
+                sample = (synth.bf16_bits_to_f64(gs[0]), synth.gaussian((rows, cols), (4, 0, 0, 0, synth.ROLE_WEIGHT),
+                                                                        "f32", std=0.02))
+        hp = ns.hparams(lr=0.05, momentum=0.95, nesterov=True, normuon=True, beta2=0.95, norm_eps=1e-8,
+                        ns=ns.ns_config(compute_dtype="bf16"))
+        garr = (ns.Group * len(groups))(*[g for g, _ in groups])
+        wsb = ns.step_groups_workspace_bytes([g for g, _ in groups], hp)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+        def step_fn():
+            rc = L.muon_step_groups(garr, len(groups), ctypes.byref(hp), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                    sptr())
+            if rc != 0:
+                raise RuntimeError(f"muon_step_groups failed: {rc} {L.muon_last_error()}")
+        workload = "conv-megabatch-normuon-step"
+        extra = {"groups": [f"{n}x{r}x{c}" for n, r, c in shapes], "normuon": True,
+                 "step": "full Muon/NorMuon step"}
+
+        def cpu_leg():
+            t0, done = time.perf_counter(), 0
+            g, w = sample
+            ohp = oracle.MuonHParams(lr=0.05, normuon=True, mom_dtype="bf16")
+            while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0) and done < 64:
+                oracle.muon_step(w.astype(np.float64), g, np.zeros(g.shape), np.zeros(g.shape[0]), ohp)
+                done += 1
+            dt = time.perf_counter() - t0
+            # scaled to the workload's mix by dense float64 NS FLOPs
+            f1 = 5 * (4 * 256 * 256 * 1152 + 2 * 256 ** 3)
+            fw = sum(n * 5 * (4 * min(r, c) ** 2 * max(r, c) + 2 * min(r, c) ** 3) for n, r, c in shapes)
+            nm = sum(n for n, _, _ in shapes)
+            return (done / dt) * f1 / fw * nm, (f"float64 numpy oracle, {done} Muon/NorMuon steps of one 256 x 1152 "
+                                                f"matrix in {dt:.1f} s, scaled by dense NS FLOPs to the workload")
+
+    ms, prof = timed_steps(step_fn, args.steps, args.warmup)
+    nmat = sum(n for n, _, _ in shapes)
+    fl_L = sum(n * ns_flops(r, c)[0] for n, r, c in shapes)
+    fl_E = sum(n * ns_flops(r, c)[1] for n, r, c in shapes)
+    per_class = class_table(prof)
+    dom = max(("gram", "poly", "update"), key=lambda k: prof[k]["ms"])
+    d = prof[dom]
+    sec = d["ms"] * 1e-3
+    tf = d["flop"] / sec / 1e12
+    gbps = d["bytes"] / sec / 1e9
+    hbm = d["flop"] / max(d["bytes"], 1) < PEAK_BF16_TFLOPS / 8.0
+    out = {
+        "metric": METRIC, "value": round(nmat / (ms * 1e-3), 3), "unit": "orth/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": dict({"workload": workload, "matrices": nmat, "ns_iterations": 5,
+                        "ns_compute": "bf16 storage, fp32 accumulate (MFMA)",
+                        "params_per_s": round(sum(n * r * c for n, r, c in shapes) / (ms * 1e-3), 1),
+                        "tflops_L": round(fl_L / (ms * 1e-3) / 1e12, 2),
+                        "pct_peak_L": round(100 * fl_L / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                        "tflops_E": round(fl_E / (ms * 1e-3) / 1e12, 2),
+                        "kernel_classes": per_class}, **extra),
+        "roofline": {
+            "bound": "hbm" if hbm else "mfma",
+            "kernel": f"{dom} GEMM class (gemm_nt_bf16_kernel)",
+            "achieved": round(gbps if hbm else tf, 2),
+            "peak": 8000.0 if hbm else PEAK_BF16_TFLOPS,
+            "unit": "GB/s" if hbm else "TFLOP/s",
+            "frac": round((gbps / 8000.0) if hbm else (tf / PEAK_BF16_TFLOPS), 4),
+            "traffic": None,
+            "tflops": round(tf, 2), "gbps": round(gbps, 1),
+            "launches": d["launches"], "avg_launch_us": round(1e3 * d["ms"] / max(d["launches"], 1), 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the CPU", file=sys.stderr, flush=True)
+        v, desc = cpu_leg()
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        except Exception:
+            threads = os.cpu_count()
+        out["cpu_baseline"] = {"value": round(v, 6), "unit": "orth/s", "cores": int(threads), "kind": "oracle",
+                               "sample": desc}
+    print(json.dumps(out), flush=True)
 
 
 def main():
@@ -161,12 +351,21 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--workload", choices=["layer", "heads", "conv"], default="layer",
+                    help="layer: the Muon/NorMuon step of Llama-3-8B layers (the default line); heads: "
+                         "per-head Newton-Schulz of q [32,128,4096] and k [8,128,4096]; conv: the NorMuon step "
+                         "of the conv megabatches [64,256,128,3,3] and [32,512,512,5]")
     ap.add_argument("--layers", type=int, default=1,
                     help="Llama-3-8B layers per step (1: the layer workload; 32: the whole model)")
+    ap.add_argument("--print-source-digest", action="store_true",
+                    help="print the digest of the HIP sources that profiles/traffic.json is keyed on, and exit")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the steps, fill and then sum a buffer of this many MiB (known bytes written "
                          "and read, for calibrating HBM traffic counters)")
     args = ap.parse_args()
+    if args.print_source_digest:
+        print(source_digest())
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -180,6 +379,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+
+    if args.workload != "layer":
+        return side_workload(args, dev)
 
     if args.layers < 1 or args.layers > 64:
         print("--layers must be in 1..64", file=sys.stderr)
@@ -266,19 +468,7 @@ def main():
     value = nmat / (ms_per_step * 1e-3)
     tf_L = fl_L / (ms_per_step * 1e-3) / 1e12
     tf_E = fl_E / (ms_per_step * 1e-3) / 1e12
-    # Per kernel class: launches, mean launch time, share of kernel time, and the
-    # rate of its algorithmic work (GB/s of algorithmic bytes for the memory-bound
-    # classes, TFLOP/s for the GEMMs).
-    per_class = {}
-    for k, v in prof.items():
-        sec = v["ms"] * 1e-3
-        e = {"launches": v["launches"], "avg_us": round(1e3 * v["ms"] / max(v["launches"], 1), 2),
-             "share": round(v["ms"] / max(sum(x["ms"] for x in prof.values()), 1e-9), 4)}
-        if sec > 0 and v["flop"] > 0:
-            e["tflops"] = round(v["flop"] / sec / 1e12, 1)
-        elif sec > 0 and v["bytes"] > 0:
-            e["gbps"] = round(v["bytes"] / sec / 1e9, 1)
-        per_class[k] = e
+    per_class = class_table(prof)
     out = {
         "metric": METRIC,
         "value": round(value, 3),
