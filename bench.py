@@ -167,16 +167,15 @@ def traffic_for(kernel_name):
 
 def timed_steps(step_fn, steps, warmup):
     """Warm up, then time `steps` calls of step_fn on the current stream with
-    HIP events (per-launch library timing on); returns ms per step and the
-    library's per-class launch totals."""
+    HIP events; then run `steps` more with the library's per-launch events on.
+    The steps of these workloads are short, so events around every launch would
+    add their own gaps to the step time: ms per step comes from the first run,
+    the per-class launch totals from the second."""
     import torch
     import newton_schulz_ns5_amd as ns
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         step_fn()
-    torch.cuda.synchronize()
-    ns.profile_reset()
-    ns.profile_enable(True)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -185,8 +184,14 @@ def timed_steps(step_fn, steps, warmup):
         step_fn()
     ev1.record(stream)
     torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    ns.profile_reset()
+    ns.profile_enable(True)
+    for _ in range(steps):
+        step_fn()
+    torch.cuda.synchronize()
     ns.profile_enable(False)
-    return ev0.elapsed_time(ev1) / steps, {k: ns.profile_query(k) for k in ns.KERNEL_CLASSES}
+    return ms, {k: ns.profile_query(k) for k in ns.KERNEL_CLASSES}
 
 
 def class_table(prof):

@@ -174,6 +174,30 @@ __global__ __launch_bounds__(256) void norm_kernel(const NormParams p) {
   if (threadIdx.x == 0) p.rs[b] = 1.f / (sqrtf(tot) + p.eps);
 }
 
+// Split-K Gram: A = bf16(rs^2 * (part_0 + part_1 + ...)), the chunks added in
+// order.  Thread -> 8 consecutive elements of one row of the mp x mp matrix.
+__global__ __launch_bounds__(256) void split_sum_kernel(const SplitSumParams p) {
+  const int b = blockIdx.y;
+  const int64_t mm = (int64_t)p.mp * p.mp;
+  const int64_t e8 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  const float* src = p.part + (int64_t)b * p.ksplit * mm + e8;
+  f32x4 s0 = *(const f32x4*)src, s1 = *(const f32x4*)(src + 4);
+  for (int k = 1; k < p.ksplit; ++k) {
+    const f32x4 t0 = *(const f32x4*)(src + k * mm), t1 = *(const f32x4*)(src + k * mm + 4);
+    s0 += t0;
+    s1 += t1;
+  }
+  const float rsb = p.rs ? p.rs[b] : 1.f;
+  const float alpha = rsb * rsb;
+  u32x4 w;
+  w[0] = pack_bf2(alpha * s0[0], alpha * s0[1]);
+  w[1] = pack_bf2(alpha * s0[2], alpha * s0[3]);
+  w[2] = pack_bf2(alpha * s1[0], alpha * s1[1]);
+  w[3] = pack_bf2(alpha * s1[2], alpha * s1[3]);
+  const int64_t i = e8 / p.mp, j = e8 - i * p.mp;
+  *(u32x4*)((uint16_t*)p.A + (int64_t)b * p.a_bs + i * p.lda + j) = w;
+}
+
 // NorMuon row statistics: one wave64 per row.  Lane l sums the squares of
 // elements 512 t + 8 l + e (t = 0, 1, ...; e = 0..7) in that order.
 __global__ __launch_bounds__(256) void rowstat_kernel(const RowStatParams p) {
@@ -307,6 +331,13 @@ hipError_t launch_prep(const PrepParams& p, int nb, hipStream_t s) {
 hipError_t launch_norm(const NormParams& p, int nb, hipStream_t s) {
   if (nb <= 0) return hipSuccess;
   return launch_kernel(norm_kernel, dim3(nb), p, s);
+}
+
+hipError_t launch_split_sum(const SplitSumParams& p, int nb, hipStream_t s) {
+  // mp is a multiple of 128, so mp^2 / 8 is a whole number of 256-thread blocks.
+  if (nb <= 0) return hipSuccess;
+  if (p.mp <= 0 || p.mp % 128 != 0 || p.lda % 8 != 0 || p.ksplit < 1) return hipErrorInvalidValue;
+  return launch_kernel(split_sum_kernel, dim3((unsigned)((int64_t)p.mp * p.mp / 8 / 256), nb), p, s);
 }
 
 hipError_t launch_rowstat(const RowStatParams& p, int nb, hipStream_t s) {

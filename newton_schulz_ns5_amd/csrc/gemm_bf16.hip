@@ -175,10 +175,22 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   int b, tm, tn;
   const GemmParams& p = decode_tile<SYRK>(grp, b, tm, tn);
 
+  // Split K (SYRK only): batch entry b is chunk ch of matrix bm, covering K
+  // values [k0, k0 + Kc); chunk edges are multiples of 128.
+  int bm = b, k0 = 0, Kc = p.K;
+  if constexpr (SYRK) {
+    if (p.ksplit > 1) {
+      bm = b / p.ksplit;
+      const int ch = b - bm * p.ksplit, kb = p.K / 128;
+      k0 = 128 * (int)((int64_t)ch * kb / p.ksplit);
+      Kc = 128 * (int)((int64_t)(ch + 1) * kb / p.ksplit) - k0;
+    }
+  }
   const int ldp = __builtin_amdgcn_readfirstlane((int)p.ldp);
   const int ldq = __builtin_amdgcn_readfirstlane((int)p.ldq);
-  const uint16_t* Pg = (const uint16_t*)p.P + (int64_t)b * p.sP + (int64_t)tm * BT * p.ldp;
-  const uint16_t* Qg = (const uint16_t*)p.Q + (int64_t)b * p.sQ + (NN ? (int64_t)tn * BT : (int64_t)tn * BT * p.ldq);
+  const uint16_t* Pg = (const uint16_t*)p.P + (int64_t)bm * p.sP + (int64_t)tm * BT * p.ldp + k0;
+  const uint16_t* Qg =
+      (const uint16_t*)p.Q + (int64_t)bm * p.sQ + (NN ? (int64_t)tn * BT : (int64_t)tn * BT * p.ldq + k0);
   const int64_t qbytes = (NN ? (int64_t)p.K : (int64_t)BT) * p.ldq * 2;
   const __amdgpu_buffer_rsrc_t prs = make_rsrc(Pg, (int64_t)BT * p.ldp * 2);
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Qg, qbytes);
@@ -218,7 +230,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
       qvo[par] = prow * ldq * 2 + dkc * 16;
     }
   }
-  const int KT = p.K / KS;
+  const int KT = Kc / KS;
   auto slot = [&](int t, int op) { return smem + ((2 * t + op) % NSLOT) * OPB; };
   const uint32_t smem_lds =
       __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem);
@@ -287,7 +299,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
       a[u - F] = __builtin_bit_cast(bf16x8, *(const u32x4*)(slot(t, 0) + prd + (u - F) * 32 * ROWB + so));
   };
 
-  const float rsb = p.rs ? p.rs[b] : 1.f;
+  const float rsb = p.rs ? p.rs[bm] : 1.f;
   const float alpha = p.alpha * (p.alpha_pow == 2 ? rsb * rsb : (p.alpha_pow == 1 ? rsb : 1.f));
   const float beta = p.beta * (p.beta_pow == 1 ? rsb : 1.f);
 
@@ -445,7 +457,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   // compact generic path with element stores where needed.
   float* const S = reinterpret_cast<float*>(smem);
   const uint16_t* __restrict__ Dg = p.D ? (const uint16_t*)p.D + (int64_t)b * p.sD : nullptr;
-  const bool obf = SYRK || p.c_dtype == MUON_BF16;
+  const bool obf = p.c_dtype == MUON_BF16;  // fp32: split-K partial products
   const int esz = obf ? 2 : 4;
   uint8_t* const Cg = p.C ? (uint8_t*)p.C + (int64_t)b * p.sC * esz : nullptr;
   uint8_t* const Tg = SYRK ? Cg : (p.Ct ? (uint8_t*)p.Ct + (int64_t)b * p.sCt * esz : nullptr);

@@ -73,9 +73,20 @@ Geom make_geom(int64_t rows, int64_t cols, int32_t compute) {
   return g;
 }
 
+// K chunks of the Gram A = X X^T of a bf16 geometry (1: no split).  A matrix
+// with m <= 256 has one to three Gram tiles, too few workgroups to fill the
+// chip over a long K = n; its Gram is then computed in chunks of about 4 m
+// columns (at most 16), whose fp32 products are summed afterwards.  The count
+// depends on the shape only, so a matrix's result does not depend on its batch.
+int gram_ksplit(const Geom& g) {
+  if (!g.bf || g.mp > 256) return 1;
+  const int64_t s = g.np / (4 * g.mp);
+  return s < 2 ? 1 : (s > 16 ? 16 : (int)s);
+}
+
 // Workspace of `nb` NS problems.
 struct Layout {
-  size_t X0, X1, A, B, partial, rs, total;
+  size_t X0, X1, A, B, partial, rs, part, total;
   int tiles;
 };
 
@@ -91,6 +102,8 @@ Layout make_layout(const Geom& g, int64_t nb) {
   L.B = take((size_t)nb * g.mp * g.mp * es);
   L.partial = take((size_t)nb * L.tiles * 4);
   L.rs = take((size_t)nb * 4);
+  const int ks = gram_ksplit(g);
+  L.part = ks > 1 ? take((size_t)nb * ks * g.mp * g.mp * 4) : 0;
   L.total = off;
   return L;
 }
@@ -219,7 +232,9 @@ hipError_t launch_phase(std::vector<GemmParams>& probs, bool syrk, bool nn, int 
     std::vector<GemmParams*> sel;
     for (auto& p : probs)
       if (bf16_tile_for(p.M, p.N) == tile) sel.push_back(&p);
-    std::stable_sort(sel.begin(), sel.end(), [](const GemmParams* x, const GemmParams* y) { return x->K > y->K; });
+    // K per workgroup: a split-K problem's chunks are about K / ksplit long.
+    auto kwg = [](const GemmParams* x) { return x->ksplit > 1 ? x->K / x->ksplit : x->K; };
+    std::stable_sort(sel.begin(), sel.end(), [&](const GemmParams* x, const GemmParams* y) { return kwg(x) > kwg(y); });
     for (size_t i0 = 0; i0 < sel.size(); i0 += kMaxProblems) {
       GemmGroup grp{};
       grp.nprob = 0;
@@ -264,6 +279,8 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
     const bool first = it == 0, last = it == cfg.steps - 1;
     const Coeffs cf = coeffs_of(cfg, it);
     std::vector<GemmParams> gram, poly, upd;
+    struct Sum { SplitSumParams p; int nb; double bytes; };
+    std::vector<Sum> sums;
     for (size_t k = 0; k < jobs.size(); ++k) {
       const NsJob& J = jobs[k];
       const Geom& g = J.g;
@@ -285,6 +302,20 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
         p.rs = first ? rs : nullptr; p.alpha_pow = 2;
         p.batch = (int)J.nb;
         p.flop = B * m * m * n; p.bytes = B * (m * n + m * m) * 2;
+        const int ks = gram_ksplit(g);
+        if (ks > 1) {
+          // fp32 product of each K chunk; the sum below scales and rounds
+          SplitSumParams q{};
+          q.part = (const float*)(ws + J.L.part); q.ksplit = ks; q.mp = (int)g.mp;
+          q.A = A; q.lda = g.mp; q.a_bs = sa;
+          q.rs = p.rs;
+          sums.push_back({q, (int)J.nb, B * (ks * m * m * 4 + m * m * 2)});
+          p.C = ws + J.L.part; p.sC = sa; p.c_dtype = MUON_F32;
+          p.rs = nullptr;
+          p.batch = (int)(J.nb * ks);
+          p.ksplit = ks;
+          p.bytes += B * (ks - 1) * m * m * 4;
+        }
         gram.push_back(p);
       }
       {  // B = c A A + b A; A is stored exactly symmetric, so the b A term is
@@ -331,6 +362,9 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
     }
     hipError_t e;
     if ((e = launch_phase(gram, true, false, MUON_K_GRAM, s)) != hipSuccess) return e;
+    for (const Sum& u : sums)
+      if ((e = run(MUON_K_GRAM, 0, u.bytes, s, [&]() { return launch_split_sum(u.p, u.nb, s); })) != hipSuccess)
+        return e;
     if ((e = launch_phase(poly, true, false, MUON_K_POLY, s)) != hipSuccess) return e;
     if ((e = launch_phase(upd, false, true, MUON_K_UPDATE, s)) != hipSuccess) return e;
     for (auto& c : cur) c ^= 1;

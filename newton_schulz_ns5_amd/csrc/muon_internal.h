@@ -41,6 +41,9 @@ struct GemmParams {
   int32_t alpha_pow, beta_pow;  // alpha_b = alpha * rs[b]^alpha_pow ...
   int32_t batch;
   int32_t tiles_m, tiles_n, tiles_per_batch;
+  int32_t ksplit;         // bf16 SYRK: > 1 splits K into this many chunks (cut at multiples
+                          // of 128); batch entry b is chunk b % ksplit of matrix
+                          // b / ksplit (P, Q, rs), and C[b] receives that chunk's product
   double flop, bytes;     // host bookkeeping for launch timing (not read by kernels)
 };
 
@@ -78,6 +81,15 @@ struct NormParams {
   float* rs;              // rs[b] = 1 / (sqrt(sum partial) + eps)
 };
 
+// ---- split-K Gram: sum of the chunks' partial products -----------------------
+// A[b] = bf16(rs[b]^2 * sum_s part[b][s]) over full mp x mp matrices (rs may be
+// null: factor 1); the chunks are added in order s = 0, 1, ...
+struct SplitSumParams {
+  const float* part; int32_t ksplit; int32_t mp;
+  void* A; int64_t lda; int64_t a_bs;
+  const float* rs;
+};
+
 // ---- NorMuon statistics ---------------------------------------------------
 struct RowStatParams {
   const void* O; int32_t o_dtype; int64_t o_bs, o_rs;
@@ -111,6 +123,7 @@ hipError_t launch_gemm_bf16(const GemmGroup& g, bool syrk, bool nn, int tile, hi
 hipError_t launch_gemm_f32(const GemmParams& p, bool nn, bool syrk, hipStream_t s);
 hipError_t launch_prep(const PrepParams& p, int nb, hipStream_t s);
 hipError_t launch_norm(const NormParams& p, int nb, hipStream_t s);
+hipError_t launch_split_sum(const SplitSumParams& p, int nb, hipStream_t s);
 hipError_t launch_rowstat(const RowStatParams& p, int nb, hipStream_t s);
 hipError_t launch_rho(const RhoParams& p, int nb, hipStream_t s);
 hipError_t launch_apply(const ApplyParams& p, int nb, hipStream_t s);

@@ -274,3 +274,22 @@ def test_two_streams_get_their_own_workspace():
     torch.cuda.synchronize()
     for ya, yb in outs:
         assert torch.equal(ya, ra) and torch.equal(yb, rb)
+
+
+# A short side of at most 256 with a long side of at least 8x it: the Gram is
+# computed over K chunks whose fp32 products are summed in a fixed order
+# (even and uneven chunk edges, tall and wide, 2 to 16 chunks).
+@pytest.mark.parametrize("shape", [(3, 100, 1500), (2, 128, 1100), (2, 200, 2300), (1, 3000, 120), (2, 128, 8192)])
+def test_split_k_gram_shapes(shape):
+    err = run_case(shape, "bf16", "bf16", (27, shape[1], shape[2], 1, 0))
+    assert err <= TOL["bf16"], err
+
+
+def test_split_k_gram_batch_invariant():
+    # A 128 x 4096 matrix alone and as entry 2 of a batch of 5: bitwise equal.
+    torch = torch_cuda()
+    x = to_dev(synth.gaussian((5, 128, 4096), (27, 1, 0, 1, 0), "bf16"), "bf16")
+    full = ns.ns_batched(x)
+    one = ns.ns_batched(x[2:3].clone())
+    torch.cuda.synchronize()
+    assert torch.equal(full[2], one[0])
