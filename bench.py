@@ -165,33 +165,62 @@ def traffic_for(kernel_name):
     return None
 
 
-def timed_steps(step_fn, steps, warmup):
-    """Warm up, then time `steps` calls of step_fn on the current stream with
-    HIP events; then run `steps` more with the library's per-launch events on.
-    The steps of these workloads are short, so events around every launch would
-    add their own gaps to the step time: ms per step comes from the first run,
-    the per-class launch totals from the second."""
+def capture(step_fn):
+    """One step captured in a HIP graph (the library only enqueues kernels while
+    its launch timing is off); returns the graph's replay."""
     import torch
-    import newton_schulz_ns5_amd as ns
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            step_fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    return graph.replay
+
+
+def event_time(fn, steps, warmup):
+    """Milliseconds per call of fn, from HIP events on the current stream."""
+    import torch
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
-        step_fn()
+        fn()
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
     for _ in range(steps):
-        step_fn()
+        fn()
     ev1.record(stream)
     torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / steps
+    return ev0.elapsed_time(ev1) / steps
+
+
+def timed_steps(step_fn, steps, warmup):
+    """Time `steps` steps replayed from a HIP graph and `steps` steps launched
+    from the host, then run `steps` more with the library's per-launch events
+    on.  These steps are dozens of launches of a few microseconds each, so
+    launching them from the host leaves the GPU waiting between kernels; events
+    around every launch would add gaps of their own.  Returns ms per step
+    (graph, eager) and the per-class launch totals of the third run."""
+    import torch
+    import newton_schulz_ns5_amd as ns
+    ms_eager = event_time(step_fn, steps, warmup)
+    replay = capture(step_fn)
+    ms = event_time(replay, steps, warmup)
     ns.profile_reset()
     ns.profile_enable(True)
+    # A spin kernel of ~0.1 s keeps the GPU busy while the host enqueues the
+    # profiled steps, so the launches then run back to back and each event
+    # pair brackets its kernel rather than the host's launch latency.
+    torch.cuda._sleep(200_000_000)
     for _ in range(steps):
         step_fn()
     torch.cuda.synchronize()
     ns.profile_enable(False)
-    return ms, {k: ns.profile_query(k) for k in ns.KERNEL_CLASSES}
+    return ms, ms_eager, {k: ns.profile_query(k) for k in ns.KERNEL_CLASSES}
 
 
 def class_table(prof):
@@ -257,7 +286,7 @@ def side_workload(args, dev):
             dt = time.perf_counter() - t0
             return done / dt, f"float64 numpy oracle, Newton-Schulz of {done} q heads (128 x 4096) in {dt:.1f} s"
     else:
-        groups, shapes = [], []
+        groups, shapes, tensors = [], [], []
         for gi, (name, n, pshape) in enumerate(synth.conv_megabatches()):
             rows, cols = pshape[0], int(np.prod(pshape[1:]))
             gs = synth.power_law_many((rows, cols), (4, gi, 0), [(4, gi, i, 1) for i in range(n)], "bf16")
@@ -267,7 +296,8 @@ def side_workload(args, dev):
             M = [torch.zeros(pshape, dtype=torch.bfloat16, device=dev) for _ in range(n)]
             V = [torch.zeros(rows, dtype=torch.float32, device=dev) for _ in range(n)]
             WM = [w.to(torch.bfloat16) for w in W]
-            groups.append(ns._make_group(W, G, M, V, WM, heads=1))
+            groups.append(ns._make_group(W, G, M, V, WM, heads=1))  # its `keep` holds the tensors
+            tensors.append((G, W, M, V, WM))
             shapes.append((n, rows, cols))
             if gi == 0:
                 sample = (synth.bf16_bits_to_f64(gs[0]), synth.gaussian((rows, cols), (4, 0, 0, 0, synth.ROLE_WEIGHT),
@@ -302,7 +332,7 @@ def side_workload(args, dev):
             return (done / dt) * f1 / fw * nm, (f"float64 numpy oracle, {done} Muon/NorMuon steps of one 256 x 1152 "
                                                 f"matrix in {dt:.1f} s, scaled by dense NS FLOPs to the workload")
 
-    ms, prof = timed_steps(step_fn, args.steps, args.warmup)
+    ms, ms_eager, prof = timed_steps(step_fn, args.steps, args.warmup)
     nmat = sum(n for n, _, _ in shapes)
     fl_L = sum(n * ns_flops(r, c)[0] for n, r, c in shapes)
     fl_E = sum(n * ns_flops(r, c)[1] for n, r, c in shapes)
@@ -318,6 +348,8 @@ def side_workload(args, dev):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": dict({"workload": workload, "matrices": nmat, "ns_iterations": 5,
+                        "launch": "HIP graph replay of one step",
+                        "ms_per_step_host_launched": round(ms_eager, 4),
                         "ns_compute": "bf16 storage, fp32 accumulate (MFMA)",
                         "params_per_s": round(sum(n * r * c for n, r, c in shapes) / (ms * 1e-3), 1),
                         "tflops_L": round(fl_L / (ms * 1e-3) / 1e12, 2),

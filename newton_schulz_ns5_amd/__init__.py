@@ -215,7 +215,11 @@ def _make_group(w_master, grads, moms, variances=None, w_model=None, heads=1, sp
     g.grad_dtype = _dt(grads[0])
     g.mom_dtype = _dt(moms[0])
     g.model_dtype = MUON_BF16 if w_model else -1
-    keep = [_ptr_array(w_master), _ptr_array(grads), _ptr_array(moms)]
+    # `keep` holds the pointer tables and the tensors themselves: a Group is
+    # only valid while its tensors' memory is, so whoever holds the Group past
+    # this call holds `keep` with it.
+    keep = [_ptr_array(w_master), _ptr_array(grads), _ptr_array(moms),
+            (list(w_master), list(grads), list(moms), list(variances or []), list(w_model or []))]
     g.w_master = ctypes.cast(keep[0], ctypes.POINTER(ctypes.c_void_p))
     g.grad = ctypes.cast(keep[1], ctypes.POINTER(ctypes.c_void_p))
     g.mom = ctypes.cast(keep[2], ctypes.POINTER(ctypes.c_void_p))

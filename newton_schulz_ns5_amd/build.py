@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmuon_mi355x.so")
-SOURCES = ["gemm_bf16.hip", "gemm_f32.hip", "elementwise.hip", "muon_host.hip"]
+SOURCES = ["gemm_bf16.hip", "gemm_f32.hip", "elementwise.hip", "poly_small.hip", "muon_host.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-mcode-object-version=5", "-O3", "-std=c++17", "-fPIC",

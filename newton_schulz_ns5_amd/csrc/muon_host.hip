@@ -81,7 +81,7 @@ Geom make_geom(int64_t rows, int64_t cols, int32_t compute) {
 int gram_ksplit(const Geom& g) {
   if (!g.bf || g.mp > 256) return 1;
   const int64_t s = g.np / (4 * g.mp);
-  return s < 2 ? 1 : (s > 16 ? 16 : (int)s);
+  return s < 2 ? 1 : (s > kMaxKsplit ? kMaxKsplit : (int)s);
 }
 
 // Workspace of `nb` NS problems.
@@ -280,7 +280,9 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
     const Coeffs cf = coeffs_of(cfg, it);
     std::vector<GemmParams> gram, poly, upd;
     struct Sum { SplitSumParams p; int nb; double bytes; };
+    struct Fused { Poly128Params p; int nb; double flop, bytes; };
     std::vector<Sum> sums;
+    std::vector<Fused> fused;
     for (size_t k = 0; k < jobs.size(); ++k) {
       const NsJob& J = jobs[k];
       const Geom& g = J.g;
@@ -303,13 +305,24 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
         p.batch = (int)J.nb;
         p.flop = B * m * m * n; p.bytes = B * (m * n + m * m) * 2;
         const int ks = gram_ksplit(g);
-        if (ks > 1) {
+        if (ks > 1 && g.mp == 128) {
+          // fp32 product of each K chunk, summed by the fused kernel that also
+          // computes B (A is not stored)
+          Poly128Params q{};
+          q.part = (const float*)(ws + J.L.part); q.ksplit = ks;
+          q.rs = p.rs;
+          q.b = cf.b; q.c = cf.c;
+          q.B = Bm; q.ldb = g.mp; q.b_bs = sa;
+          fused.push_back({q, (int)J.nb, B * m * m * m, B * (ks * m * m * 4 + m * m * 2)});
+        } else if (ks > 1) {
           // fp32 product of each K chunk; the sum below scales and rounds
           SplitSumParams q{};
           q.part = (const float*)(ws + J.L.part); q.ksplit = ks; q.mp = (int)g.mp;
           q.A = A; q.lda = g.mp; q.a_bs = sa;
           q.rs = p.rs;
           sums.push_back({q, (int)J.nb, B * (ks * m * m * 4 + m * m * 2)});
+        }
+        if (ks > 1) {
           p.C = ws + J.L.part; p.sC = sa; p.c_dtype = MUON_F32;
           p.rs = nullptr;
           p.batch = (int)(J.nb * ks);
@@ -333,7 +346,7 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
         p.alpha = cf.c; p.beta = cf.b;
         p.batch = (int)J.nb;
         p.flop = B * m * m * m; p.bytes = B * 2 * m * m * 2;
-        poly.push_back(p);
+        if (!(gram_ksplit(g) > 1 && g.mp == 128)) poly.push_back(p);
       }
       {  // X' = B X + a X (times rs on the first iteration): NN with Q = X,
          // whose transposed tile is the D tile, so a X is added inside the
@@ -364,6 +377,9 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
     if ((e = launch_phase(gram, true, false, MUON_K_GRAM, s)) != hipSuccess) return e;
     for (const Sum& u : sums)
       if ((e = run(MUON_K_GRAM, 0, u.bytes, s, [&]() { return launch_split_sum(u.p, u.nb, s); })) != hipSuccess)
+        return e;
+    for (const Fused& u : fused)
+      if ((e = run(MUON_K_POLY, u.flop, u.bytes, s, [&]() { return launch_poly128(u.p, u.nb, s); })) != hipSuccess)
         return e;
     if ((e = launch_phase(poly, true, false, MUON_K_POLY, s)) != hipSuccess) return e;
     if ((e = launch_phase(upd, false, true, MUON_K_UPDATE, s)) != hipSuccess) return e;

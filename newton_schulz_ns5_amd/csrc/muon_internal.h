@@ -90,6 +90,17 @@ struct SplitSumParams {
   const float* rs;
 };
 
+// ---- split-K Gram sum fused with the polynomial, 128 x 128 matrices ----------
+// B[b] = bf16(c A A + b A) with A = bf16(rs[b]^2 * sum_s part[b][s]) (rs may
+// be null: factor 1); one workgroup per matrix.
+constexpr int kMaxKsplit = 16;   // K chunks of a split Gram, at most
+struct Poly128Params {
+  const float* part; int32_t ksplit;
+  const float* rs;
+  float b, c;
+  void* B; int64_t ldb; int64_t b_bs;
+};
+
 // ---- NorMuon statistics ---------------------------------------------------
 struct RowStatParams {
   const void* O; int32_t o_dtype; int64_t o_bs, o_rs;
@@ -124,6 +135,7 @@ hipError_t launch_gemm_f32(const GemmParams& p, bool nn, bool syrk, hipStream_t 
 hipError_t launch_prep(const PrepParams& p, int nb, hipStream_t s);
 hipError_t launch_norm(const NormParams& p, int nb, hipStream_t s);
 hipError_t launch_split_sum(const SplitSumParams& p, int nb, hipStream_t s);
+hipError_t launch_poly128(const Poly128Params& p, int nb, hipStream_t s);
 hipError_t launch_rowstat(const RowStatParams& p, int nb, hipStream_t s);
 hipError_t launch_rho(const RhoParams& p, int nb, hipStream_t s);
 hipError_t launch_apply(const ApplyParams& p, int nb, hipStream_t s);

@@ -44,3 +44,30 @@ def test_bad_hyperparameters_are_rejected_at_construction(kw):
 def test_vectors_are_rejected():
     with pytest.raises(ns.MuonError):
         ns.MuonNS5(params((64,)))
+
+
+def test_group_keeps_its_tensors_alive():
+    # A Group holds raw pointers; the `keep` returned with it must hold the
+    # tensors too, or memory freed (and possibly unmapped) behind the Group's
+    # back would be written by the next step that uses it.
+    import gc
+    import weakref
+    shape = (64, 96)
+
+    def make():
+        w = [torch.zeros(shape) for _ in range(2)]
+        g = [torch.zeros(shape, dtype=torch.bfloat16) for _ in range(2)]
+        m = [torch.zeros(shape, dtype=torch.bfloat16) for _ in range(2)]
+        v = [torch.zeros(shape[0]) for _ in range(2)]
+        wm = [torch.zeros(shape, dtype=torch.bfloat16) for _ in range(2)]
+        refs = [weakref.ref(t) for t in w + g + m + v + wm]
+        group, keep = ns._make_group(w, g, m, v, wm)
+        return group, keep, refs, w[1].data_ptr()
+
+    group, keep, refs, p1 = make()
+    gc.collect()
+    assert all(r() is not None for r in refs)
+    assert group.w_master[1] == p1
+    del keep
+    gc.collect()
+    assert all(r() is None for r in refs)
