@@ -453,8 +453,8 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   //  - transposed pass: thread -> (column, 8 consecutive rows), stored to
   //    T[j][i .. i+7] (SYRK: the mirrored half of C; the final output of a
   //    tall matrix: X'^T).
-  // Diagonal SYRK tiles, ragged edges, fp32 outputs and an explicit D take a
-  // compact generic path with element stores where needed.
+  // Ragged edges and an explicit D take a compact generic path with element
+  // stores where needed.
   float* const S = reinterpret_cast<float*>(smem);
   const uint16_t* __restrict__ Dg = p.D ? (const uint16_t*)p.D + (int64_t)b * p.sD : nullptr;
   const bool obf = p.c_dtype == MUON_BF16;  // fp32: split-K partial products
@@ -516,14 +516,36 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
     auto trow = [&](int s) { return (s / HWT) * WT + pass * HWT + (s % HWT); };
     const int i0 = tm * BT;
     const int j0 = tn * BT;
-    // Almost every tile: all its rows and columns are stored, bf16, no D,
-    // aligned rows.  Then both passes store bf16(alpha S) with 16-byte stores;
-    // the transposed pass recomputes alpha S, so its values are bitwise
-    // those of the row pass.  On a SYRK diagonal tile the row pass stores
+    // Almost every tile: all its rows and columns are stored, no D, aligned
+    // rows.  Then both passes store alpha S (bf16, or fp32 for split-K
+    // partial products) with 16-byte stores; the transposed pass recomputes
+    // alpha S, so its values are bitwise those of the row pass.  On a SYRK diagonal tile the row pass stores
     // the chunks on or above the diagonal (element stores where the diagonal
     // crosses a chunk) and the transposed pass mirrors the strictly upper
     // part, so the stored matrix is exactly symmetric.
-    const bool fast = obf && !Dg && i0 + BT <= Mlim && j0 + BT <= Nlim && (!Cg || cvec) && (!Tg || tvec);
+    const bool fast = !Dg && i0 + BT <= Mlim && j0 + BT <= Nlim && (!Cg || cvec) && (!Tg || tvec);
+    // Store elements e0 .. e1 - 1 of v[0..7] at dst (bf16 or fp32); one or
+    // two 16-byte stores when all eight are stored.
+    auto put8 = [&](uint8_t* dst, const float (&v)[8], int e0, int e1) {
+      if (obf) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf2(v[2 * e], v[2 * e + 1]);
+        if (e0 <= 0 && e1 >= 8) {
+          *(u32x4*)dst = w;
+        } else {
+          for (int e = e0; e < e1; ++e) ((uint16_t*)dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+        }
+      } else if (e0 <= 0 && e1 >= 8) {
+        f32x4 w0, w1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { w0[e] = v[e]; w1[e] = v[4 + e]; }
+        *(f32x4*)dst = w0;
+        *(f32x4*)(dst + 16) = w1;
+      } else {
+        for (int e = e0; e < e1; ++e) ((float*)dst)[e] = v[e];
+      }
+    };
     if (fast) {
       if (Cg) {
         const int c8 = (tid % CPR) * 8, r0 = tid / CPR;
@@ -532,18 +554,16 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
           const int rr = r0 + it * RPI;
           const float* srow = S + rr * PITCH + c8;
           const f32x4 s0 = *(const f32x4*)srow, s1 = *(const f32x4*)(srow + 4);
-          u32x4 w;
-          w[0] = pack_bf2(alpha * s0[0], alpha * s0[1]);
-          w[1] = pack_bf2(alpha * s0[2], alpha * s0[3]);
-          w[2] = pack_bf2(alpha * s1[0], alpha * s1[1]);
-          w[3] = pack_bf2(alpha * s1[2], alpha * s1[3]);
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { v[e] = alpha * s0[e]; v[4 + e] = alpha * s1[e]; }
           const int tr = trow(rr);
-          uint8_t* const dst = Cg + ((int64_t)(i0 + tr) * ldc + j0 + c8) * 2;
+          uint8_t* const dst = Cg + ((int64_t)(i0 + tr) * ldc + j0 + c8) * esz;
           const int lo = tr - c8;  // columns c8 + e with e >= lo are on or above the diagonal
           if (!diag || lo <= 0) {
-            *(u32x4*)dst = w;
+            put8(dst, v, 0, 8);
           } else if (lo < 8) {
-            for (int e = lo; e < 8; ++e) ((uint16_t*)dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+            put8(dst, v, lo, 8);
           }
         }
       }
@@ -555,21 +575,16 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
           const int ti = trow(i8);
           const int hi = diag ? jj - ti : 8;
           if (hi <= 0) continue;
-          u32x4 w;
+          float v[8];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            w[e] = pack_bf2(alpha * S[(i8 + 2 * e) * PITCH + jj], alpha * S[(i8 + 2 * e + 1) * PITCH + jj]);
-          uint8_t* const dst = Tg + ((int64_t)(j0 + jj) * ldt + i0 + ti) * 2;
-          if (hi >= 8) {
-            *(u32x4*)dst = w;
-          } else {
-            for (int e = 0; e < hi; ++e) ((uint16_t*)dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-          }
+          for (int e = 0; e < 8; ++e) v[e] = alpha * S[(i8 + e) * PITCH + jj];
+          uint8_t* const dst = Tg + ((int64_t)(j0 + jj) * ldt + i0 + ti) * esz;
+          put8(dst, v, 0, hi < 8 ? hi : 8);
         }
       }
     } else {
-      // Edges, the SYRK diagonal, fp32 output, an explicit D: element-wise
-      // where needed, through v = alpha S (+ beta D) written back to S.
+      // Ragged edges or an explicit D: element-wise where needed, through
+      // v = alpha S (+ beta D) written back to S.
       const int c8 = (tid % CPR) * 8, r0 = tid / CPR;
       const int j = j0 + c8;
 #pragma unroll 1
