@@ -261,25 +261,28 @@ def side_workload(args, dev):
             x = synth.gaussian((rows, 4096), (3, 0, i, 1, synth.ROLE_GRAD), "bf16")
             xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev).view(heads, rows // heads, 4096)
             yt = torch.empty_like(xt)
-            cfg = ns.ns_config(compute_dtype="bf16")
-            ws = torch.empty(ns.ns_workspace_bytes(heads, rows // heads, 4096, cfg), dtype=torch.uint8, device=dev)
-            parts.append((xt, yt, cfg, ws, x))
+            parts.append((xt, yt, x))
+        # Both projections in one muon_ns_groups call: every Newton-Schulz
+        # launch covers the 40 heads.
+        cfg = ns.ns_config(compute_dtype="bf16")
+        probs = (ns.NSProblem * 2)(*[ns.NSProblem(xt.data_ptr(), ns.MUON_BF16, xt.stride(0), xt.stride(1),
+                                                  yt.data_ptr(), ns.MUON_BF16, yt.stride(0), yt.stride(1),
+                                                  *xt.shape) for xt, yt, _ in parts])
+        ws = torch.empty(ns.ns_groups_workspace_bytes([tuple(xt.shape) for xt, _, _ in parts], cfg),
+                         dtype=torch.uint8, device=dev)
 
         def step_fn():
-            for xt, yt, cfg, ws, _ in parts:
-                n, r, c = xt.shape
-                rc = L.muon_ns_batched(ctypes.c_void_p(xt.data_ptr()), ns.MUON_BF16, xt.stride(0), xt.stride(1),
-                                       ctypes.c_void_p(yt.data_ptr()), ns.MUON_BF16, yt.stride(0), yt.stride(1),
-                                       n, r, c, ctypes.byref(cfg), ctypes.c_void_p(ws.data_ptr()), ws.numel(), sptr())
-                if rc != 0:
-                    raise RuntimeError(f"muon_ns_batched failed: {rc} {L.muon_last_error()}")
+            rc = L.muon_ns_groups(probs, 2, ctypes.byref(cfg), ctypes.c_void_p(ws.data_ptr()), ws.numel(), sptr())
+            if rc != 0:
+                raise RuntimeError(f"muon_ns_groups failed: {rc} {L.muon_last_error()}")
         shapes = [(32, 128, 4096), (8, 128, 4096)]
         workload = "llama3-8b-q-k-per-head-ns5"
-        extra = {"heads": ["q 32x128x4096", "k 8x128x4096"], "normuon": False, "step": "Newton-Schulz only"}
+        extra = {"heads": ["q 32x128x4096", "k 8x128x4096"], "normuon": False, "step": "Newton-Schulz only",
+                 "call": "muon_ns_groups: q and k heads share every launch"}
 
         def cpu_leg():
             t0, done = time.perf_counter(), 0
-            x = synth.bf16_bits_to_f64(parts[0][4])
+            x = synth.bf16_bits_to_f64(parts[0][2])
             while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0) and done < 32:
                 oracle.newton_schulz5(x[128 * done:128 * (done + 1)])
                 done += 1

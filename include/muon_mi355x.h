@@ -39,8 +39,8 @@
  *    synchronizes: work is only enqueued on `stream` (a hipStream_t; NULL is
  *    the default stream) and the call returns after the enqueue.
  *  - Matrices are row-major with unit column stride; row and batch strides
- *    are in elements.  Matrix pointers of muon_ns_batched and
- *    normuon_normalize need only be aligned to their element size; the
+ *    are in elements.  Matrix pointers of muon_ns_batched, muon_ns_groups
+ *    and normuon_normalize need only be aligned to their element size; the
  *    per-parameter tensors of the step entry points must be 16-byte aligned
  *    (as every tensor allocation is).  Workspaces must be 256-byte aligned.
  *  - Zero-sized problems (n == 0, rows == 0 or cols == 0) are valid no-ops.
@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 3
+#define MUON_ABI_VERSION 4
 /* Layout of the caller-owned optimizer state: momentum has the parameter's
  * shape and dtype; the NorMuon variance is one fp32 value per output channel
  * ([ConvFix] "What it does"). */
@@ -150,6 +150,39 @@ int muon_ns_batched(const void* x, int32_t x_dtype, int64_t x_batch_stride, int6
                     void* y, int32_t y_dtype, int64_t y_batch_stride, int64_t y_row_stride,
                     int64_t n, int64_t rows, int64_t cols, const muon_ns_config* cfg,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* One problem of muon_ns_groups: the arguments of one muon_ns_batched call. */
+typedef struct muon_ns_problem {
+  const void* x;
+  int32_t x_dtype;
+  int64_t x_batch_stride, x_row_stride;
+  void* y;
+  int32_t y_dtype;
+  int64_t y_batch_stride, y_row_stride;
+  int64_t n, rows, cols;
+} muon_ns_problem;
+
+/* Workspace bytes muon_ns_groups needs for these nprob problems: the sum of
+ * muon_ns_workspace_bytes over them. */
+int muon_ns_groups_workspace_bytes(const muon_ns_problem* probs, int64_t nprob,
+                                   const muon_ns_config* cfg, size_t* bytes);
+
+/* muon_ns_batched on each of nprob problems (host array, read during the call
+ * only), with every Newton-Schulz launch shared by all of them: e.g. the
+ * per-head views of q_proj [32, 128, 4096] and k_proj [8, 128, 4096] of one
+ * layer ([AutoTP] option 3) in one launch per kernel instead of one per
+ * projection ([LSMuon] _run_ns: the per-matrix loop is launch-bound, so
+ * batch).  Each y[i] of each problem is bitwise what muon_ns_batched gives.
+ * With cfg->max_batch > 0 each problem is cut into chunks of at most
+ * max_batch matrices, and pass k covers chunk k of every problem.
+ * A problem's output span (first to last byte its strides reach) must not
+ * overlap another problem's input or output span.  nprob is in 0..4096.
+ * workspace: device, at least muon_ns_groups_workspace_bytes() bytes, 256-byte
+ *            aligned; its contents on entry do not matter.
+ * Errors as for muon_ns_batched, checked for every problem before anything
+ * is enqueued; MUON_ERR_INVALID_ARG also for overlapping problems. */
+int muon_ns_groups(const muon_ns_problem* probs, int64_t nprob, const muon_ns_config* cfg,
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- NorMuon normalization --------------------------------------------- */
 

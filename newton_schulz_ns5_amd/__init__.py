@@ -11,6 +11,9 @@ Entry points (same names as the C ABI):
 * ``ns_batched(x, out=None, ...)`` -- NS5 of each matrix of a [n, rows, cols]
   (or [rows, cols]) tensor, any batch / row strides (megabatch slices, per-head
   views from ``per_head_view``);
+* ``ns_groups(xs, outs=None, ...)`` -- ``ns_batched`` on several tensors with
+  every Newton-Schulz launch shared by all of them (e.g. the per-head views of
+  q_proj and k_proj of one layer);
 * ``normuon_normalize(o, v, beta2, eps)`` -- NorMuon on [n, rows, cols];
 * ``step_group(...)`` -- one Muon / NorMuon step of same-shape parameters;
 * ``MuonNS5`` -- a small optimizer that groups parameters by flattened shape
@@ -21,9 +24,9 @@ import math
 from collections import OrderedDict
 
 from . import _lib
-from ._lib import MUON_BF16, MUON_F32, MuonError, NSConfig, Group, HParams, KERNEL_CLASSES
+from ._lib import MUON_BF16, MUON_F32, MuonError, NSConfig, NSProblem, Group, HParams, KERNEL_CLASSES
 
-__all__ = ["ns_batched", "normuon_normalize", "step_group", "step_groups", "step_groups_workspace_bytes", "MuonNS5", "per_head_view", "ns_config",
+__all__ = ["ns_batched", "ns_groups", "ns_groups_workspace_bytes", "normuon_normalize", "step_group", "step_groups", "step_groups_workspace_bytes", "MuonNS5", "per_head_view", "ns_config",
            "hparams", "ns_workspace_bytes", "step_workspace_bytes", "normuon_workspace_bytes",
            "profile_enable", "profile_reset", "profile_query", "MuonError", "QUINTIC", "abi_version",
            "state_layout_version", "lib"]
@@ -175,6 +178,51 @@ def ns_batched(x, out=None, *, steps=5, coeffs=QUINTIC, eps=1e-7, compute_dtype=
         _ptr(y3), _dt(y3), y3.stride(0), y3.stride(1),
         n, rows, cols, ctypes.byref(cfg), _ptr(ws), ws.numel(), _stream(x)))
     return out
+
+
+def _ns_problems(xs, outs):
+    if len(xs) != len(outs):
+        raise MuonError(_lib.MUON_ERR_INVALID_ARG, f"{len(xs)} inputs but {len(outs)} outputs")
+    probs = (NSProblem * max(len(xs), 1))()
+    for i, (x, y) in enumerate(zip(xs, outs)):
+        x3, y3 = _as3(x), _as3(y)
+        if x3.shape != y3.shape:
+            raise MuonError(_lib.MUON_ERR_INVALID_ARG, f"problem {i}: out shape {tuple(y.shape)} != x shape {tuple(x.shape)}")
+        if x3.numel() and (x3.stride(2) != 1 or y3.stride(2) != 1):
+            raise MuonError(_lib.MUON_ERR_INVALID_ARG, f"problem {i}: x and out need unit column stride")
+        n, rows, cols = x3.shape
+        probs[i] = NSProblem(_ptr(x3), _dt(x3), x3.stride(0), x3.stride(1),
+                             _ptr(y3), _dt(y3), y3.stride(0), y3.stride(1), n, rows, cols)
+    return probs
+
+
+def ns_groups_workspace_bytes(shapes, cfg):
+    """Workspace of ns_groups for problems of these (n, rows, cols) shapes."""
+    probs = (NSProblem * max(len(shapes), 1))()
+    for i, (n, rows, cols) in enumerate(shapes):
+        probs[i] = NSProblem(None, MUON_BF16, 0, cols, None, MUON_BF16, 0, cols, n, rows, cols)
+    out = ctypes.c_size_t(0)
+    _lib.check(lib().muon_ns_groups_workspace_bytes(probs, len(shapes), ctypes.byref(cfg), ctypes.byref(out)))
+    return out.value
+
+
+def ns_groups(xs, outs=None, *, steps=5, coeffs=QUINTIC, eps=1e-7, compute_dtype="bf16", max_batch=0,
+              cfg=None, workspace=None):
+    """ns_batched on each tensor of ``xs`` (each [rows, cols] or [n, rows, cols], unit
+    column stride), one call and one set of Newton-Schulz launches for all of them."""
+    torch = _torch()
+    cfg = cfg if cfg is not None else ns_config(steps, coeffs, eps, compute_dtype, max_batch)
+    xs = list(xs)
+    if outs is None:
+        outs = [torch.empty_like(x, memory_format=torch.contiguous_format) for x in xs]
+    outs = list(outs)
+    if not xs:
+        return outs
+    probs = _ns_problems(xs, outs)
+    need = ns_groups_workspace_bytes([tuple(_as3(x).shape) for x in xs], cfg)
+    ws = workspace if workspace is not None else _workspace(xs[0].device, need)
+    _lib.check(lib().muon_ns_groups(probs, len(xs), ctypes.byref(cfg), _ptr(ws), ws.numel(), _stream(xs[0])))
+    return outs
 
 
 def normuon_normalize(o, v, beta2=0.95, eps=1e-8, workspace=None):

@@ -36,6 +36,12 @@ class NSConfig(ctypes.Structure):
                 ("coeffs", (c_f32 * 3) * NS_MAX_STEPS)]
 
 
+class NSProblem(ctypes.Structure):
+    _fields_ = [("x", c_vp), ("x_dtype", c_i32), ("x_batch_stride", c_i64), ("x_row_stride", c_i64),
+                ("y", c_vp), ("y_dtype", c_i32), ("y_batch_stride", c_i64), ("y_row_stride", c_i64),
+                ("n", c_i64), ("rows", c_i64), ("cols", c_i64)]
+
+
 class Group(ctypes.Structure):
     _fields_ = [("n", c_i64), ("rows", c_i64), ("cols", c_i64), ("heads", c_i64),
                 ("grad_dtype", c_i32), ("mom_dtype", c_i32), ("model_dtype", c_i32), ("reserved", c_i32),
@@ -60,6 +66,9 @@ SIGNATURES = {
     "muon_ns_workspace_bytes": (c_i32, [c_i64, c_i64, c_i64, ctypes.POINTER(NSConfig), ctypes.POINTER(c_sz)]),
     "muon_ns_batched": (c_i32, [c_vp, c_i32, c_i64, c_i64, c_vp, c_i32, c_i64, c_i64, c_i64, c_i64, c_i64,
                                 ctypes.POINTER(NSConfig), c_vp, c_sz, c_vp]),
+    "muon_ns_groups_workspace_bytes": (c_i32, [ctypes.POINTER(NSProblem), c_i64, ctypes.POINTER(NSConfig),
+                                               ctypes.POINTER(c_sz)]),
+    "muon_ns_groups": (c_i32, [ctypes.POINTER(NSProblem), c_i64, ctypes.POINTER(NSConfig), c_vp, c_sz, c_vp]),
     "normuon_workspace_bytes": (c_i32, [c_i64, c_i64, c_i64, ctypes.POINTER(c_sz)]),
     "normuon_normalize": (c_i32, [c_vp, c_i32, c_i64, c_i64, c_i64, c_i64, c_i64, c_vp, c_i64, c_f32, c_f32,
                                   c_vp, c_sz, c_vp]),

@@ -478,6 +478,126 @@ int64_t chunk_of(int64_t n, int64_t max_batch) {
   return c < 65535 ? c : 65535;
 }
 
+
+bool ns_empty(const muon_ns_problem& q) { return q.n == 0 || q.rows == 0 || q.cols == 0; }
+
+// The argument checks of one Newton-Schulz problem (the config is checked by
+// the caller); an empty problem passes once its sizes and dtypes do.
+int check_ns_problem(const muon_ns_problem& q) {
+  int rc = check_dims(q.n, q.rows, q.cols);
+  if (rc) return rc;
+  if (!dtype_ok(q.x_dtype) || !dtype_ok(q.y_dtype)) return fail(MUON_ERR_UNSUPPORTED, "x/y dtype must be MUON_F32 or MUON_BF16");
+  if (ns_empty(q)) return MUON_OK;
+  if (!q.x || !q.y) return fail(MUON_ERR_INVALID_ARG, "x or y is NULL");
+  if (q.x_row_stride < q.cols || q.y_row_stride < q.cols) return fail(MUON_ERR_INVALID_ARG, "row stride smaller than cols");
+  if (q.x_batch_stride < 0 || q.y_batch_stride < 0) return fail(MUON_ERR_INVALID_ARG, "negative batch stride");
+  if (q.n > 1 && q.y_batch_stride < (q.rows - 1) * q.y_row_stride + q.cols)
+    return fail(MUON_ERR_INVALID_ARG, "output batches overlap");
+  if (((uintptr_t)q.x % esize(q.x_dtype)) || ((uintptr_t)q.y % esize(q.y_dtype)))
+    return fail(MUON_ERR_INVALID_ARG, "x/y not aligned to their element size");
+  // In place needs equal layouts, so that the final store of a matrix only
+  // overwrites that matrix's own (already read) input.
+  if (q.y == q.x && (q.x_dtype != q.y_dtype || q.x_batch_stride != q.y_batch_stride || q.x_row_stride != q.y_row_stride))
+    return fail(MUON_ERR_INVALID_ARG, "in-place call needs identical dtype and strides");
+  return MUON_OK;
+}
+
+// Workspace bytes of one problem: its region holds one pass of at most
+// max_batch matrices.
+size_t ns_region_bytes(const muon_ns_problem& q, const muon_ns_config& cfg) {
+  if (ns_empty(q)) return 0;
+  return make_layout(make_geom(q.rows, q.cols, cfg.compute_dtype), chunk_of(q.n, cfg.max_batch)).total;
+}
+
+int check_workspace(const void* ws, size_t have, size_t need) {
+  if (!ws) return fail(MUON_ERR_INVALID_ARG, "workspace is NULL");
+  if ((uintptr_t)ws & 255) return fail(MUON_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (have < need) return fail(MUON_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, have);
+  return MUON_OK;
+}
+
+// Byte span [lo, hi) reached by a strided batch of matrices.
+struct Span { uintptr_t lo, hi; };
+Span span_of(const void* p, int32_t dt, int64_t bs, int64_t rs, int64_t n, int64_t rows, int64_t cols) {
+  const uintptr_t lo = (uintptr_t)p;
+  return {lo, lo + (uintptr_t)(((n - 1) * bs + (rows - 1) * rs + cols) * (int64_t)esize(dt))};
+}
+
+// No problem's output span meets another problem's input or output span.
+int check_disjoint(const muon_ns_problem* q, int64_t nq) {
+  auto meet = [](Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; };
+  for (int64_t i = 0; i < nq; ++i) {
+    if (ns_empty(q[i])) continue;
+    const Span yi = span_of(q[i].y, q[i].y_dtype, q[i].y_batch_stride, q[i].y_row_stride, q[i].n, q[i].rows, q[i].cols);
+    for (int64_t j = 0; j < nq; ++j) {
+      if (j == i || ns_empty(q[j])) continue;
+      const Span xj = span_of(q[j].x, q[j].x_dtype, q[j].x_batch_stride, q[j].x_row_stride, q[j].n, q[j].rows, q[j].cols);
+      const Span yj = span_of(q[j].y, q[j].y_dtype, q[j].y_batch_stride, q[j].y_row_stride, q[j].n, q[j].rows, q[j].cols);
+      if (meet(yi, xj) || meet(yi, yj))
+        return fail(MUON_ERR_INVALID_ARG, "output of problem %lld overlaps problem %lld", (long long)i, (long long)j);
+    }
+  }
+  return MUON_OK;
+}
+
+// Newton-Schulz of every (checked, non-empty or empty) problem.  Problem i
+// owns a region of ns_region_bytes at the running offset in ws and is cut
+// into passes of chunk_of(n_i, max_batch) matrices; pass k loads and
+// normalizes chunk k of every problem that has one, and one set of
+// iteration launches then covers them all.
+hipError_t ns_run_passes(const muon_ns_problem* q, int64_t nq, const muon_ns_config& cfg, char* ws, hipStream_t s) {
+  struct Live { const muon_ns_problem* q; Geom g; int64_t chunk; Layout L; char* ws; };
+  std::vector<Live> live;
+  size_t off = 0;
+  int64_t passes = 0;
+  for (int64_t i = 0; i < nq; ++i) {
+    if (ns_empty(q[i])) continue;
+    Live v{&q[i], make_geom(q[i].rows, q[i].cols, cfg.compute_dtype), chunk_of(q[i].n, cfg.max_batch), {}, nullptr};
+    v.L = make_layout(v.g, v.chunk);
+    v.ws = ws + off;
+    off += v.L.total;
+    passes = std::max(passes, (q[i].n + v.chunk - 1) / v.chunk);
+    live.push_back(v);
+  }
+  for (int64_t k = 0; k < passes; ++k) {
+    std::vector<NsJob> jobs;
+    for (const Live& v : live) {
+      const muon_ns_problem& p = *v.q;
+      const int64_t c0 = k * v.chunk;
+      if (c0 >= p.n) continue;
+      const int64_t nb = std::min(v.chunk, p.n - c0);
+      const size_t xe = esize(p.x_dtype), ye = esize(p.y_dtype);
+      PrepParams pp{};
+      pp.mode = 0;
+      pp.tall = v.g.tall;
+      pp.rows = (int)p.rows; pp.cols = (int)p.cols;
+      pp.mp = (int)v.g.mp; pp.np = (int)v.g.np;
+      pp.heads = 1;
+      pp.src_dtype = p.x_dtype;
+      pp.x_bf16 = v.g.bf;
+      pp.x = (const char*)p.x + c0 * p.x_batch_stride * xe;
+      pp.x_bs = p.x_batch_stride; pp.x_rs = p.x_row_stride;
+      pp.X = v.ws + v.L.X0; pp.X_bs = v.g.mp * v.g.np;
+      pp.partial = (float*)(v.ws + v.L.partial);
+      hipError_t e = run(MUON_K_PREP, 0, (double)nb * p.rows * p.cols * (xe + (v.g.bf ? 2 : 4)), s,
+                         [&]() { return launch_prep(pp, (int)nb, s); });
+      if (e != hipSuccess) return e;
+      if ((e = norm_finalize(v.g, nb, cfg.eps, v.ws, v.L, s)) != hipSuccess) return e;
+      FinalOut out{(char*)p.y + c0 * p.y_batch_stride * ye, p.y_dtype, p.y_row_stride, p.y_batch_stride};
+      jobs.push_back(NsJob{v.g, nb, v.ws, v.L, out});
+    }
+    hipError_t e = ns_iterations(jobs, cfg, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+int ns_run(const muon_ns_problem* q, int64_t nq, const muon_ns_config& cfg, char* ws, hipStream_t s) {
+  hipError_t e = ns_run_passes(q, nq, cfg, ws, s);
+  if (e != hipSuccess) return hip_fail(e, "Newton-Schulz kernels");
+  return ok();
+}
+
 }  // namespace
 
 // =============================================================================
@@ -545,54 +665,48 @@ int muon_ns_batched(const void* x, int32_t x_dtype, int64_t x_batch_stride, int6
                     void* y, int32_t y_dtype, int64_t y_batch_stride, int64_t y_row_stride,
                     int64_t n, int64_t rows, int64_t cols, const muon_ns_config* cfg,
                     void* workspace, size_t workspace_bytes, void* stream) {
+  const muon_ns_problem q{x, x_dtype, x_batch_stride, x_row_stride, y, y_dtype, y_batch_stride, y_row_stride,
+                          n, rows, cols};
   int rc = check_cfg(cfg);
   if (rc) return rc;
-  if ((rc = check_dims(n, rows, cols))) return rc;
-  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return fail(MUON_ERR_UNSUPPORTED, "x/y dtype must be MUON_F32 or MUON_BF16");
-  if (n == 0 || rows == 0 || cols == 0) return ok();
-  if (!x || !y) return fail(MUON_ERR_INVALID_ARG, "x or y is NULL");
-  if (x_row_stride < cols || y_row_stride < cols) return fail(MUON_ERR_INVALID_ARG, "row stride smaller than cols");
-  if (x_batch_stride < 0 || y_batch_stride < 0) return fail(MUON_ERR_INVALID_ARG, "negative batch stride");
-  if (n > 1 && y_batch_stride < (rows - 1) * y_row_stride + cols) return fail(MUON_ERR_INVALID_ARG, "output batches overlap");
-  if (((uintptr_t)x % esize(x_dtype)) || ((uintptr_t)y % esize(y_dtype))) return fail(MUON_ERR_INVALID_ARG, "x/y not aligned to their element size");
-  if (y != x) {
-    // Partial overlap of input and output would let the final store clobber unread input
-    // of another batch entry only if they share memory; in-place with equal strides is allowed.
-  } else if (x_dtype != y_dtype || x_batch_stride != y_batch_stride || x_row_stride != y_row_stride) {
-    return fail(MUON_ERR_INVALID_ARG, "in-place call needs identical dtype and strides");
-  }
-  const Geom g = make_geom(rows, cols, cfg->compute_dtype);
-  const int64_t chunk = chunk_of(n, cfg->max_batch);
-  const Layout L = make_layout(g, chunk);
-  if (!workspace) return fail(MUON_ERR_INVALID_ARG, "workspace is NULL");
-  if ((uintptr_t)workspace & 255) return fail(MUON_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  if (workspace_bytes < L.total) return fail(MUON_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", L.total, workspace_bytes);
+  if ((rc = check_ns_problem(q))) return rc;
+  if (ns_empty(q)) return ok();
+  const size_t need = make_layout(make_geom(rows, cols, cfg->compute_dtype), chunk_of(n, cfg->max_batch)).total;
+  if ((rc = check_workspace(workspace, workspace_bytes, need))) return rc;
+  return ns_run(&q, 1, *cfg, (char*)workspace, (hipStream_t)stream);
+}
 
-  hipStream_t s = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  const size_t xe = esize(x_dtype), ye = esize(y_dtype);
-  for (int64_t c0 = 0; c0 < n; c0 += chunk) {
-    const int64_t nb = (n - c0) < chunk ? (n - c0) : chunk;
-    PrepParams pp{};
-    pp.mode = 0;
-    pp.tall = g.tall;
-    pp.rows = (int)rows; pp.cols = (int)cols;
-    pp.mp = (int)g.mp; pp.np = (int)g.np;
-    pp.heads = 1;
-    pp.src_dtype = x_dtype;
-    pp.x_bf16 = g.bf;
-    pp.x = (const char*)x + c0 * x_batch_stride * xe;
-    pp.x_bs = x_batch_stride; pp.x_rs = x_row_stride;
-    pp.X = ws + L.X0; pp.X_bs = g.mp * g.np;
-    pp.partial = (float*)(ws + L.partial);
-    hipError_t e = run(MUON_K_PREP, 0, (double)nb * rows * cols * (xe + (g.bf ? 2 : 4)), s,
-                       [&]() { return launch_prep(pp, (int)nb, s); });
-    if (e != hipSuccess) return hip_fail(e, "load kernel");
-    if ((e = norm_finalize(g, nb, cfg->eps, ws, L, s)) != hipSuccess) return hip_fail(e, "norm kernel");
-    FinalOut out{(char*)y + c0 * y_batch_stride * ye, y_dtype, y_row_stride, y_batch_stride};
-    if ((e = ns_iterations({NsJob{g, nb, ws, L, out}}, *cfg, s)) != hipSuccess) return hip_fail(e, "Newton-Schulz kernels");
+int muon_ns_groups_workspace_bytes(const muon_ns_problem* probs, int64_t nprob, const muon_ns_config* cfg,
+                                   size_t* bytes) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!bytes) return fail(MUON_ERR_INVALID_ARG, "bytes is NULL");
+  if (nprob < 0 || nprob > 4096) return fail(MUON_ERR_INVALID_ARG, "nprob must be in 0..4096");
+  if (nprob > 0 && !probs) return fail(MUON_ERR_INVALID_ARG, "probs is NULL");
+  size_t total = 0;
+  for (int64_t i = 0; i < nprob; ++i) {
+    if ((rc = check_dims(probs[i].n, probs[i].rows, probs[i].cols))) return rc;
+    total += ns_region_bytes(probs[i], *cfg);
   }
+  *bytes = total;
   return ok();
+}
+
+int muon_ns_groups(const muon_ns_problem* probs, int64_t nprob, const muon_ns_config* cfg,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (nprob < 0 || nprob > 4096) return fail(MUON_ERR_INVALID_ARG, "nprob must be in 0..4096");
+  if (nprob > 0 && !probs) return fail(MUON_ERR_INVALID_ARG, "probs is NULL");
+  size_t need = 0;
+  for (int64_t i = 0; i < nprob; ++i) {
+    if ((rc = check_ns_problem(probs[i]))) return fail(rc, "problem %lld: %s", (long long)i, g_err.c_str());
+    need += ns_region_bytes(probs[i], *cfg);
+  }
+  if ((rc = check_disjoint(probs, nprob))) return rc;
+  if (need == 0) return ok();
+  if ((rc = check_workspace(workspace, workspace_bytes, need))) return rc;
+  return ns_run(probs, nprob, *cfg, (char*)workspace, (hipStream_t)stream);
 }
 
 int normuon_workspace_bytes(int64_t n, int64_t rows, int64_t cols, size_t* bytes) {

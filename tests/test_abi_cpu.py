@@ -25,7 +25,7 @@ def header_functions():
 
 def test_header_declares_the_expected_entry_points():
     names = header_functions()
-    for required in ["muon_ns_batched", "muon_step_group", "normuon_normalize", "muon_ns_workspace_bytes",
+    for required in ["muon_ns_batched", "muon_ns_groups", "muon_step_group", "normuon_normalize", "muon_ns_workspace_bytes",
                      "muon_step_workspace_bytes", "normuon_workspace_bytes", "muon_last_error"]:
         assert required in names
 
@@ -47,6 +47,11 @@ int main(void) {
   printf("muon_ns_config %zu\n", sizeof(muon_ns_config));
   printf("muon_group %zu\n", sizeof(muon_group));
   printf("muon_hparams %zu\n", sizeof(muon_hparams));
+  printf("muon_ns_problem %zu\n", sizeof(muon_ns_problem));
+  F(muon_ns_problem, x); F(muon_ns_problem, x_dtype); F(muon_ns_problem, x_batch_stride);
+  F(muon_ns_problem, x_row_stride); F(muon_ns_problem, y); F(muon_ns_problem, y_dtype);
+  F(muon_ns_problem, y_batch_stride); F(muon_ns_problem, y_row_stride); F(muon_ns_problem, n);
+  F(muon_ns_problem, rows); F(muon_ns_problem, cols);
   F(muon_ns_config, steps); F(muon_ns_config, a); F(muon_ns_config, b); F(muon_ns_config, c);
   F(muon_ns_config, eps); F(muon_ns_config, compute_dtype); F(muon_ns_config, schedule); F(muon_ns_config, max_batch);
   F(muon_ns_config, coeffs);
@@ -71,7 +76,8 @@ int main(void) {
 
 def test_ctypes_structs_match_c_layout():
     lay = _c_layout()
-    for cname, py in [("muon_ns_config", m.NSConfig), ("muon_group", m.Group), ("muon_hparams", m.HParams)]:
+    for cname, py in [("muon_ns_config", m.NSConfig), ("muon_group", m.Group), ("muon_hparams", m.HParams),
+                      ("muon_ns_problem", m.NSProblem)]:
         assert ctypes.sizeof(py) == lay[cname], cname
         for fname, _ in py._fields_:
             assert getattr(py, fname).offset == lay[f"{cname}.{fname}"], (cname, fname)
@@ -88,7 +94,7 @@ def test_one_hip_runtime_per_process():
 
 def test_versions_and_status_strings():
     L = m.lib()
-    assert L.muon_abi_version() == 3 and L.muon_state_layout_version() == 1
+    assert L.muon_abi_version() == 4 and L.muon_state_layout_version() == 1
     for code, word in [(0, b"ok"), (-1, b"invalid"), (-2, b"unsupported"), (-3, b"workspace"), (-4, b"HIP")]:
         assert word in L.muon_status_string(code)
     assert L.muon_kernel_class_name(4) == b"update"
@@ -181,6 +187,68 @@ def test_ns_workspace_query():
     f = m.ns_workspace_bytes(1, 256, 256, m.ns_config(compute_dtype="f32"))
     h = m.ns_workspace_bytes(1, 256, 256, c)
     assert f > h
+
+
+def ns_problem(**over):
+    a = dict(x=FAKE, xd=1, xbs=64 * 64, xrs=64, y=FAKE, yd=1, ybs=64 * 64, yrs=64, n=1, rows=64, cols=64)
+    a.update(over)
+    return m.NSProblem(a["x"], a["xd"], a["xbs"], a["xrs"], a["y"], a["yd"], a["ybs"], a["yrs"],
+                       a["n"], a["rows"], a["cols"])
+
+
+def groups_call(probs, cfg=None, ws=FAKE, wsb=1 << 40, nprob=None):
+    arr = (m.NSProblem * max(len(probs), 1))(*probs)
+    cfg = cfg or m.ns_config()
+    n = len(probs) if nprob is None else nprob
+    return m.lib().muon_ns_groups(arr if probs else None, n, ctypes.byref(cfg), ctypes.c_void_p(ws), wsb, None)
+
+
+def test_ns_groups_workspace_is_the_sum_of_the_problems():
+    c = m.ns_config()
+    shapes = [(32, 128, 4096), (8, 128, 4096), (3, 300, 520), (0, 64, 64), (2, 520, 300)]
+    assert m.ns_groups_workspace_bytes(shapes, c) == sum(m.ns_workspace_bytes(*s, c) for s in shapes)
+    c3 = m.ns_config(max_batch=3)
+    assert m.ns_groups_workspace_bytes(shapes, c3) == sum(m.ns_workspace_bytes(*s, c3) for s in shapes)
+    assert m.ns_groups_workspace_bytes([], c) == 0
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(x=0), -1), (dict(y=0), -1), (dict(xrs=10), -1), (dict(xd=7), -2), (dict(n=2, ybs=10), -1),
+    (dict(rows=1 << 25), -1), (dict(x=FAKE + 1), -1), (dict(n=-1), -1),
+])
+def test_ns_groups_reports_the_failing_problem(bad, code):
+    base = 1 << 30
+    good = ns_problem(x=base, y=base)
+    assert groups_call([good, ns_problem(**bad)]) == code
+    assert b"problem 1" in m.lib().muon_last_error()
+
+
+def test_ns_groups_argument_errors():
+    base = 1 << 30
+    p0 = ns_problem(x=base, y=base + (1 << 20))
+    p1 = ns_problem(x=base + (2 << 20), y=base + (3 << 20))
+    assert groups_call([p0, p1], ws=0) == -1
+    assert groups_call([p0, p1], ws=FAKE + 16) == -1
+    assert groups_call([p0, p1], wsb=100) == -3
+    assert groups_call([p0, p1], nprob=-1) == -1
+    assert groups_call([p0, p1], nprob=4097) == -1
+    assert groups_call([], nprob=2) == -1                      # NULL array
+    c = m.ns_config()
+    c.steps = 0
+    assert groups_call([p0, p1], cfg=c) == -1
+    # outputs may not meet another problem's input or output
+    assert groups_call([p0, ns_problem(x=base + (1 << 20) + 4096, y=base + (3 << 20))]) == -1
+    assert b"overlaps" in m.lib().muon_last_error()
+    assert groups_call([p0, ns_problem(x=base + (2 << 20), y=base + (1 << 20) + 64)]) == -1
+    # in place within one problem is fine; so is sharing an input between problems
+    same_in = ns_problem(x=base, y=base + (4 << 20))
+    assert groups_call([p0, same_in], wsb=100) == -3           # gets past the overlap check
+    assert groups_call([ns_problem(x=base, y=base), p1], wsb=100) == -3
+
+
+def test_ns_groups_empty_is_noop():
+    assert groups_call([]) == 0
+    assert groups_call([ns_problem(n=0, x=0, y=0), ns_problem(rows=0)], ws=0, wsb=0) == 0
 
 
 def group_call(hp=None, **over):

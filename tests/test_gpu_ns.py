@@ -293,3 +293,46 @@ def test_split_k_gram_batch_invariant():
     one = ns.ns_batched(x[2:3].clone())
     torch.cuda.synchronize()
     assert torch.equal(full[2], one[0])
+
+
+# muon_ns_groups: several tensors in one call, every Newton-Schulz launch
+# shared by all of them; each output bitwise equal to its own muon_ns_batched
+# call, and the per-head q/k case against the oracle.
+def test_ns_groups_per_head_q_k_bitwise_and_parity():
+    torch = torch_cuda()
+    qx = synth.gaussian((4096, 4096), (3, 0, 0, 1, 0), "bf16")
+    kx = synth.gaussian((1024, 4096), (3, 0, 1, 1, 0), "bf16")
+    qh = ns.per_head_view(to_dev(qx, "bf16"), 32)
+    kh = ns.per_head_view(to_dev(kx, "bf16"), 8)
+    gq, gk = ns.ns_groups([qh, kh])
+    sq, sk = ns.ns_batched(qh), ns.ns_batched(kh)
+    torch.cuda.synchronize()
+    assert torch.equal(gq, sq) and torch.equal(gk, sk)
+    qin, kin = synth.bf16_bits_to_f64(qx), synth.bf16_bits_to_f64(kx)
+    gq64, gk64 = to_f64(gq), to_f64(gk)
+    for h in (0, 31):
+        assert rel_fro(gq64[h], oracle.newton_schulz5(qin[h * 128:(h + 1) * 128])) <= TOL["bf16"]
+    for h in (0, 7):
+        assert rel_fro(gk64[h], oracle.newton_schulz5(kin[h * 128:(h + 1) * 128])) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("compute", ["bf16", "f32"])
+def test_ns_groups_mixed_shapes_bitwise(compute):
+    # wide, tall, ragged, a split-K Gram shape, a 2-D tensor, an empty one and
+    # an fp32 input with a bf16 output, in one call and with max_batch = 2.
+    torch = torch_cuda()
+    dt = "bf16" if compute == "bf16" else "f32"
+    shapes = [(3, 300, 520), (2, 520, 300), (2, 8, 36), (3, 128, 2048), (0, 64, 64)]
+    xs = [to_dev(synth.gaussian(s, (31, i, 0, 1, 0), dt), dt) if s[0] else
+          torch.empty(s, dtype=torch.bfloat16, device="cuda") for i, s in enumerate(shapes)]
+    x2d = to_dev(synth.gaussian((200, 330), (31, 9, 0, 1, 0), "f32"), "f32")
+    xs.append(x2d)
+    outs = [torch.empty_like(x) for x in xs[:-1]] + [torch.empty((200, 330), dtype=torch.bfloat16, device="cuda")]
+    ns.ns_groups(xs, outs, compute_dtype=compute)
+    chunked = ns.ns_groups(xs, [torch.empty_like(o) for o in outs], compute_dtype=compute, max_batch=2)
+    alone = [ns.ns_batched(x, torch.empty_like(o), compute_dtype=compute) for x, o in zip(xs, outs)]
+    torch.cuda.synchronize()
+    for o, c, a in zip(outs, chunked, alone):
+        assert torch.equal(o, a) and torch.equal(c, a)
+    xin = storage_f64(synth.gaussian(shapes[0], (31, 0, 0, 1, 0), dt), dt)
+    assert rel_fro(to_f64(outs[0])[1], oracle.newton_schulz5(xin[1])) <= TOL[compute]
