@@ -231,7 +231,7 @@ hipError_t launch_phase(std::vector<GemmParams>& probs, bool syrk, bool nn, int 
   for (int tile : {256, 128}) {
     std::vector<GemmParams*> sel;
     for (auto& p : probs)
-      if (bf16_tile_for(p.M, p.N) == tile) sel.push_back(&p);
+      if (bf16_tile_for(p.M, p.N, syrk) == tile) sel.push_back(&p);
     // K per workgroup: a split-K problem's chunks are about K / ksplit long.
     auto kwg = [](const GemmParams* x) { return x->ksplit > 1 ? x->K / x->ksplit : x->K; };
     std::stable_sort(sel.begin(), sel.end(), [&](const GemmParams* x, const GemmParams* y) { return kwg(x) > kwg(y); });
@@ -378,9 +378,18 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
     for (const Sum& u : sums)
       if ((e = run(MUON_K_GRAM, 0, u.bytes, s, [&]() { return launch_split_sum(u.p, u.nb, s); })) != hipSuccess)
         return e;
-    for (const Fused& u : fused)
-      if ((e = run(MUON_K_POLY, u.flop, u.bytes, s, [&]() { return launch_poly128(u.p, u.nb, s); })) != hipSuccess)
-        return e;
+    for (size_t i0 = 0; i0 < fused.size(); i0 += kMaxPoly128) {
+      Poly128Group pg{};
+      double flop = 0, bytes = 0;
+      for (size_t i = i0; i < fused.size() && i < i0 + kMaxPoly128; ++i) {
+        pg.prob[pg.nprob] = fused[i].p;
+        pg.start[pg.nprob + 1] = pg.start[pg.nprob] + fused[i].nb;
+        ++pg.nprob;
+        flop += fused[i].flop;
+        bytes += fused[i].bytes;
+      }
+      if ((e = run(MUON_K_POLY, flop, bytes, s, [&]() { return launch_poly128(pg, s); })) != hipSuccess) return e;
+    }
     if ((e = launch_phase(poly, true, false, MUON_K_POLY, s)) != hipSuccess) return e;
     if ((e = launch_phase(upd, false, true, MUON_K_UPDATE, s)) != hipSuccess) return e;
     for (auto& c : cur) c ^= 1;

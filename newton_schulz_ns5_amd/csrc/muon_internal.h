@@ -135,12 +135,25 @@ hipError_t launch_gemm_f32(const GemmParams& p, bool nn, bool syrk, hipStream_t 
 hipError_t launch_prep(const PrepParams& p, int nb, hipStream_t s);
 hipError_t launch_norm(const NormParams& p, int nb, hipStream_t s);
 hipError_t launch_split_sum(const SplitSumParams& p, int nb, hipStream_t s);
-hipError_t launch_poly128(const Poly128Params& p, int nb, hipStream_t s);
+// Up to kMaxPoly128 such problems in one launch; problem i owns workgroups
+// start[i] .. start[i + 1] - 1, one per matrix.
+constexpr int kMaxPoly128 = 8;
+struct Poly128Group {
+  Poly128Params prob[kMaxPoly128];
+  int32_t start[kMaxPoly128 + 1];
+  int32_t nprob;
+};
+hipError_t launch_poly128(const Poly128Group& g, hipStream_t s);
 hipError_t launch_rowstat(const RowStatParams& p, int nb, hipStream_t s);
 hipError_t launch_rho(const RhoParams& p, int nb, hipStream_t s);
 hipError_t launch_apply(const ApplyParams& p, int nb, hipStream_t s);
 
 // Tile edge the bf16 GEMM uses for an M x N output (depends on shape only).
-inline int bf16_tile_for(int M, int N) { return (M % 256 == 0 && N % 256 == 0) ? 256 : 128; }
+// A symmetric product of at most 512 rows has at most 3 upper-triangle tiles
+// of 256 against 10 of 128: those fill the chip better over its K loop.
+inline int bf16_tile_for(int M, int N, bool syrk) {
+  if (syrk && M <= 512) return 128;
+  return (M % 256 == 0 && N % 256 == 0) ? 256 : 128;
+}
 
 }  // namespace muon
