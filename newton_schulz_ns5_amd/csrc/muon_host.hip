@@ -75,12 +75,14 @@ Geom make_geom(int64_t rows, int64_t cols, int32_t compute) {
 
 // K chunks of the Gram A = X X^T of a bf16 geometry (1: no split).  A matrix
 // with m <= 256 has one to three Gram tiles, too few workgroups to fill the
-// chip over a long K = n; its Gram is then computed in chunks of about 4 m
-// columns (at most 16), whose fp32 products are summed afterwards.  The count
-// depends on the shape only, so a matrix's result does not depend on its batch.
+// chip over a long K = n; its Gram is then computed in chunks of about
+// max(4 m, 1024) columns (at most 16), whose fp32 products are summed
+// afterwards (shorter chunks would move more partial products than they save
+// in latency).  The count depends on the shape only, so a matrix's result
+// does not depend on its batch.
 int gram_ksplit(const Geom& g) {
   if (!g.bf || g.mp > 256) return 1;
-  const int64_t s = g.np / (4 * g.mp);
+  const int64_t s = g.np / std::max<int64_t>(4 * g.mp, 1024);
   return s < 2 ? 1 : (s > kMaxKsplit ? kMaxKsplit : (int)s);
 }
 
@@ -231,7 +233,7 @@ hipError_t launch_phase(std::vector<GemmParams>& probs, bool syrk, bool nn, int 
   for (int tile : {256, 128}) {
     std::vector<GemmParams*> sel;
     for (auto& p : probs)
-      if (bf16_tile_for(p.M, p.N, syrk) == tile) sel.push_back(&p);
+      if (bf16_tile_for(p.M, p.N) == tile) sel.push_back(&p);
     // K per workgroup: a split-K problem's chunks are about K / ksplit long.
     auto kwg = [](const GemmParams* x) { return x->ksplit > 1 ? x->K / x->ksplit : x->K; };
     std::stable_sort(sel.begin(), sel.end(), [&](const GemmParams* x, const GemmParams* y) { return kwg(x) > kwg(y); });

@@ -149,10 +149,11 @@ hipError_t launch_rho(const RhoParams& p, int nb, hipStream_t s);
 hipError_t launch_apply(const ApplyParams& p, int nb, hipStream_t s);
 
 // Tile edge the bf16 GEMM uses for an M x N output (depends on shape only).
-// A symmetric product of at most 512 rows has at most 3 upper-triangle tiles
-// of 256 against 10 of 128: those fill the chip better over its K loop.
-inline int bf16_tile_for(int M, int N, bool syrk) {
-  if (syrk && M <= 512) return 128;
+// An output of at most 512 rows has at most 2 tile rows of 256 (a symmetric
+// one at most 3 upper-triangle tiles, against 10 of 128): such problems
+// are short-K or few-tile, and 128-edge tiles fill the chip better.
+inline int bf16_tile_for(int M, int N) {
+  if (M <= 512) return 128;
   return (M % 256 == 0 && N % 256 == 0) ? 256 : 128;
 }
 

@@ -279,7 +279,8 @@ def test_two_streams_get_their_own_workspace():
 # A short side of at most 256 with a long side of at least 8x it: the Gram is
 # computed over K chunks whose fp32 products are summed in a fixed order
 # (even and uneven chunk edges, tall and wide, 2 to 16 chunks).
-@pytest.mark.parametrize("shape", [(3, 100, 1500), (2, 128, 1100), (2, 200, 2300), (1, 3000, 120), (2, 128, 8192)])
+@pytest.mark.parametrize("shape", [(3, 100, 2100), (2, 128, 3300), (2, 200, 2300), (1, 3000, 120), (2, 128, 8192),
+                                   (1, 128, 16500)])
 def test_split_k_gram_shapes(shape):
     err = run_case(shape, "bf16", "bf16", (27, shape[1], shape[2], 1, 0))
     assert err <= TOL["bf16"], err
