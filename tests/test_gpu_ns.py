@@ -337,3 +337,19 @@ def test_ns_groups_mixed_shapes_bitwise(compute):
         assert torch.equal(o, a) and torch.equal(c, a)
     xin = storage_f64(synth.gaussian(shapes[0], (31, 0, 0, 1, 0), dt), dt)
     assert rel_fro(to_f64(outs[0])[1], oracle.newton_schulz5(xin[1])) <= TOL[compute]
+
+
+def test_ns_groups_more_problems_than_one_launch_holds():
+    # Eleven problems: every phase needs two launches (at most 8 problems per
+    # GEMM or poly128 launch).  Ten are 128-row heads with a split Gram (2 or
+    # 3 chunks, the fused sum-and-polynomial path), one is ragged.
+    torch = torch_cuda()
+    shapes = [(2, 128, 2048 + 128 * (i % 3) * 4) for i in range(10)] + [(1, 300, 520)]
+    xs = [to_dev(synth.gaussian(s, (33, i, 0, 1, 0), "bf16"), "bf16") for i, s in enumerate(shapes)]
+    grouped = ns.ns_groups(xs)
+    alone = [ns.ns_batched(x) for x in xs]
+    torch.cuda.synchronize()
+    for g, a in zip(grouped, alone):
+        assert torch.equal(g, a)
+    xin = storage_f64(synth.gaussian(shapes[9], (33, 9, 0, 1, 0), "bf16"), "bf16")
+    assert rel_fro(to_f64(grouped[9])[1], oracle.newton_schulz5(xin[1])) <= TOL["bf16"]
