@@ -498,6 +498,18 @@ def main():
           file=sys.stderr, flush=True)
 
     prof = {k: ns.profile_query(k) for k in ns.KERNEL_CLASSES}
+    # The same number of steps again without the per-launch events (informative:
+    # an event pair around every launch serializes the launch boundaries).
+    ev2 = torch.cuda.Event(enable_timing=True)
+    ev3 = torch.cuda.Event(enable_timing=True)
+    ev2.record(stream)
+    for _ in range(args.steps):
+        one_step()
+    ev3.record(stream)
+    torch.cuda.synchronize()
+    ms_plain = ev2.elapsed_time(ev3) / args.steps
+    print(f"[bench] {args.steps} more steps without launch events: {ms_plain:.3f} ms/step", file=sys.stderr,
+          flush=True)
     upd = prof["update"]
     upd_avg_ms = upd["ms"] / max(upd["launches"], 1)
     upd_tflops = upd["flop"] / (upd["ms"] * 1e-3) / 1e12 if upd["ms"] > 0 else 0.0
@@ -534,6 +546,8 @@ def main():
             "tflops_E": round(tf_E, 2), "pct_peak_E": round(100 * tf_E / PEAK_BF16_TFLOPS, 2),
             "flop_per_step_L": fl_L, "flop_per_step_E": fl_E,
             "kernel_classes": per_class,
+            "timed_region": "HIP events around every library launch (they give the roofline's kernel times)",
+            "ms_per_step_without_launch_events": round(ms_plain, 4),
         },
         "roofline": {
             "bound": "mfma",
