@@ -82,3 +82,36 @@ def test_step_groups_graph_replay_matches_eager():
             for key in ("w_master", "moms", "variances", "w_model"):
                 for x, y in zip(a[key], b[key]):
                     assert torch.equal(x, y), (step, k, key)
+
+
+def test_ns_groups_graph_replay_matches_eager():
+    # muon_ns_groups over per-head views of two projections (the fused
+    # sum-and-polynomial path) and a ragged matrix, captured once; each replay
+    # after new inputs are written equals an eager call bitwise.
+    torch = torch_cuda()
+    shapes = [(8, 128, 2048), (2, 128, 2048), (2, 300, 520)]
+    static_x = [torch.empty(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
+    outs = [torch.empty_like(x) for x in static_x]
+    cfg = ns.ns_config()
+    need = ns.ns_groups_workspace_bytes(shapes, cfg)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    ns.lib()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            ns.ns_groups(static_x, outs, cfg=cfg, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for step in (1, 2, 3):
+        xs = [to_dev(synth.gaussian(s, (35, k, 0, step, 0), "bf16"), "bf16") for k, s in enumerate(shapes)]
+        for sx, x in zip(static_x, xs):
+            sx.copy_(x)
+        eager = ns.ns_groups(xs)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e), step
