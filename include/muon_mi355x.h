@@ -303,6 +303,11 @@ int muon_step_groups(const muon_group* groups, int64_t ngroups, const muon_hpara
  * are kept per kernel class.  Off by default; enabling or disabling clears
  * nothing.  Reading synchronizes on the recorded events. */
 int muon_profile_enable(int on);
+/* Kernel classes whose launches are bracketed while timing is on: bit c of
+ * mask for class c (default all, (1u << MUON_K_COUNT) - 1).  Fewer events
+ * disturb the timed work less: an event pair serializes the launch
+ * boundaries it sits on. */
+int muon_profile_classes(uint32_t mask);
 int muon_profile_reset(void);
 int muon_profile_query(int kernel_class, int64_t* launches, double* total_ms,
                        double* total_flop, double* total_bytes);

@@ -28,7 +28,7 @@ from ._lib import MUON_BF16, MUON_F32, MuonError, NSConfig, NSProblem, Group, HP
 
 __all__ = ["ns_batched", "ns_groups", "ns_groups_workspace_bytes", "normuon_normalize", "step_group", "step_groups", "step_groups_workspace_bytes", "MuonNS5", "per_head_view", "ns_config",
            "hparams", "ns_workspace_bytes", "step_workspace_bytes", "normuon_workspace_bytes",
-           "profile_enable", "profile_reset", "profile_query", "MuonError", "QUINTIC", "abi_version",
+           "profile_enable", "profile_classes", "profile_reset", "profile_query", "MuonError", "QUINTIC", "abi_version",
            "state_layout_version", "lib"]
 
 QUINTIC = (3.4445, -4.7750, 2.0315)
@@ -428,6 +428,15 @@ class MuonNS5:
 # ---- launch timing ---------------------------------------------------------------
 def profile_enable(on=True):
     _lib.check(lib().muon_profile_enable(int(bool(on))))
+
+
+def profile_classes(names=None):
+    """Time only these kernel classes (names from KERNEL_CLASSES; None: all)."""
+    names = KERNEL_CLASSES if names is None else names
+    mask = 0
+    for n in names:
+        mask |= 1 << KERNEL_CLASSES.index(n)
+    return _lib.check(lib().muon_profile_classes(mask))
 
 
 def profile_reset():

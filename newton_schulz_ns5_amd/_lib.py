@@ -78,6 +78,7 @@ SIGNATURES = {
                                                  ctypes.POINTER(c_sz)]),
     "muon_step_groups": (c_i32, [ctypes.POINTER(Group), c_i64, ctypes.POINTER(HParams), c_vp, c_sz, c_vp]),
     "muon_profile_enable": (c_i32, [c_i32]),
+    "muon_profile_classes": (c_i32, [ctypes.c_uint32]),
     "muon_profile_reset": (c_i32, []),
     "muon_profile_query": (c_i32, [c_i32, ctypes.POINTER(c_i64), ctypes.POINTER(c_f64), ctypes.POINTER(c_f64),
                                    ctypes.POINTER(c_f64)]),

@@ -122,6 +122,7 @@ struct ClassTotals {
 };
 std::mutex g_prof_mu;
 bool g_prof_on = false;
+uint32_t g_prof_mask = (1u << MUON_K_COUNT) - 1;
 std::vector<Pending> g_pending;
 std::vector<hipEvent_t> g_event_pool;
 ClassTotals g_totals[MUON_K_COUNT];
@@ -138,7 +139,7 @@ hipError_t get_event(hipEvent_t* e) {
 // Launch through `fn`, bracketed by events when timing is on.
 template <class F>
 hipError_t run(int cls, double flop, double bytes, hipStream_t s, F&& fn) {
-  if (!g_prof_on) return fn();
+  if (!g_prof_on || !((g_prof_mask >> cls) & 1u)) return fn();
   std::lock_guard<std::mutex> lk(g_prof_mu);
   Pending pd{nullptr, nullptr, cls, flop, bytes};
   hipError_t e = get_event(&pd.a);
@@ -1096,6 +1097,13 @@ int muon_step_group(const muon_group* g, const muon_hparams* hp, void* workspace
 int muon_profile_enable(int on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_on = on != 0;
+  return ok();
+}
+
+int muon_profile_classes(uint32_t mask) {
+  if (mask >> MUON_K_COUNT) return fail(MUON_ERR_INVALID_ARG, "mask 0x%x names classes above %d", mask, MUON_K_COUNT - 1);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_mask = mask;
   return ok();
 }
 

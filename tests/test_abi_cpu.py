@@ -100,6 +100,16 @@ def test_versions_and_status_strings():
     assert L.muon_kernel_class_name(4) == b"update"
 
 
+def test_profile_class_mask():
+    L = m.lib()
+    assert L.muon_profile_classes(1 << 8) == -1          # no class 8
+    assert b"mask" in L.muon_last_error()
+    assert L.muon_profile_classes(1 << 4) == 0
+    assert L.muon_profile_classes(0xFF) == 0             # back to every class
+    m.profile_classes(["update", "gram"])
+    m.profile_classes()
+
+
 def test_defaults():
     c = m.ns_config()
     assert (c.steps, c.compute_dtype, c.max_batch) == (5, _lib.MUON_BF16, 0)
