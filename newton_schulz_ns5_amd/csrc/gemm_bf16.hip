@@ -232,6 +232,11 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   }
   const int KT = Kc / KS;
   auto slot = [&](int t, int op) { return smem + ((2 * t + op) % NSLOT) * OPB; };
+  // A SYRK diagonal tile multiplies a panel by itself: its Q rows are its P
+  // rows, so the Q loads are skipped and the Q fragments read the P slot.
+  // The waits below stay right: the loads a wait may leave in flight are
+  // still the youngest P loads.
+  const bool same_pq = SYRK && tm == tn && p.P == p.Q && p.ldp == p.ldq && p.sP == p.sQ;
   const uint32_t smem_lds =
       __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem);
 
@@ -293,7 +298,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
       if constexpr (NN)
         q[u - 1] = trq(t, ks, u - 1);
       else
-        q[u - 1] = __builtin_bit_cast(bf16x8, *(const u32x4*)(slot(t, 1) + qrd + (u - 1) * 32 * ROWB + so));
+        q[u - 1] = __builtin_bit_cast(bf16x8, *(const u32x4*)(slot(t, same_pq ? 0 : 1) + qrd + (u - 1) * 32 * ROWB + so));
     }
     else
       a[u - F] = __builtin_bit_cast(bf16x8, *(const u32x4*)(slot(t, 0) + prd + (u - F) * 32 * ROWB + so));
@@ -359,7 +364,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
     constexpr int cq = decltype(cq_c)::value, SD = decltype(sd_c)::value;
 #pragma unroll
     for (int u = 0; u < 2 * F; ++u) {
-      if ((u & 1) == 0 && (u >> 1) < DQ) dma(dt, dop, j0 + (u >> 1));
+      if ((u & 1) == 0 && (u >> 1) < DQ && !(dop == 1 && same_pq)) dma(dt, dop, j0 + (u >> 1));
       if (u < F) {
         frag(rt, rks, 2 * u, an, qn);
         frag(rt, rks, 2 * u + 1, an, qn);
@@ -396,12 +401,17 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
 #pragma unroll
   for (int j = 0; j < DPW; ++j) dma(0, 0, j);
 #pragma unroll
-  for (int j = 0; j < DPW; ++j) dma(0, 1, j);
+  for (int j = 0; j < DPW; ++j)
+    if (!same_pq) dma(0, 1, j);
 #pragma unroll
   for (int j = 0; j < DPW; ++j) dma(1, 0, j);
 #pragma unroll
-  for (int j = 0; j < DQ; ++j) dma(1, 1, j);
-  wait_vmcnt<DPW + DQ>();
+  for (int j = 0; j < DQ; ++j)
+    if (!same_pq) dma(1, 1, j);
+  if (same_pq)
+    wait_vmcnt<DPW>();  // P(1) may stay in flight
+  else
+    wait_vmcnt<DPW + DQ>();
   __builtin_amdgcn_s_barrier();
 #pragma unroll
   for (int u = 0; u < 2 * F; ++u) frag(0, 0, u, a0, q0);
