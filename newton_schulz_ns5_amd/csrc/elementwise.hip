@@ -49,11 +49,57 @@ __device__ __forceinline__ void load16(const void* row, int c, int valid, bool b
   for (int e = 0; e < 16; ++e) out[e] = (c + e < valid) ? load_elem(row, c + e, bf) : 0.f;
 }
 
+// Load 8 consecutive elements [0, 8) of a row, zero beyond `valid`.
+__device__ __forceinline__ void load8(const void* row, int valid, bool bf, bool vec, float* out) {
+  if (vec && valid >= 8) {
+    if (bf) {
+      const u32x4 a = *(const u32x4*)row;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        out[2 * w] = __uint_as_float(a[w] << 16);
+        out[2 * w + 1] = __uint_as_float(a[w] & 0xffff0000u);
+      }
+    } else {
+      const f32x4 a = ((const f32x4*)row)[0], b = ((const f32x4*)row)[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { out[e] = a[e]; out[4 + e] = b[e]; }
+    }
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = e < valid ? load_elem(row, e, bf) : 0.f;
+}
+
+// Store v[0 .. 8) (all eight with vector stores when `vec`, else the first
+// `valid`).
+__device__ __forceinline__ void store8v(void* row, int valid, bool bf, bool vec, const float* v) {
+  if (vec && valid >= 8) {
+    if (bf) {
+      u32x4 a;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) a[w] = pack_bf2(v[2 * w], v[2 * w + 1]);
+      *(u32x4*)row = a;
+    } else {
+      f32x4 a, b;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { a[e] = v[e]; b[e] = v[4 + e]; }
+      ((f32x4*)row)[0] = a;
+      ((f32x4*)row)[1] = b;
+    }
+    return;
+  }
+  for (int e = 0; e < 8 && e < valid; ++e) store_elem(row, e, v[e], bf);
+}
+
 // One 64 x 64 tile of the oriented, padded X0 per workgroup.
 //   mode 0: U = x (muon_ns_batched input)
 //   mode 1: M <- mu M + G;  U = G + mu M  (or U = M without Nesterov)
 // Writes U (rounded to the X dtype) at its oriented position, zeros in the
 // padding, and the tile's sum of U^2 (from the fp32 U) to partial[].
+// Thread -> rows tid / 8 and tid / 8 + 32 of the tile, 8 consecutive columns
+// each: eight lanes cover one 64-element row segment, so every wave access
+// is whole 128-byte lines (bf16).  The tile is staged in LDS for the
+// transposed write of a tall matrix.
 __global__ __launch_bounds__(256) void prep_kernel(const PrepParams p) {
   __shared__ float T[64][65];
   __shared__ float red[4];
@@ -61,100 +107,63 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams p) {
   const int bz = blockIdx.z;
   const int oi0 = blockIdx.y * 64, oj0 = blockIdx.x * 64;
   const int pr0 = p.tall ? oj0 : oi0, pc0 = p.tall ? oi0 : oj0;
-  const int r = tid >> 2, c0 = (tid & 3) * 16;
-  const int gr = pr0 + r, gc = pc0 + c0;
+  const int c0 = (tid & 7) * 8;
+  const int gc = pc0 + c0;
   const bool src_bf = p.src_dtype == MUON_BF16;
-  float u[16];
   float s = 0.f;
-  if (p.mode == 0) {
-    const void* row = (const uint8_t*)p.x +
-                      ((int64_t)bz * p.x_bs + (int64_t)gr * p.x_rs) * (src_bf ? 2 : 4);
-    const int valid = gr < p.rows ? p.cols - pc0 - c0 : 0;
-    const bool vec = ((p.x_rs | p.x_bs) & 7) == 0 && ((uintptr_t)p.x & 15) == 0;
-    float tmp[16];
-    if (valid > 0) load16((const uint8_t*)row + (int64_t)gc * (src_bf ? 2 : 4), 0, valid, src_bf, vec, tmp);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) u[e] = valid > 0 ? tmp[e] : 0.f;
-  } else {
-    const int pi = bz / p.heads, h = bz - pi * p.heads;
-    const bool mom_bf = p.mom_dtype == MUON_BF16;
-    const int64_t off = (int64_t)(h * p.rows + gr) * p.param_cols + gc;
-    const int valid = gr < p.rows ? p.cols - gc : 0;
-    const bool vec = (p.param_cols & 7) == 0;
-    float g[16], m[16];
-    if (valid > 0) {
-      load16((const uint8_t*)p.grad[pi] + off * (src_bf ? 2 : 4), 0, valid, src_bf, vec, g);
-      load16((const uint8_t*)p.mom[pi] + off * (mom_bf ? 2 : 4), 0, valid, mom_bf, vec, m);
-    }
+  for (int h = 0; h < 2; ++h) {
+    const int r = (tid >> 3) + 32 * h;
+    const int gr = pr0 + r;
+    float u[8];
+    if (p.mode == 0) {
+      const void* row = (const uint8_t*)p.x +
+                        ((int64_t)bz * p.x_bs + (int64_t)gr * p.x_rs + gc) * (src_bf ? 2 : 4);
+      const int valid = gr < p.rows ? p.cols - gc : 0;
+      const bool vec = ((p.x_rs | p.x_bs) & 7) == 0 && ((uintptr_t)p.x & 15) == 0;
+      float tmp[8];
+      if (valid > 0) load8(row, valid, src_bf, vec, tmp);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      if (e < valid) {
-        const float mn = p.mu * m[e] + g[e];
-        u[e] = p.nesterov ? g[e] + p.mu * mn : mn;
-        m[e] = mn;
-      } else {
-        u[e] = 0.f;
+      for (int e = 0; e < 8; ++e) u[e] = valid > 0 ? tmp[e] : 0.f;
+    } else {
+      const int pi = bz / p.heads, hd = bz - pi * p.heads;
+      const bool mom_bf = p.mom_dtype == MUON_BF16;
+      const int64_t off = (int64_t)(hd * p.rows + gr) * p.param_cols + gc;
+      const int valid = gr < p.rows ? p.cols - gc : 0;
+      const bool vec = (p.param_cols & 7) == 0;
+      float g[8], m[8];
+      if (valid > 0) {
+        load8((const uint8_t*)p.grad[pi] + off * (src_bf ? 2 : 4), valid, src_bf, vec, g);
+        load8((const uint8_t*)p.mom[pi] + off * (mom_bf ? 2 : 4), valid, mom_bf, vec, m);
       }
-    }
-    if (valid > 0) {
-      void* mp = (uint8_t*)p.mom[pi] + off * (mom_bf ? 2 : 4);
-      if (vec && valid >= 16) {
-        if (mom_bf) {
-          u32x4 a, b;
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            a[w] = pack_bf2(m[2 * w], m[2 * w + 1]);
-            b[w] = pack_bf2(m[8 + 2 * w], m[8 + 2 * w + 1]);
-          }
-          ((u32x4*)mp)[0] = a;
-          ((u32x4*)mp)[1] = b;
+      for (int e = 0; e < 8; ++e) {
+        if (e < valid) {
+          const float mn = p.mu * m[e] + g[e];
+          u[e] = p.nesterov ? g[e] + p.mu * mn : mn;
+          m[e] = mn;
         } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            f32x4 t;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) t[e] = m[4 * q + e];
-            ((f32x4*)mp)[q] = t;
-          }
+          u[e] = 0.f;
         }
-      } else {
-        for (int e = 0; e < 16 && e < valid; ++e) store_elem(mp, e, m[e], mom_bf);
       }
+      if (valid > 0) store8v((uint8_t*)p.mom[pi] + off * (mom_bf ? 2 : 4), valid, mom_bf, vec, m);
     }
-  }
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    s += u[e] * u[e];
-    T[r][c0 + e] = u[e];
+    for (int e = 0; e < 8; ++e) {
+      s += u[e] * u[e];
+      T[r][c0 + e] = u[e];
+    }
   }
   __syncthreads();
-  // Oriented write: X[oi0 + orow][oj0 + oc0 .. +16].
-  {
-    const int orow = tid >> 2, oc0 = (tid & 3) * 16;
-    float v[16];
+  // Oriented write: X[oi0 + orow][oj0 + c0 .. +8].
 #pragma unroll
-    for (int e = 0; e < 16; ++e) v[e] = p.tall ? T[oc0 + e][orow] : T[orow][oc0 + e];
-    const int64_t xoff = (int64_t)bz * p.X_bs + (int64_t)(oi0 + orow) * p.np + oj0 + oc0;
-    if (p.x_bf16) {
-      u32x4 a, b;
+  for (int h = 0; h < 2; ++h) {
+    const int orow = (tid >> 3) + 32 * h;
+    float v[8];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        a[w] = pack_bf2(v[2 * w], v[2 * w + 1]);
-        b[w] = pack_bf2(v[8 + 2 * w], v[8 + 2 * w + 1]);
-      }
-      u32x4* dst = (u32x4*)((uint16_t*)p.X + xoff);
-      dst[0] = a;
-      dst[1] = b;
-    } else {
-      f32x4* dst = (f32x4*)((float*)p.X + xoff);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        f32x4 t;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) t[e] = v[4 * q + e];
-        dst[q] = t;
-      }
-    }
+    for (int e = 0; e < 8; ++e) v[e] = p.tall ? T[c0 + e][orow] : T[orow][c0 + e];
+    const int64_t xoff = (int64_t)bz * p.X_bs + (int64_t)(oi0 + orow) * p.np + oj0 + c0;
+    store8v((uint8_t*)p.X + xoff * (p.x_bf16 ? 2 : 4), 8, p.x_bf16, true, v);
   }
   const float tot = block_sum(s, red);
   if (tid == 0) {
