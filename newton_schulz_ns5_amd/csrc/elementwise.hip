@@ -218,7 +218,35 @@ __global__ __launch_bounds__(256) void rowstat_kernel(const RowStatParams p) {
   const uint8_t* row = (const uint8_t*)p.O + ((int64_t)b * p.o_bs + (int64_t)r * p.o_rs) * (bf ? 2 : 4);
   const bool vec = ((p.o_bs | p.o_rs) & 7) == 0 && ((uintptr_t)p.O & 15) == 0;
   float s = 0.f;
-  for (int c = lane * 8; c < p.cols; c += 512) {
+  int c = lane * 8;
+  if (vec) {
+    // Four chunks in flight per lane; their squares are still added chunk by
+    // chunk in column order, as in the loop below.
+    for (; c + 3 * 512 + 8 <= p.cols; c += 4 * 512) {
+      float x[4][8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int ck = c + 512 * k;
+        if (bf) {
+          const u32x4 a = *(const u32x4*)(row + (int64_t)ck * 2);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            x[k][2 * w] = __uint_as_float(a[w] << 16);
+            x[k][2 * w + 1] = __uint_as_float(a[w] & 0xffff0000u);
+          }
+        } else {
+          const f32x4 a = *(const f32x4*)(row + (int64_t)ck * 4), b2 = *(const f32x4*)(row + (int64_t)ck * 4 + 16);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { x[k][e] = a[e]; x[k][4 + e] = b2[e]; }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += x[k][e] * x[k][e];
+    }
+  }
+  for (; c < p.cols; c += 512) {
     float x[8];
     if (vec && c + 8 <= p.cols) {
       if (bf) {
@@ -290,7 +318,51 @@ __global__ __launch_bounds__(256) void apply_kernel(const ApplyParams p) {
   float* w = p.w[b] + (int64_t)r * p.cols;
   uint16_t* wm = p.wm[b] ? (uint16_t*)p.wm[b] + (int64_t)r * p.cols : nullptr;
   if (p.vec) {
-    for (int c = lane * 8; c < p.cols; c += 512) {
+    // Two chunks per lane per step: both chunks' loads are issued before
+    // either is stored (O and W are distinct buffers).
+    int c = lane * 8;
+    for (; c + 512 < p.cols; c += 1024) {
+      float o[2][8];
+      f32x4 w0[2], w1[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int ck = c + 512 * k;
+        if (bf) {
+          const u32x4 a = *(const u32x4*)(orow + (int64_t)ck * 2);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            o[k][2 * q] = __uint_as_float(a[q] << 16);
+            o[k][2 * q + 1] = __uint_as_float(a[q] & 0xffff0000u);
+          }
+        } else {
+          const f32x4 a = *(const f32x4*)(orow + (int64_t)ck * 4), b2 = *(const f32x4*)(orow + (int64_t)ck * 4 + 16);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { o[k][e] = a[e]; o[k][4 + e] = b2[e]; }
+        }
+        w0[k] = *(const f32x4*)(w + ck);
+        w1[k] = *(const f32x4*)(w + ck + 4);
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int ck = c + 512 * k;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w0[k][e] = fmaf(-coef, o[k][e], p.decay * w0[k][e]);
+          w1[k][e] = fmaf(-coef, o[k][4 + e], p.decay * w1[k][e]);
+        }
+        *(f32x4*)(w + ck) = w0[k];
+        *(f32x4*)(w + ck + 4) = w1[k];
+        if (wm) {
+          u32x4 t;
+          t[0] = pack_bf2(w0[k][0], w0[k][1]);
+          t[1] = pack_bf2(w0[k][2], w0[k][3]);
+          t[2] = pack_bf2(w1[k][0], w1[k][1]);
+          t[3] = pack_bf2(w1[k][2], w1[k][3]);
+          *(u32x4*)(wm + ck) = t;
+        }
+      }
+    }
+    for (; c < p.cols; c += 512) {
       float o[8];
       if (bf) {
         const u32x4 a = *(const u32x4*)(orow + (int64_t)c * 2);
