@@ -204,23 +204,32 @@ def test_c4_conv_megabatches_normuon_two_steps():
                   check=[0, n // 2, n - 1], model_copy=True)
 
 
-def test_conv_equals_reshaped_linear_bitwise():
+# A convolution weight [out, *rest] steps bitwise like the [out, prod(rest)]
+# weight it flattens to: Conv1d, Conv2d and Conv3d shapes, megabatches of 1, 2,
+# 3 and 5, with and without NorMuon, over two steps.
+@pytest.mark.parametrize("shape,n", [((6, 5, 7), 1), ((8, 4, 3, 3), 2), ((4, 3, 2, 3, 3), 3), ((5, 6, 4), 5)])
+@pytest.mark.parametrize("normuon", [True, False])
+def test_conv_equals_reshaped_linear_bitwise(shape, n, normuon):
     torch = torch_cuda()
-    shape = (8, 4, 3, 3)
-    g = [to_dev(x, "bf16") for x in grads_for(5, 2, shape, "bf16", 1)]
-    w = [to_dev(x, "f32") for x in make_state(5, 2, shape, "bf16", "bf16")]
-    w2 = [t.clone().reshape(8, 36) for t in w]
-    m = [torch.zeros(shape, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
-    m2 = [torch.zeros((8, 36), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
-    v = [torch.zeros(8, device="cuda") for _ in range(2)]
-    v2 = [torch.zeros(8, device="cuda") for _ in range(2)]
-    ns.step_group(w, g, m, v, normuon=True)
-    ns.step_group(w2, [t.reshape(8, 36) for t in g], m2, v2, normuon=True)
+    rows, cols = shape[0], int(np.prod(shape[1:]))
+    w = [to_dev(x, "f32") for x in make_state(5, n, shape, "bf16", "bf16")]
+    w2 = [t.clone().reshape(rows, cols) for t in w]
+    m = [torch.zeros(shape, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+    m2 = [torch.zeros((rows, cols), dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+    v = [torch.zeros(rows, device="cuda") for _ in range(n)]
+    v2 = [torch.zeros(rows, device="cuda") for _ in range(n)]
+    for step in (1, 2):
+        g = [to_dev(x, "bf16") for x in grads_for(5, n, shape, "bf16", step)]
+        ns.step_group(w, g, m, v if normuon else None, normuon=normuon)
+        ns.step_group(w2, [t.reshape(rows, cols) for t in g], m2, v2 if normuon else None, normuon=normuon)
     torch.cuda.synchronize()
     for a, b in zip(w, w2):
-        assert torch.equal(a.reshape(8, 36), b)
-    for a, b in zip(v, v2):
-        assert torch.equal(a, b)
+        assert torch.equal(a.reshape(rows, cols), b)
+    for a, b in zip(m, m2):
+        assert torch.equal(a.reshape(rows, cols), b)
+    if normuon:
+        for a, b in zip(v, v2):
+            assert torch.equal(a, b)
 
 
 def test_group_size_invariance_bitwise():
