@@ -405,6 +405,37 @@ class MuonNS5:
                                     list(sp) if sp else None))
         self.workspace_bytes = step_groups_workspace_bytes([g for g, _ in made], self.hp) if made else 0
 
+    def state_dict(self):
+        """The optimizer state, per parameter in the order given: fp32 master weight,
+        momentum and NorMuon variance (the tensors themselves), tagged with the
+        library's state layout version (one fp32 variance per output channel)."""
+        return {"state_layout_version": state_layout_version(),
+                "state": [{k: self.state[id(p)][k] for k in ("master", "mom", "var")} for p in self.params]}
+
+    def load_state_dict(self, sd):
+        """Copy a state_dict() into this optimizer's state (same parameters, same
+        shapes and dtypes).  Refuses another state layout version, checked before
+        anything is copied."""
+        torch = _torch()
+        if sd.get("state_layout_version") != state_layout_version():
+            raise MuonError(_lib.MUON_ERR_INVALID_ARG,
+                            f"state layout version {sd.get('state_layout_version')} != {state_layout_version()}")
+        entries = sd.get("state", [])
+        if len(entries) != len(self.params):
+            raise MuonError(_lib.MUON_ERR_INVALID_ARG, f"{len(entries)} parameter states for {len(self.params)} parameters")
+        for p, e in zip(self.params, entries):
+            st = self.state[id(p)]
+            for k in ("master", "mom", "var"):
+                a, b = st[k], e.get(k)
+                if (a is None) != (b is None) or (a is not None and (a.shape != b.shape or a.dtype != b.dtype)):
+                    raise MuonError(_lib.MUON_ERR_INVALID_ARG, f"state '{k}' does not match the parameter's")
+        with torch.no_grad():
+            for p, e in zip(self.params, entries):
+                st = self.state[id(p)]
+                for k in ("master", "mom", "var"):
+                    if st[k] is not None:
+                        st[k].copy_(e[k])
+
     def step(self):
         torch = _torch()
         todo = []

@@ -365,3 +365,47 @@ def test_muon_ns5_optimizer_two_steps():
             else:
                 assert p.data.data_ptr() == opt.state[id(p)]["master"].data_ptr()
             ostate[k].update(w=r["w"], m=r["m"], v=r["v"])
+
+
+def test_muon_ns5_checkpoint_resume_bitwise():
+    # Two steps straight equal one step, state_dict through torch.save /
+    # torch.load (weights only), a fresh optimizer on the saved parameters and
+    # one more step: parameters, masters, momenta and variances bitwise.
+    import io
+    torch = torch_cuda()
+    specs = [((256, 384), torch.bfloat16), ((128, 256), torch.float32), ((8, 4, 3, 3), torch.bfloat16)]
+
+    def make_params():
+        return [torch.nn.Parameter(to_dev(synth.gaussian(s, (36, k, 0, 0, synth.ROLE_WEIGHT), "f32", std=0.02),
+                                          "f32").to(dt)) for k, (s, dt) in enumerate(specs)]
+
+    def set_grads(ps, step):
+        for k, (s, dt) in enumerate(specs):
+            r, c = s[0], int(np.prod(s[1:]))
+            g = synth.power_law((r, c), (36, k, 1), (36, k, 1, step), "bf16").reshape(s)
+            ps[k].grad = to_dev(g, "bf16").to(dt)
+
+    straight = make_params()
+    opt = ns.MuonNS5(straight, lr=0.05, normuon=True)
+    for step in (1, 2):
+        set_grads(straight, step)
+        opt.step()
+    first = make_params()
+    opt1 = ns.MuonNS5(first, lr=0.05, normuon=True)
+    set_grads(first, 1)
+    opt1.step()
+    torch.cuda.synchronize()
+    buf = io.BytesIO()
+    torch.save({"params": [p.detach() for p in first], "opt": opt1.state_dict()}, buf)
+    buf.seek(0)
+    saved = torch.load(buf, weights_only=True, map_location="cuda")
+    resumed = [torch.nn.Parameter(t.clone()) for t in saved["params"]]
+    opt2 = ns.MuonNS5(resumed, lr=0.05, normuon=True)
+    opt2.load_state_dict(saved["opt"])
+    set_grads(resumed, 2)
+    opt2.step()
+    torch.cuda.synchronize()
+    for a, b in zip(straight, resumed):
+        assert torch.equal(a.data, b.data)
+        for k in ("master", "mom", "var"):
+            assert torch.equal(opt.state[id(a)][k], opt2.state[id(b)][k]), k

@@ -71,3 +71,42 @@ def test_group_keeps_its_tensors_alive():
     del keep
     gc.collect()
     assert all(r() is None for r in refs)
+
+
+def test_state_dict_round_trip_and_checks():
+    # state_dict / load_state_dict move the caller-owned state (master, momentum,
+    # NorMuon variance) through torch.save / torch.load (weights only) and
+    # refuse a mismatching layout version or geometry before copying anything.
+    import io
+    ps = params((64, 96), (8, 4, 3, 3))
+    opt = ns.MuonNS5(ps, normuon=True)
+    for i, p in enumerate(ps):
+        st = opt.state[id(p)]
+        st["master"].fill_(0.5 + i)
+        st["mom"].fill_(-1.0 - i)
+        st["var"].fill_(0.25 * (i + 1))
+    buf = io.BytesIO()
+    torch.save(opt.state_dict(), buf)
+    buf.seek(0)
+    sd = torch.load(buf, weights_only=True)
+    assert sd["state_layout_version"] == ns.state_layout_version()
+    ps2 = params((64, 96), (8, 4, 3, 3))
+    opt2 = ns.MuonNS5(ps2, normuon=True)
+    opt2.load_state_dict(sd)
+    for p, q in zip(ps, ps2):
+        for k in ("master", "mom", "var"):
+            assert torch.equal(opt.state[id(p)][k], opt2.state[id(q)][k])
+    before = [opt2.state[id(q)]["master"].clone() for q in ps2]
+    bad_version = dict(sd, state_layout_version=sd["state_layout_version"] + 1)
+    with pytest.raises(ns.MuonError):
+        opt2.load_state_dict(bad_version)
+    with pytest.raises(ns.MuonError):
+        opt2.load_state_dict(dict(sd, state=sd["state"][:1]))
+    shape_bad = dict(sd, state=[sd["state"][0], dict(sd["state"][1], mom=torch.zeros(8, 36, dtype=torch.bfloat16))])
+    with pytest.raises(ns.MuonError):
+        opt2.load_state_dict(shape_bad)
+    no_var = ns.MuonNS5(params((64, 96), (8, 4, 3, 3)), normuon=False)
+    with pytest.raises(ns.MuonError):
+        no_var.load_state_dict(sd)                     # a NorMuon state into a plain Muon optimizer
+    for q, b in zip(ps2, before):
+        assert torch.equal(opt2.state[id(q)]["master"], b)
