@@ -140,12 +140,15 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, int64_t bytes) {
 // does not see it as an LDS write, so it does not make later LDS reads wait
 // for every load in flight (it would before each transpose read); the kernel
 // orders these loads itself with explicit vmcnt waits and barriers.
+// The LDS address reaches the instruction through M0, passed as an input
+// operand bound to that register: the compiler writes M0 itself and knows
+// it is read here, so nothing the compiler keeps in M0 is overwritten.
 __device__ __forceinline__ void lds_dma16_asm(i32x4 rsrc, uint32_t lds, int voff, int soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+  asm volatile("buffer_load_dwordx4 %1, %2, %3 offen lds"
                :
-               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc),
+               : "{m0}"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc),
                  "s"(__builtin_amdgcn_readfirstlane(soff))
-               : "memory", "m0");
+               : "memory");
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
