@@ -55,6 +55,14 @@
  *    larger matrices fail with MUON_ERR_INVALID_ARG.
  *  - Results for one matrix are bitwise independent of how many other
  *    matrices share the call and of its position in the batch.
+ *  - Input range: the Frobenius normalization is folded into the first
+ *    iteration, whose products accumulate the unnormalized input in fp32, and
+ *    ||U||_F^2 is summed in fp32.  Any input with ||U||_F below 1.8e19 (its
+ *    square within the fp32 range) is supported, down to the smallest normal
+ *    values; above it the output is NaN (never a silent zero).  Entries so
+ *    small that their squares fall below the fp32 normal range leave
+ *    ||U||_F far below eps, where the first iteration is a scaling by
+ *    a / (||U||_F + eps) that does not square the entries.
  */
 #ifndef MUON_MI355X_H
 #define MUON_MI355X_H
@@ -134,7 +142,9 @@ int muon_ns_workspace_bytes(int64_t n, int64_t rows, int64_t cols,
  * x      device, x_dtype (MUON_F32 / MUON_BF16); element (i, r, c) at
  *        x + i*x_batch_stride + r*x_row_stride + c.
  * y      device, y_dtype, same indexing with its own strides.  y may equal x
- *        (in place) when the strides are equal; other overlaps are invalid.
+ *        (in place) when the dtypes and strides are equal; any other overlap
+ *        of the bytes y reaches with the bytes x reaches is refused
+ *        (MUON_ERR_INVALID_ARG).
  * Layouts covered by the strides:
  *   - a megabatch [N, out, F] of flattened parameters ([ConvFix] "Problem and
  *     fix"): batch stride out*F, row stride F;
@@ -144,7 +154,8 @@ int muon_ns_workspace_bytes(int64_t n, int64_t rows, int64_t cols,
  * workspace: device, at least muon_ns_workspace_bytes() bytes, 256-byte
  *            aligned; its contents on entry do not matter.
  * Errors: MUON_ERR_INVALID_ARG (null pointers for a non-empty problem,
- * negative sizes, strides too small, steps outside 1..64, reserved != 0),
+ * negative sizes, strides too small, overlapping x and y, steps outside
+ * 1..64, schedule not 0 or 1, max_batch < 0, non-finite coefficients),
  * MUON_ERR_UNSUPPORTED (unknown dtype), MUON_ERR_WORKSPACE, MUON_ERR_HIP. */
 int muon_ns_batched(const void* x, int32_t x_dtype, int64_t x_batch_stride, int64_t x_row_stride,
                     void* y, int32_t y_dtype, int64_t y_batch_stride, int64_t y_row_stride,

@@ -172,7 +172,10 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams p) {
   }
 }
 
-// rs[b] = 1 / (sqrt(sum of the matrix's tile partials) + eps).
+// rs[b] = 1 / (sqrt(sum of the matrix's tile partials) + eps).  A sum that
+// is not finite (an input whose squared Frobenius norm exceeds the fp32
+// range, or a NaN in it) gives rs = NaN, so the output is NaN rather than a
+// silently zero matrix.
 __global__ __launch_bounds__(256) void norm_kernel(const NormParams p) {
   __shared__ float red[4];
   const int b = blockIdx.x;
@@ -180,7 +183,7 @@ __global__ __launch_bounds__(256) void norm_kernel(const NormParams p) {
   float s = 0.f;
   for (int i = threadIdx.x; i < p.tiles; i += 256) s += src[i];
   const float tot = block_sum(s, red);
-  if (threadIdx.x == 0) p.rs[b] = 1.f / (sqrtf(tot) + p.eps);
+  if (threadIdx.x == 0) p.rs[b] = __builtin_isfinite(tot) ? 1.f / (sqrtf(tot) + p.eps) : __builtin_nanf("");
 }
 
 // Split-K Gram: A = bf16(rs^2 * (part_0 + part_1 + ...)), the chunks added in

@@ -491,6 +491,13 @@ int64_t chunk_of(int64_t n, int64_t max_batch) {
 }
 
 
+// Byte span [lo, hi) reached by a strided batch of matrices.
+struct Span { uintptr_t lo, hi; };
+Span span_of(const void* p, int32_t dt, int64_t bs, int64_t rs, int64_t n, int64_t rows, int64_t cols) {
+  const uintptr_t lo = (uintptr_t)p;
+  return {lo, lo + (uintptr_t)(((n - 1) * bs + (rows - 1) * rs + cols) * (int64_t)esize(dt))};
+}
+
 bool ns_empty(const muon_ns_problem& q) { return q.n == 0 || q.rows == 0 || q.cols == 0; }
 
 // The argument checks of one Newton-Schulz problem (the config is checked by
@@ -508,9 +515,18 @@ int check_ns_problem(const muon_ns_problem& q) {
   if (((uintptr_t)q.x % esize(q.x_dtype)) || ((uintptr_t)q.y % esize(q.y_dtype)))
     return fail(MUON_ERR_INVALID_ARG, "x/y not aligned to their element size");
   // In place needs equal layouts, so that the final store of a matrix only
-  // overwrites that matrix's own (already read) input.
-  if (q.y == q.x && (q.x_dtype != q.y_dtype || q.x_batch_stride != q.y_batch_stride || q.x_row_stride != q.y_row_stride))
-    return fail(MUON_ERR_INVALID_ARG, "in-place call needs identical dtype and strides");
+  // overwrites that matrix's own (already read) input.  Any other overlap of
+  // the output with the input is refused: when the work is cut into passes
+  // (max_batch, or more than 65535 matrices) an earlier pass would overwrite
+  // inputs of a later one.
+  if (q.y == q.x) {
+    if (q.x_dtype != q.y_dtype || q.x_batch_stride != q.y_batch_stride || q.x_row_stride != q.y_row_stride)
+      return fail(MUON_ERR_INVALID_ARG, "in-place call needs identical dtype and strides");
+  } else {
+    const Span xs = span_of(q.x, q.x_dtype, q.x_batch_stride, q.x_row_stride, q.n, q.rows, q.cols);
+    const Span ys = span_of(q.y, q.y_dtype, q.y_batch_stride, q.y_row_stride, q.n, q.rows, q.cols);
+    if (xs.lo < ys.hi && ys.lo < xs.hi) return fail(MUON_ERR_INVALID_ARG, "output overlaps the input (only y == x is allowed)");
+  }
   return MUON_OK;
 }
 
@@ -526,13 +542,6 @@ int check_workspace(const void* ws, size_t have, size_t need) {
   if ((uintptr_t)ws & 255) return fail(MUON_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   if (have < need) return fail(MUON_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, have);
   return MUON_OK;
-}
-
-// Byte span [lo, hi) reached by a strided batch of matrices.
-struct Span { uintptr_t lo, hi; };
-Span span_of(const void* p, int32_t dt, int64_t bs, int64_t rs, int64_t n, int64_t rows, int64_t cols) {
-  const uintptr_t lo = (uintptr_t)p;
-  return {lo, lo + (uintptr_t)(((n - 1) * bs + (rows - 1) * rs + cols) * (int64_t)esize(dt))};
 }
 
 // No problem's output span meets another problem's input or output span.

@@ -140,6 +140,8 @@ def ns_call(**over):
     (dict(n=-1), -1), (dict(rows=-3), -1), (dict(xrs=10), -1), (dict(yrs=63), -1), (dict(xbs=-1), -1),
     (dict(xd=7), -2), (dict(yd=2), -2), (dict(cfg_kw=dict(steps=0)), -1), (dict(cfg_kw=dict(steps=65)), -1),
     (dict(cfg=None), -1), (dict(wsb=100), -3), (dict(n=2, ybs=10), -1), (dict(x=FAKE + 1), -1),
+    # y overlapping x without being x, and in place with another dtype or stride
+    (dict(y=FAKE + 128), -1), (dict(n=3, y=FAKE + 64 * 64 * 2 * 2), -1), (dict(yd=0), -1), (dict(yrs=72), -1),
     (dict(rows=1 << 25), -1), (dict(rows=128, cols=(1 << 22) - 127, xrs=1 << 22, yrs=1 << 22, xbs=1 << 30,
                                      ybs=1 << 30), -1),
 ])
