@@ -380,20 +380,31 @@ class MuonNS5:
             key = (tuple(p.shape), p.dtype, int(heads.get(id(p), 1)), tuple(int(h) for h in sp) if sp else None)
             self.groups.setdefault(key, []).append(p)
         self.state = {}
+        # The library takes contiguous row-major tensors.  A contiguous fp32
+        # parameter is its own master weight; any other parameter gets a
+        # contiguous fp32 master.  A bf16 parameter receives RNE(master) from
+        # the update kernel: in place when contiguous, else into a contiguous
+        # bf16 buffer that step() copies into the parameter (a channels_last
+        # conv weight, say).  A non-contiguous fp32 parameter gets its
+        # master copied back the same way.
+        self._copy_back = []
         for key, ps in self.groups.items():
             for p in ps:
                 md = mom_dtype or p.dtype
-                # An fp32 parameter is its own master weight; a bf16 one gets an
-                # fp32 master and receives RNE(master) from the update kernel.
-                if p.dtype == torch.float32 and p.is_contiguous():
-                    master = p.data
-                else:
-                    master = p.detach().to(torch.float32).contiguous().clone()
+                own = p.dtype == torch.float32 and p.is_contiguous()
+                master = p.data if own else p.detach().to(torch.float32).contiguous().clone()
+                model = None
+                if p.dtype == torch.bfloat16:
+                    model = p.data if p.is_contiguous() else torch.empty(p.shape, dtype=torch.bfloat16,
+                                                                          device=p.device)
                 self.state[id(p)] = {
                     "master": master,
                     "mom": torch.zeros(p.shape, dtype=md, device=p.device),
                     "var": torch.zeros(p.shape[0], dtype=torch.float32, device=p.device) if normuon else None,
+                    "model": model,
                 }
+                if not own and not (model is not None and model.data_ptr() == p.data_ptr()):
+                    self._copy_back.append(p)
         # Reject bad geometry (heads, row splits) and hyperparameters here, not
         # at the first step: the workspace query checks every group's shape
         # and the Newton-Schulz configuration without touching device memory.
@@ -449,11 +460,19 @@ class MuonNS5:
                 "grads": [p.grad.contiguous() for p in live],
                 "moms": [s["mom"] for s in st],
                 "variances": [s["var"] for s in st] if self.hp.normuon else None,
-                "w_model": [p.data for p in live] if dt == torch.bfloat16 else None,
+                "w_model": [s["model"] for s in st] if dt == torch.bfloat16 else None,
                 "heads": h,
                 "split_rows": list(sp) if sp else None,
             })
         step_groups(todo, hp=self.hp)
+        # Parameters whose storage the library does not write: copy the new
+        # values in (a layout change only, on the same stream).
+        with torch.no_grad():
+            for p in self._copy_back:
+                if p.grad is None:
+                    continue
+                st = self.state[id(p)]
+                p.data.copy_(st["model"] if p.dtype == torch.bfloat16 else st["master"])
 
 
 # ---- launch timing ---------------------------------------------------------------
