@@ -58,3 +58,33 @@ def bf16_ulp_diff(a, b):
 
 
 TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def check_step_against_oracle(tag, w_after, m_after, v_after, wm_after, w_before, g_f64, ostate, hp, tol):
+    """One parameter after one GPU step against one oracle step taken from the
+    oracle's own state ``ostate`` (dict with w, m, v; advanced in place).
+
+    w_after / m_after / v_after: exact float64 copies of the GPU's fp32 master,
+    momentum and NorMuon variance (v_after None without NorMuon); wm_after: the
+    bf16 model copy as uint16 bits, or None; w_before: the master before the
+    step.  Checks the weight change (relative Frobenius error <= tol), the
+    momentum (within 1 bf16 ulp, or 2^-20 (|mu m| + |g|) where the update
+    cancels; fp32 momentum within max(tol, 1e-6) relative), the variance
+    (<= 2 tol) and the model copy (bitwise RNE of the GPU master)."""
+    import oracle
+    r = oracle.muon_step(ostate["w"], g_f64, ostate["m"], ostate["v"], hp)
+    err = rel_fro(w_after - w_before, r["w"] - ostate["w"])
+    assert err <= tol, (tag, "dW", err)
+    if hp.mom_dtype == "bf16":
+        diff = bf16_ulp_diff(m_after, r["m"])
+        scale = hp.momentum * np.abs(ostate["m"]) + np.abs(g_f64)
+        off = (diff > 1) & (np.abs(m_after - r["m"]) > 2.0 ** -20 * scale)
+        assert not off.any(), (tag, "momentum", int(off.sum()))
+    else:
+        assert rel_fro(m_after, r["m"]) <= max(tol, 1e-6), (tag, "momentum")
+    if hp.normuon:
+        assert rel_fro(v_after, r["v"]) <= 2 * tol, (tag, "variance")
+    if wm_after is not None:
+        assert np.array_equal(wm_after, synth.f64_to_bf16_bits(w_after)), (tag, "model copy")
+    ostate.update(w=r["w"], m=r["m"], v=r["v"])
+    return err

@@ -5,7 +5,8 @@ memset, no synchronization while launch timing is off), so a
 ``muon_step_groups`` call can be captured once and replayed.  The graph is
 replayed three times, each time after new gradients are written into its
 static input tensors and after eager steps of an identical copy of the state,
-and every replay is compared bitwise with the eager result.
+and every replay is compared bitwise with the eager result; a second captured
+step is replayed twice and each replay is checked against the float64 oracle.
 """
 import numpy as np
 import pytest
@@ -115,3 +116,54 @@ def test_ns_groups_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for o, e in zip(outs, eager):
             assert torch.equal(o, e), step
+
+
+def test_step_groups_graph_replay_matches_oracle():
+    # The captured step against the float64 oracle: two replays (new
+    # gradients written into the captured input tensors before each), every
+    # parameter's weight change, momentum, NorMuon variance and model copy
+    # checked after each replay (the head-split group per head, as the
+    # oracle's per-head step).
+    import oracle
+    from gpu_util import TOL, check_step_against_oracle, to_f64
+    torch = torch_cuda()
+    hp = ns.hparams(normuon=True, ns=ns.ns_config(compute_dtype="bf16"))
+    graphed = make_states(torch, 37)
+    static_g = [[torch.empty(shape, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+                for shape, n, _ in SHAPES]
+    for st, g in zip(graphed, static_g):
+        st["grads"] = g
+    need = ns.step_groups_workspace_bytes([ns._make_group(st["w_master"], st["grads"], st["moms"],
+                                                          st["variances"], st["w_model"], st["heads"])[0]
+                                           for st in graphed], hp)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    ns.lib()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            ns.step_groups(graphed, hp=hp, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ostate = [[{"w": to_f64(w), "m": np.zeros(shape), "v": np.zeros(shape[0])} for w in st["w_master"]]
+              for st, (shape, n, _) in zip(graphed, SHAPES)]
+    for step in (1, 2):
+        gs = grads(37, step)
+        for k in range(len(SHAPES)):
+            for i, g in enumerate(gs[k]):
+                static_g[k][i].copy_(to_dev(g, "bf16"))
+        before = [[to_f64(w) for w in st["w_master"]] for st in graphed]
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, (shape, n, heads) in enumerate(SHAPES):
+            ohp = oracle.MuonHParams(lr=0.05, normuon=True, heads=heads, mom_dtype="bf16")
+            st = graphed[k]
+            for i in range(n):
+                wm = st["w_model"][i].cpu().view(torch.int16).numpy().view(np.uint16)
+                check_step_against_oracle(
+                    f"replay {step} group {k} param {i}", to_f64(st["w_master"][i]), to_f64(st["moms"][i]),
+                    to_f64(st["variances"][i]), wm, before[k][i], synth.bf16_bits_to_f64(gs[k][i]), ostate[k][i],
+                    ohp, TOL["bf16"])

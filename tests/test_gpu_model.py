@@ -7,11 +7,16 @@ fp32 master weights and a bf16 model copy, for two steps.  Gradients follow
 the power-law recipe (U diag(i^-0.7) V^T + 0.1 N(0,1)); U, V and s are drawn
 once per shape.
 
-Checks: sampled matrices against the oracle (k and v on both steps, q and
-gate on step 1); every other matrix bitwise
-against the same parameters stepped by per-group calls (c2) or by the
-single-layer configuration (c5), since a matrix's result does not depend on
-the batch it is stepped in.
+The GPU work of each workload runs once, in a module fixture that keeps host
+copies of what the checks need; every matrix is then checked against the
+oracle in a test of its own (the oracle takes tens of seconds per 4096 x
+14336 matrix-step):
+
+* c2: all seven matrices on both steps; every matrix also bitwise equal to
+  the same parameters stepped by per-group calls;
+* c5: all seven matrices of one seeded layer on both steps, k and v of a
+  second one; both layers bitwise equal to the same layer stepped alone
+  (a matrix's result does not depend on the batch it is stepped in).
 """
 import functools
 
@@ -20,16 +25,20 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import TOL, bf16_ulp_diff, rel_fro, storage_f64, to_dev, to_f64, torch_cuda
+from gpu_util import TOL, check_step_against_oracle, to_dev, torch_cuda
 
 import newton_schulz_ns5_amd as ns
 
 pytestmark = pytest.mark.gpu
 
 LAYER = synth.LLAMA3_8B_LAYER
+NAMES = [n for n, _ in LAYER]
+SHAPE = dict(LAYER)
 WORKLOAD = 2        # key prefix of the layer workload's inputs
 INDEX = {name: i for i, (name, _) in enumerate(LAYER)}
 LR = 0.05
+KEYS = ("w_master", "moms", "variances", "w_model")
+C5_LAYERS = 32
 
 
 def shape_groups():
@@ -56,6 +65,10 @@ def hparams():
                 ns=ns.ns_config(compute_dtype="bf16"))
 
 
+def oracle_hp():
+    return oracle.MuonHParams(lr=LR, normuon=True, mom_dtype="bf16")
+
+
 def new_state(torch, shape, w0):
     return {
         "w_master": w0.clone(),
@@ -79,86 +92,105 @@ def groups_of(states, grads, names_by_shape):
     return out
 
 
-def check_against_oracle(torch, name, st, before, g_bits, ostate, step):
-    """One matrix after one step vs the oracle step from the oracle's own state."""
-    hp = oracle.MuonHParams(lr=LR, normuon=True, mom_dtype="bf16")
-    r = oracle.muon_step(ostate["w"], storage_f64(g_bits, "bf16"), ostate["m"], ostate["v"], hp)
-    tol = TOL["bf16"]
-    w_gpu = to_f64(st["w_master"])
-    err = rel_fro(w_gpu - before, r["w"] - ostate["w"])
-    assert err <= tol, (name, step, "dW", err)
-    m_gpu = to_f64(st["moms"])
-    diff = bf16_ulp_diff(m_gpu, r["m"])
-    scale = 0.95 * np.abs(ostate["m"]) + np.abs(storage_f64(g_bits, "bf16"))
-    assert not ((diff > 1) & (np.abs(m_gpu - r["m"]) > 2.0 ** -20 * scale)).any(), (name, step, "momentum")
-    assert rel_fro(to_f64(st["variances"]), r["v"]) <= 2 * tol, (name, step, "variance")
-    got = st["w_model"].cpu().view(torch.int16).numpy().view(np.uint16)
-    assert np.array_equal(got, synth.f64_to_bf16_bits(w_gpu)), (name, step, "model copy")
-    ostate.update(w=r["w"], m=r["m"], v=r["v"])
+def bits16(torch, t):
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
 
 
-def test_c2_layer_grouped_step_parity():
+def snapshot(torch, st):
+    """Host copies of one parameter's state: fp32 master and variance, bf16
+    momentum and model copy as bit patterns."""
+    return {"w": st["w_master"].cpu().numpy(), "m": bits16(torch, st["moms"]),
+            "v": st["variances"].cpu().numpy(), "wm": bits16(torch, st["w_model"])}
+
+
+def check_two_steps(tag, w0, snaps, gbits):
+    """One matrix's two GPU steps (host snapshots) against two oracle steps."""
+    shape = w0.shape
+    ostate = {"w": w0.astype(np.float64), "m": np.zeros(shape), "v": np.zeros(shape[0])}
+    before = w0.astype(np.float64)
+    errs = []
+    for step in (1, 2):
+        sn = snaps[step]
+        w_after = sn["w"].astype(np.float64)
+        errs.append(check_step_against_oracle(
+            f"{tag} step {step}", w_after, synth.bf16_bits_to_f64(sn["m"]), sn["v"].astype(np.float64), sn["wm"],
+            before, synth.bf16_bits_to_f64(gbits[step]), ostate, oracle_hp(), TOL["bf16"]))
+        before = w_after
+    print(f"{tag}: relative error of the weight change vs the oracle, steps 1-2: "
+          f"{errs[0]:.3e} {errs[1]:.3e}", flush=True)
+
+
+# ---- c2: one layer ---------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def c2_run():
     torch = torch_cuda()
     groups = shape_groups()
-    w0 = {n: to_dev(synth.gaussian(s, (WORKLOAD, 0, INDEX[n], 0, synth.ROLE_WEIGHT), "f32", std=0.02), "f32")
-          for n, s in LAYER}
-    grouped = {n: new_state(torch, s, w0[n]) for n, s in LAYER}
-    single = {n: new_state(torch, s, w0[n]) for n, s in LAYER}
-    # name -> oracle-checked steps; gate (14336 x 4096) is the tall class whose
-    # last update writes the transposed output, about 11 TFLOP of float64 work
-    sampled = {"k": (1, 2), "v": (1, 2), "q": (1,), "gate": (1,)}
-    ostate = {n: {"w": to_f64(w0[n]), "m": np.zeros(dict(LAYER)[n]), "v": np.zeros(dict(LAYER)[n][0])}
-              for n in sampled}
+    w0 = {n: synth.gaussian(s, (WORKLOAD, 0, INDEX[n], 0, synth.ROLE_WEIGHT), "f32", std=0.02) for n, s in LAYER}
+    grouped = {n: new_state(torch, s, to_dev(w0[n], "f32")) for n, s in LAYER}
+    single = {n: new_state(torch, s, to_dev(w0[n], "f32")) for n, s in LAYER}
+    out = {"w0": w0, "bits": {}, "snaps": {n: {} for n in NAMES}, "mismatch": []}
     for step in (1, 2):
         bits = {n: synth.power_law_from_signal(signal(s), (WORKLOAD, 0, INDEX[n], step)) for n, s in LAYER}
         grads = {n: to_dev(bits[n], "bf16") for n in bits}
-        before = {n: to_f64(grouped[n]["w_master"]) for n in sampled}
         ns.step_groups(groups_of(grouped, grads, groups), **hparams())
         for shape, names in groups:
             ns.step_groups(groups_of(single, grads, [(shape, names)]), **hparams())
         torch.cuda.synchronize()
-        for n, _ in LAYER:
-            for key in ("w_master", "moms", "variances", "w_model"):
-                assert torch.equal(grouped[n][key], single[n][key]), (n, step, key)
-        for n, steps in sampled.items():
-            if step <= max(steps):
-                if step in steps:
-                    check_against_oracle(torch, n, grouped[n], before[n], bits[n], ostate[n], step)
-                else:
-                    hp = oracle.MuonHParams(lr=LR, normuon=True, mom_dtype="bf16")
-                    r = oracle.muon_step(ostate[n]["w"], storage_f64(bits[n], "bf16"), ostate[n]["m"],
-                                         ostate[n]["v"], hp)
-                    ostate[n].update(w=r["w"], m=r["m"], v=r["v"])
+        out["mismatch"] += [(n, step, k) for n in NAMES for k in KEYS if not torch.equal(grouped[n][k], single[n][k])]
+        for n in NAMES:
+            out["snaps"][n][step] = snapshot(torch, grouped[n])
+        out["bits"][step] = bits
+        del grads
+    del grouped, single
+    torch.cuda.empty_cache()
+    return out
 
 
-def test_c5_model_step_batch_invariance_and_parity():
+@pytest.mark.timeout(600)
+def test_c2_grouped_step_bitwise_equals_per_group_calls(c2_run):
+    assert not c2_run["mismatch"], c2_run["mismatch"][:8]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", NAMES)
+def test_c2_matrix_two_steps_against_oracle(c2_run, name):
+    check_two_steps(f"c2 {name}", c2_run["w0"][name], c2_run["snaps"][name],
+                    {s: c2_run["bits"][s][name] for s in (1, 2)})
+
+
+# ---- c5: the 32-layer model --------------------------------------------------------
+
+C5_PICKS = sorted(int(x) for x in synth.generator(5, 99).choice(C5_LAYERS, size=2, replace=False))
+C5_ORACLE = [(C5_PICKS[0], n) for n in NAMES] + [(C5_PICKS[1], "k"), (C5_PICKS[1], "v")]
+
+
+@pytest.fixture(scope="module")
+def c5_run():
     """32 layers, 224 matrices (6,979,321,856 parameters) in four groups of
     64, 64, 64 and 32 matrices; per-layer noise drawn on the GPU."""
     torch = torch_cuda()
-    L = 32
     groups = shape_groups()
     sig_dev = {s: torch.from_numpy(signal(s).astype(np.float32)).cuda() for s, _ in groups}
-    order = [(s, [(l, n) for l in range(L) for n in names]) for s, names in groups]
+    order = [(s, [(l, n) for l in range(C5_LAYERS) for n in names]) for s, names in groups]
 
     def w_init(l, n):
         gen = torch.Generator(device="cuda")
         gen.manual_seed(synth.key_seed((5, l, INDEX[n], 0, synth.ROLE_WEIGHT)))
-        return 0.02 * torch.randn(dict(LAYER)[n], generator=gen, device="cuda", dtype=torch.float32)
+        return 0.02 * torch.randn(SHAPE[n], generator=gen, device="cuda", dtype=torch.float32)
 
     def grad(l, n, step):
-        return synth.power_law_device(sig_dev[dict(LAYER)[n]], (5, l, INDEX[n], step))
+        return synth.power_law_device(sig_dev[SHAPE[n]], (5, l, INDEX[n], step))
 
     state = {}
     for s, members in order:
         for l, n in members:
             state[(l, n)] = new_state(torch, s, w_init(l, n))
-    picks = sorted(int(x) for x in synth.generator(5, 99).choice(L, size=2, replace=False))
-    alone = {(l, n): new_state(torch, s, state[(l, n)]["w_master"]) for l in picks for n, s in LAYER}
-    ostate = {(l, n): {"w": to_f64(state[(l, n)]["w_master"]), "m": np.zeros(dict(LAYER)[n]),
-                       "v": np.zeros(dict(LAYER)[n][0])} for l in picks for n in ("k", "v")}
+    alone = {(l, n): new_state(torch, s, state[(l, n)]["w_master"]) for l in C5_PICKS for n, s in LAYER}
+    out = {"w0": {k: state[k]["w_master"].cpu().numpy() for k in C5_ORACLE}, "bits": {k: {} for k in C5_ORACLE},
+           "snaps": {k: {} for k in C5_ORACLE}, "mismatch": []}
     for step in (1, 2):
         grads = {key: grad(*key, step) for key in state}
-        before = {key: to_f64(state[key]["w_master"]) for key in ostate}
         args = []
         for s, members in order:
             args.append({
@@ -169,15 +201,28 @@ def test_c5_model_step_batch_invariance_and_parity():
                 "w_model": [state[k]["w_model"] for k in members],
             })
         ns.step_groups(args, **hparams())
-        for l in picks:
-            ns.step_groups(groups_of({n: alone[(l, n)] for n, _ in LAYER}, {n: grads[(l, n)] for n, _ in LAYER},
-                                     groups), **hparams())
+        for l in C5_PICKS:
+            ns.step_groups(groups_of({n: alone[(l, n)] for n in NAMES}, {n: grads[(l, n)] for n in NAMES}, groups),
+                           **hparams())
         torch.cuda.synchronize()
-        for l in picks:
-            for n, _ in LAYER:
-                for key in ("w_master", "moms", "variances", "w_model"):
-                    assert torch.equal(state[(l, n)][key], alone[(l, n)][key]), (l, n, step, key)
-        for (l, n), os_ in ostate.items():
-            bits = grads[(l, n)].cpu().view(torch.int16).numpy().view(np.uint16)
-            check_against_oracle(torch, f"{n}{l}", state[(l, n)], before[(l, n)], bits, os_, step)
-        del grads
+        out["mismatch"] += [(l, n, step, k) for l in C5_PICKS for n in NAMES for k in KEYS
+                            if not torch.equal(state[(l, n)][k], alone[(l, n)][k])]
+        for key in C5_ORACLE:
+            out["snaps"][key][step] = snapshot(torch, state[key])
+            out["bits"][key][step] = bits16(torch, grads[key])
+        del grads, args
+    del state, alone, sig_dev
+    torch.cuda.empty_cache()
+    return out
+
+
+@pytest.mark.timeout(600)
+def test_c5_sampled_layers_bitwise_equal_single_layer_steps(c5_run):
+    assert not c5_run["mismatch"], c5_run["mismatch"][:8]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("layer,name", C5_ORACLE)
+def test_c5_matrix_two_steps_against_oracle(c5_run, layer, name):
+    key = (layer, name)
+    check_two_steps(f"c5 layer {layer} {name}", c5_run["w0"][key], c5_run["snaps"][key], c5_run["bits"][key])

@@ -26,7 +26,7 @@ def make_state(cfg, n, shape, gdt, mdt, key_layer=0):
     return ws
 
 
-def grads_for(cfg, n, shape, gdt, step, power=False):
+def grads_for(cfg, n, shape, gdt, step, power=False, gscale=1.0):
     out = []
     for i in range(n):
         if power:
@@ -34,13 +34,13 @@ def grads_for(cfg, n, shape, gdt, step, power=False):
             c = int(np.prod(shape[1:]))
             g = synth.power_law((r, c), (cfg, 0, i), (cfg, 0, i, step), gdt).reshape(shape)
         else:
-            g = synth.gaussian(shape, (cfg, 0, i, step, synth.ROLE_GRAD), gdt)
+            g = synth.gaussian(shape, (cfg, 0, i, step, synth.ROLE_GRAD), gdt, std=gscale)
         out.append(g)
     return out
 
 
 def run_steps(shape, n, gdt, mdt, compute, steps=2, normuon=False, heads=1, model_copy=False, power=False,
-              cfg_id=7, lr=0.05, wd=0.0, check=None, split_rows=None):
+              cfg_id=7, lr=0.05, wd=0.0, check=None, split_rows=None, gscale=1.0):
     torch = torch_cuda()
     w0 = make_state(cfg_id, n, shape, gdt, mdt)
     tdt = {"bf16": torch.bfloat16, "f32": torch.float32}
@@ -57,7 +57,7 @@ def run_steps(shape, n, gdt, mdt, compute, steps=2, normuon=False, heads=1, mode
     tol = TOL[compute]
     check = list(range(n)) if check is None else check
     for step in range(1, steps + 1):
-        g = grads_for(cfg_id, n, shape, gdt, step, power)
+        g = grads_for(cfg_id, n, shape, gdt, step, power, gscale)
         G = [to_dev(x, gdt) for x in g]
         before = [to_f64(w) for w in W]
         ns.step_group(W, G, M, V, WM, heads=heads, split_rows=split_rows, lr=lr, weight_decay=wd,
@@ -300,6 +300,74 @@ def test_normuon_normalize_parity():
         ref, rv = oracle.normuon(o[i].astype(np.float64), v0[i].astype(np.float64), 0.95, 1e-8)
         assert rel_fro(got[i], ref) <= 1e-5
         assert rel_fro(gv[i], rv) <= 1e-5
+
+
+@pytest.mark.parametrize("gscale", [1e-12, 1e12])
+@pytest.mark.parametrize("compute", ["bf16", "f32"])
+def test_step_gradient_scale(gscale, compute):
+    # Momentum, the folded normalization and NorMuon at gradient scales far
+    # from 1 (two steps, so the momentum term enters).
+    dt = compute
+    run_steps((192, 320), 2, dt, dt, compute, steps=2, normuon=True, model_copy=True, cfg_id=42, gscale=gscale)
+
+
+def test_normuon_normalize_bf16_in_place():
+    # bf16 o normalized in place: each element within one bf16 ulp of the
+    # oracle's value rounded to bf16 (the kernel forms rho d_r o in fp32 and
+    # rounds once); the fp32 variance within 1e-5.  cols = 37 leaves a ragged
+    # row end.
+    torch = torch_cuda()
+    for n, rows, cols in ((3, 96, 200), (2, 40, 37)):
+        o64 = synth.gaussian((n, rows, cols), (43, rows, 0, 1, 0), "f32").astype(np.float64)
+        o64 *= np.linspace(0.25, 4.0, rows)[None, :, None]
+        ob = synth.store(o64, "bf16")
+        v0 = (np.abs(synth.gaussian((n, rows), (43, rows, 1, 1, 0), "f32")) * 0.01).astype(np.float32)
+        ot = to_dev(ob, "bf16")
+        vt = to_dev(v0, "f32")
+        ns.normuon_normalize(ot, vt, beta2=0.95, eps=1e-8)
+        torch.cuda.synchronize()
+        got = to_f64(ot)
+        gv = to_f64(vt)
+        for i in range(n):
+            ref, rv = oracle.normuon(synth.bf16_bits_to_f64(ob[i]), v0[i].astype(np.float64), 0.95, 1e-8)
+            assert bf16_ulp_diff(got[i], ref).max() <= 1, (n, rows, cols, i)
+            assert rel_fro(gv[i], rv) <= 1e-5
+
+
+def test_muon_ns5_channels_last_conv_weights():
+    # Conv weights stored channels_last (not row-major contiguous), fp32 and
+    # bf16: MuonNS5 steps them through contiguous buffers and writes the
+    # results back into the parameters; bitwise equal to the same weights
+    # stored contiguous, and the update against the oracle.
+    torch = torch_cuda()
+    shape = (64, 32, 3, 3)
+    for dt in (torch.float32, torch.bfloat16):
+        w0 = synth.gaussian(shape, (44, 0, 0, 0, synth.ROLE_WEIGHT), "f32", std=0.02)
+        plain = torch.nn.Parameter(to_dev(w0, "f32").to(dt))
+        cl = torch.nn.Parameter(to_dev(w0, "f32").to(dt).contiguous(memory_format=torch.channels_last))
+        assert not cl.is_contiguous()
+        opt_p = ns.MuonNS5([plain], lr=0.05, normuon=True)
+        opt_c = ns.MuonNS5([cl], lr=0.05, normuon=True)
+        mdt = "bf16" if dt == torch.bfloat16 else "f32"
+        master = opt_p.state[id(plain)]["master"]
+        ostate = {"w": to_f64(master).reshape(64, -1), "m": np.zeros((64, 288)), "v": np.zeros(64)}
+        hp = oracle.MuonHParams(lr=0.05, normuon=True, mom_dtype=mdt)
+        for step in (1, 2):
+            g = synth.power_law((64, 288), (44, 0, 1), (44, 0, 1, step), "bf16").reshape(shape)
+            plain.grad = to_dev(g, "bf16").to(dt)
+            cl.grad = plain.grad.clone().contiguous(memory_format=torch.channels_last)
+            start = cl.data.clone()
+            before = to_f64(master).reshape(64, -1)
+            opt_p.step()
+            opt_c.step()
+            torch.cuda.synchronize()
+            assert torch.equal(plain.data, cl.data), (dt, step)
+            assert torch.equal(master, opt_c.state[id(cl)]["master"]), (dt, step)
+            assert not torch.equal(cl.data, start), (dt, step)
+            r = oracle.muon_step(ostate["w"], storage_f64(g, "bf16").reshape(64, -1), ostate["m"], ostate["v"], hp)
+            after = to_f64(master).reshape(64, -1)
+            assert rel_fro(after - before, r["w"] - ostate["w"]) <= TOL["bf16"], (dt, step)
+            ostate.update(w=r["w"], m=r["m"], v=r["v"])
 
 
 def test_empty_group_is_noop():
