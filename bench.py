@@ -34,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 MFMA (published)
 METRIC = "NS5 orthogonalizations/sec + TFLOP/s (% bf16 MFMA peak) at Llama-8B shapes"
 LAYER = (("q", (4096, 4096)), ("k", (1024, 4096)), ("v", (1024, 4096)), ("o", (4096, 4096)),
          ("gate", (14336, 4096)), ("up", (14336, 4096)), ("down", (4096, 14336)))
@@ -51,19 +52,31 @@ def make_layer_inputs():
     drawn once per shape (key: workload, layer, index of the first matrix of
     that shape); each matrix has its own noise (key: workload, layer, index,
     step 1)."""
+    import concurrent.futures as cf
     import synth
     grads, weights = {}, {}
     index = {name: i for i, (name, _) in enumerate(LAYER)}
-    for shape, names in groups_of_layer():
+
+    def one_shape(item):
+        # The shapes are independent draws (their own keys), so they are made
+        # in parallel threads (numpy's QR and matmul release the GIL); the
+        # values do not depend on the order.
+        shape, names = item
         t = time.perf_counter()
         first = index[names[0]]
         gs = synth.power_law_many(shape, (WORKLOAD_ID, 0, first),
                                   [(WORKLOAD_ID, 0, index[n], 1) for n in names], "bf16")
-        for n, g in zip(names, gs):
-            grads[n] = g
-            weights[n] = synth.gaussian(shape, (WORKLOAD_ID, 0, index[n], 0, synth.ROLE_WEIGHT), "f32", std=0.02)
+        ws = [synth.gaussian(shape, (WORKLOAD_ID, 0, index[n], 0, synth.ROLE_WEIGHT), "f32", std=0.02)
+              for n in names]
         print(f"[bench] generated {'+'.join(names)} {shape} in {time.perf_counter() - t:.1f} s",
               file=sys.stderr, flush=True)
+        return names, gs, ws
+
+    with cf.ThreadPoolExecutor(max_workers=4) as ex:
+        for names, gs, ws in ex.map(one_shape, groups_of_layer()):
+            for n, g, w in zip(names, gs, ws):
+                grads[n] = g
+                weights[n] = w
     return grads, weights
 
 
@@ -99,16 +112,39 @@ def groups_of_layer():
     return [(shape, by_shape[shape]) for shape in order]
 
 
-def cpu_baseline(grads, weights, target_seconds=20.0):
-    """The oracle as it stands, on q, k and v of the layer (3 of 7 matrices),
-    scaled by dense float64 NS FLOPs to the whole layer."""
-    import oracle
-    import synth
+def host_info():
+    """What the CPU baseline ran on: the host's logical CPUs, its CPU model and
+    the BLAS threads numpy uses."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         threads = os.cpu_count()
+    return {"cpu_count": os.cpu_count(), "cpu_model": model, "blas_threads": int(threads)}
+
+
+def step_stats(ms):
+    """Median, min, p90 and mean of per-step times (ms)."""
+    a = np.sort(np.asarray(ms, dtype=np.float64))
+    return {"reps": int(a.size), "median": round(float(np.median(a)), 4), "min": round(float(a[0]), 4),
+            "p90": round(float(np.percentile(a, 90)), 4), "mean": round(float(a.mean()), 4)}
+
+
+def cpu_baseline(grads, weights, target_seconds=20.0):
+    """The oracle as it stands, on q, k and v of the layer (3 of 7 matrices),
+    scaled by dense float64 NS FLOPs to the whole layer."""
+    import oracle
+    import synth
+    host = host_info()
     hp = oracle.MuonHParams(lr=0.05, normuon=True, mom_dtype="bf16")
 
     def dense(rows, cols):
@@ -129,8 +165,8 @@ def cpu_baseline(grads, weights, target_seconds=20.0):
     f_sample = sum(dense(*dict(LAYER)[n]) for n in done)
     f_layer = sum(dense(*s) for _, s in LAYER)
     layer_seconds = dt * f_layer / f_sample
-    return {"value": round(len(LAYER) / layer_seconds, 6), "unit": "orth/s", "cores": int(threads),
-            "kind": "oracle",
+    return {"value": round(len(LAYER) / layer_seconds, 6), "unit": "orth/s", "cores": host["blas_threads"],
+            "kind": "oracle", **host,
             "sample": f"float64 numpy oracle, one Muon/NorMuon step of {'+'.join(done)} "
                       f"({dt:.1f} s), scaled by dense NS FLOPs ({f_sample:.3e} of {f_layer:.3e}) to the 7-matrix layer"}
 
@@ -182,20 +218,22 @@ def capture(step_fn):
 
 
 def event_time(fn, steps, warmup):
-    """Milliseconds per call of fn, from HIP events on the current stream."""
+    """Milliseconds per call of fn (the mean over `steps` calls) and the
+    per-call times, from HIP events recorded on the current stream between
+    consecutive calls."""
     import torch
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(steps):
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record(stream)
+    for i in range(steps):
         fn()
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1) / steps
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return evs[0].elapsed_time(evs[-1]) / steps, per
 
 
 def timed_steps(step_fn, steps, warmup):
@@ -207,9 +245,9 @@ def timed_steps(step_fn, steps, warmup):
     (graph, eager) and the per-class launch totals of the third run."""
     import torch
     import newton_schulz_ns5_amd as ns
-    ms_eager = event_time(step_fn, steps, warmup)
+    ms_eager, _ = event_time(step_fn, steps, warmup)
     replay = capture(step_fn)
-    ms = event_time(replay, steps, warmup)
+    ms, per = event_time(replay, steps, warmup)
     ns.profile_reset()
     ns.profile_enable(True)
     # A spin kernel of ~0.1 s keeps the GPU busy while the host enqueues the
@@ -220,7 +258,7 @@ def timed_steps(step_fn, steps, warmup):
         step_fn()
     torch.cuda.synchronize()
     ns.profile_enable(False)
-    return ms, ms_eager, {k: ns.profile_query(k) for k in ns.KERNEL_CLASSES}
+    return ms, ms_eager, per, {k: ns.profile_query(k) for k in ns.KERNEL_CLASSES}
 
 
 def class_table(prof):
@@ -242,11 +280,11 @@ def class_table(prof):
 
 
 def side_workload(args, dev):
-    """The per-head and conv-megabatch workloads: one JSON line in the same
-    format as the layer workload.  Their Newton-Schulz GEMMs have m = 128..512,
-    so the roofline names the GEMM class with the largest share of time and
-    takes HBM as its bound when its algorithmic FLOP per byte is below the
-    ridge (2516.6 TFLOP/s over 8 TB/s)."""
+    """The per-head, conv-megabatch and fp32 256 x 256 workloads: one JSON line
+    in the same format as the layer workload.  Their Newton-Schulz GEMMs have
+    m = 128..512, so the roofline names the GEMM class with the largest share
+    of time and takes HBM as its bound when its algorithmic FLOP per byte is
+    below the ridge (the MFMA peak of the compute dtype over 8 TB/s)."""
     import ctypes
     import torch
     import newton_schulz_ns5_amd as ns
@@ -254,7 +292,42 @@ def side_workload(args, dev):
     import synth
     L = ns.lib()
     sptr = lambda: ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    if args.workload == "heads":
+    compute = "bf16"
+    if args.workload == "c1":
+        # One 256 x 256 fp32 N(0,1) gradient, fp32 master and momentum; one
+        # Muon step in fp32 compute mode (momentum 0.95 Nesterov, lr 0.05, five
+        # quintic iterations, eps 1e-7 on the norm), no NorMuon.
+        compute = "f32"
+        shape = (256, 256)
+        g = synth.gaussian(shape, (1, 0, 0, 1, synth.ROLE_GRAD), "f32")
+        w = synth.gaussian(shape, (1, 0, 0, 0, synth.ROLE_WEIGHT), "f32", std=0.02)
+        G = [torch.from_numpy(g).to(dev)]
+        W = [torch.from_numpy(w).to(dev)]
+        M = [torch.zeros(shape, dtype=torch.float32, device=dev)]
+        group, keep = ns._make_group(W, G, M, None, None, heads=1)
+        hp = ns.hparams(lr=0.05, momentum=0.95, nesterov=True, normuon=False,
+                        ns=ns.ns_config(compute_dtype="f32"))
+        garr = (ns.Group * 1)(group)
+        ws = torch.empty(max(ns.step_groups_workspace_bytes([group], hp), 256), dtype=torch.uint8, device=dev)
+
+        def step_fn():
+            rc = L.muon_step_groups(garr, 1, ctypes.byref(hp), ctypes.c_void_p(ws.data_ptr()), ws.numel(), sptr())
+            if rc != 0:
+                raise RuntimeError(f"muon_step_groups failed: {rc} {L.muon_last_error()}")
+        shapes = [(1, 256, 256)]
+        workload = "single-256x256-fp32-muon-step"
+        extra = {"normuon": False, "step": "full Muon step, fp32 compute (fp32 MFMA)",
+                 "grad": "256x256 fp32 N(0,1)"}
+
+        def cpu_leg():
+            t0, done = time.perf_counter(), 0
+            ohp = oracle.MuonHParams(lr=0.05, normuon=False, mom_dtype="f32")
+            while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0) and done < 2000:
+                oracle.muon_step(w.astype(np.float64), g.astype(np.float64), np.zeros(shape), None, ohp)
+                done += 1
+            dt = time.perf_counter() - t0
+            return done / dt, f"float64 numpy oracle, {done} Muon steps of the 256 x 256 matrix in {dt:.1f} s"
+    elif args.workload == "heads":
         # q_proj 4096 x 4096 as 32 heads of 128 rows, k_proj 1024 x 4096 as 8; N(0,1) bf16; NS only.
         parts = []
         for i, (rows, heads) in enumerate(((4096, 32), (1024, 8))):
@@ -335,7 +408,7 @@ def side_workload(args, dev):
             return (done / dt) * f1 / fw * nm, (f"float64 numpy oracle, {done} Muon/NorMuon steps of one 256 x 1152 "
                                                 f"matrix in {dt:.1f} s, scaled by dense NS FLOPs to the workload")
 
-    ms, ms_eager, prof = timed_steps(step_fn, args.steps, args.warmup)
+    ms, ms_eager, per, prof = timed_steps(step_fn, args.steps, args.warmup)
     nmat = sum(n for n, _, _ in shapes)
     fl_L = sum(n * ns_flops(r, c)[0] for n, r, c in shapes)
     fl_E = sum(n * ns_flops(r, c)[1] for n, r, c in shapes)
@@ -345,27 +418,31 @@ def side_workload(args, dev):
     sec = d["ms"] * 1e-3
     tf = d["flop"] / sec / 1e12
     gbps = d["bytes"] / sec / 1e9
-    hbm = d["flop"] / max(d["bytes"], 1) < PEAK_BF16_TFLOPS / 8.0
+    peak = PEAK_BF16_TFLOPS if compute == "bf16" else PEAK_F32_TFLOPS
+    hbm = d["flop"] / max(d["bytes"], 1) < peak / 8.0
+    kname = "gemm_nt_bf16_kernel" if compute == "bf16" else "gemm_f32_kernel"
     out = {
         "metric": METRIC, "value": round(nmat / (ms * 1e-3), 3), "unit": "orth/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": compute, "data": "synthetic",
         "config": dict({"workload": workload, "matrices": nmat, "ns_iterations": 5,
                         "launch": "HIP graph replay of one step",
                         "ms_per_step_host_launched": round(ms_eager, 4),
-                        "ns_compute": "bf16 storage, fp32 accumulate (MFMA)",
+                        "step_ms": step_stats(per),
+                        "ns_compute": ("bf16 storage, fp32 accumulate (MFMA)" if compute == "bf16"
+                                       else "fp32 throughout (fp32 MFMA)"),
                         "params_per_s": round(sum(n * r * c for n, r, c in shapes) / (ms * 1e-3), 1),
                         "tflops_L": round(fl_L / (ms * 1e-3) / 1e12, 2),
-                        "pct_peak_L": round(100 * fl_L / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                        "pct_peak_L": round(100 * fl_L / (ms * 1e-3) / 1e12 / peak, 2),
                         "tflops_E": round(fl_E / (ms * 1e-3) / 1e12, 2),
                         "kernel_classes": per_class}, **extra),
         "roofline": {
             "bound": "hbm" if hbm else "mfma",
-            "kernel": f"{dom} GEMM class (gemm_nt_bf16_kernel)",
+            "kernel": f"{dom} GEMM class ({kname})",
             "achieved": round(gbps if hbm else tf, 2),
-            "peak": 8000.0 if hbm else PEAK_BF16_TFLOPS,
+            "peak": 8000.0 if hbm else peak,
             "unit": "GB/s" if hbm else "TFLOP/s",
-            "frac": round((gbps / 8000.0) if hbm else (tf / PEAK_BF16_TFLOPS), 4),
+            "frac": round((gbps / 8000.0) if hbm else (tf / peak), 4),
             "traffic": None,
             "tflops": round(tf, 2), "gbps": round(gbps, 1),
             "launches": d["launches"], "avg_launch_us": round(1e3 * d["ms"] / max(d["launches"], 1), 2),
@@ -374,13 +451,9 @@ def side_workload(args, dev):
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the CPU", file=sys.stderr, flush=True)
         v, desc = cpu_leg()
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-        except Exception:
-            threads = os.cpu_count()
-        out["cpu_baseline"] = {"value": round(v, 6), "unit": "orth/s", "cores": int(threads), "kind": "oracle",
-                               "sample": desc}
+        host = host_info()
+        out["cpu_baseline"] = {"value": round(v, 6), "unit": "orth/s", "cores": host["blas_threads"],
+                               "kind": "oracle", **host, "sample": desc}
     print(json.dumps(out), flush=True)
 
 
@@ -391,10 +464,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
-    ap.add_argument("--workload", choices=["layer", "heads", "conv"], default="layer",
+    ap.add_argument("--workload", choices=["layer", "heads", "conv", "c1"], default="layer",
                     help="layer: the Muon/NorMuon step of Llama-3-8B layers (the default line); heads: "
                          "per-head Newton-Schulz of q [32,128,4096] and k [8,128,4096]; conv: the NorMuon step "
-                         "of the conv megabatches [64,256,128,3,3] and [32,512,512,5]")
+                         "of the conv megabatches [64,256,128,3,3] and [32,512,512,5]; c1: the fp32-mode Muon "
+                         "step of one 256x256 fp32 gradient")
     ap.add_argument("--layers", type=int, default=1,
                     help="Llama-3-8B layers per step (1: the layer workload; 32: the whole model)")
     ap.add_argument("--print-source-digest", action="store_true",
@@ -487,17 +561,19 @@ def main():
     ns.profile_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(args.steps):
+    # One event between consecutive steps: the per-step times give the
+    # median, min and p90 beside the mean.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
         one_step()
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ns.profile_enable(False)
-    ms_total = ev0.elapsed_time(ev1)
+    ms_total = evs[0].elapsed_time(evs[-1])
     ms_per_step = ms_total / args.steps
+    per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall:.2f} s)",
           file=sys.stderr, flush=True)
 
@@ -553,6 +629,7 @@ def main():
             "ns_iterations": 5,
             "ns_compute": "bf16 storage, fp32 accumulate (MFMA)",
             "normuon": True,
+            "step_ms": step_stats(per_step),
             "tflops_L": round(tf_L, 2), "pct_peak_L": round(100 * tf_L / PEAK_BF16_TFLOPS, 2),
             "tflops_E": round(tf_E, 2), "pct_peak_E": round(100 * tf_E / PEAK_BF16_TFLOPS, 2),
             "flop_per_step_L": fl_L, "flop_per_step_E": fl_E,
