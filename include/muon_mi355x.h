@@ -162,6 +162,29 @@ int muon_ns_batched(const void* x, int32_t x_dtype, int64_t x_batch_stride, int6
                     int64_t n, int64_t rows, int64_t cols, const muon_ns_config* cfg,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Size of the scratch array muon_ns_batched_noalloc works in: 256 MiB. */
+#define MUON_NS_NOALLOC_WORKSPACE_BYTES ((size_t)256 << 20)
+
+/* muon_ns_batched without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The call allocates nothing: its
+ * workspace is a fixed array of MUON_NS_NOALLOC_WORKSPACE_BYTES in the
+ * library's device code, one copy per GPU, held from the library's load on
+ * that GPU until the process ends (the first call on a GPU looks up that
+ * GPU's copy; no allocation and no stream work).  Its contents on entry do
+ * not matter, and it keeps the last call's contents.
+ * Every call on one GPU works in that GPU's one array: calls that can run
+ * at the same time on one GPU (on different streams, or from threads whose
+ * calls are not ordered on one stream) race and give wrong results.  Calls
+ * enqueued on one stream are ordered and safe.
+ * Arguments, results and errors as for muon_ns_batched, and
+ * MUON_ERR_WORKSPACE when the problem's muon_ns_workspace_bytes exceeds
+ * MUON_NS_NOALLOC_WORKSPACE_BYTES (nothing is enqueued; a smaller
+ * cfg->max_batch lowers it). */
+int muon_ns_batched_noalloc(const void* x, int32_t x_dtype, int64_t x_batch_stride, int64_t x_row_stride,
+                            void* y, int32_t y_dtype, int64_t y_batch_stride, int64_t y_row_stride,
+                            int64_t n, int64_t rows, int64_t cols, const muon_ns_config* cfg, void* stream);
+
 /* One problem of muon_ns_groups: the arguments of one muon_ns_batched call. */
 typedef struct muon_ns_problem {
   const void* x;

@@ -11,6 +11,9 @@ Entry points (same names as the C ABI):
 * ``ns_batched(x, out=None, ...)`` -- NS5 of each matrix of a [n, rows, cols]
   (or [rows, cols]) tensor, any batch / row strides (megabatch slices, per-head
   views from ``per_head_view``);
+* ``ns_batched_noalloc(x, out=None, ...)`` -- ``ns_batched`` without a
+  workspace: the library's fixed per-GPU scratch array (for callers that
+  cannot allocate);
 * ``ns_groups(xs, outs=None, ...)`` -- ``ns_batched`` on several tensors with
   every Newton-Schulz launch shared by all of them (e.g. the per-head views of
   q_proj and k_proj of one layer);
@@ -26,7 +29,7 @@ from collections import OrderedDict
 from . import _lib
 from ._lib import MUON_BF16, MUON_F32, MuonError, NSConfig, NSProblem, Group, HParams, KERNEL_CLASSES
 
-__all__ = ["ns_batched", "ns_groups", "ns_groups_workspace_bytes", "normuon_normalize", "step_group", "step_groups", "step_groups_workspace_bytes", "MuonNS5", "per_head_view", "ns_config",
+__all__ = ["ns_batched", "ns_batched_noalloc", "NOALLOC_WORKSPACE_BYTES", "ns_groups", "ns_groups_workspace_bytes", "normuon_normalize", "step_group", "step_groups", "step_groups_workspace_bytes", "MuonNS5", "per_head_view", "ns_config",
            "hparams", "ns_workspace_bytes", "step_workspace_bytes", "normuon_workspace_bytes",
            "profile_enable", "profile_classes", "profile_reset", "profile_query", "MuonError", "QUINTIC", "abi_version",
            "state_layout_version", "lib"]
@@ -178,6 +181,32 @@ def ns_batched(x, out=None, *, steps=5, coeffs=QUINTIC, eps=1e-7, compute_dtype=
         _ptr(y3), _dt(y3), y3.stride(0), y3.stride(1),
         n, rows, cols, ctypes.byref(cfg), _ptr(ws), ws.numel(), _stream(x)))
     return out
+
+
+def ns_batched_noalloc(x, out=None, *, steps=5, coeffs=QUINTIC, eps=1e-7, compute_dtype="bf16", max_batch=0,
+                       cfg=None):
+    """ns_batched through muon_ns_batched_noalloc: no workspace argument; the
+    library works in its fixed per-GPU scratch array (at most
+    NOALLOC_WORKSPACE_BYTES of workspace).  Calls that can overlap on one GPU
+    race; calls on one stream are ordered."""
+    torch = _torch()
+    cfg = cfg if cfg is not None else ns_config(steps, coeffs, eps, compute_dtype, max_batch)
+    if out is None:
+        out = torch.empty_like(x, memory_format=torch.contiguous_format)
+    x3, y3 = _as3(x), _as3(out)
+    if x3.shape != y3.shape:
+        raise MuonError(_lib.MUON_ERR_INVALID_ARG, f"out shape {tuple(out.shape)} != x shape {tuple(x.shape)}")
+    if x3.numel() and (x3.stride(2) != 1 or y3.stride(2) != 1):
+        raise MuonError(_lib.MUON_ERR_INVALID_ARG, "x and out need unit column stride")
+    n, rows, cols = x3.shape
+    _lib.check(lib().muon_ns_batched_noalloc(
+        _ptr(x3), _dt(x3), x3.stride(0), x3.stride(1),
+        _ptr(y3), _dt(y3), y3.stride(0), y3.stride(1),
+        n, rows, cols, ctypes.byref(cfg), _stream(x)))
+    return out
+
+
+NOALLOC_WORKSPACE_BYTES = 256 << 20
 
 
 def _ns_problems(xs, outs):

@@ -66,6 +66,8 @@ SIGNATURES = {
     "muon_ns_workspace_bytes": (c_i32, [c_i64, c_i64, c_i64, ctypes.POINTER(NSConfig), ctypes.POINTER(c_sz)]),
     "muon_ns_batched": (c_i32, [c_vp, c_i32, c_i64, c_i64, c_vp, c_i32, c_i64, c_i64, c_i64, c_i64, c_i64,
                                 ctypes.POINTER(NSConfig), c_vp, c_sz, c_vp]),
+    "muon_ns_batched_noalloc": (c_i32, [c_vp, c_i32, c_i64, c_i64, c_vp, c_i32, c_i64, c_i64, c_i64, c_i64, c_i64,
+                                        ctypes.POINTER(NSConfig), c_vp]),
     "muon_ns_groups_workspace_bytes": (c_i32, [ctypes.POINTER(NSProblem), c_i64, ctypes.POINTER(NSConfig),
                                                ctypes.POINTER(c_sz)]),
     "muon_ns_groups": (c_i32, [ctypes.POINTER(NSProblem), c_i64, ctypes.POINTER(NSConfig), c_vp, c_sz, c_vp]),

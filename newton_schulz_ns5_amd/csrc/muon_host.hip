@@ -619,6 +619,44 @@ int ns_run(const muon_ns_problem* q, int64_t nq, const muon_ns_config& cfg, char
   return ok();
 }
 
+// ---- the workspace of muon_ns_batched_noalloc --------------------------------
+// A fixed array in the library's device code: every GPU the library runs on
+// holds its own copy until the process ends.  On the host, `scratch` names a
+// stand-in, not a device address; the address of each GPU's copy comes from
+// hipGetSymbolAddress with that GPU current, looked up on the first call on
+// that GPU and kept per device ordinal.
+static __device__ __align__(256) unsigned char scratch[MUON_NS_NOALLOC_WORKSPACE_BYTES];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;
+
+// Device address of the scratch array on the device that runs `s` (the
+// current device for the null stream).
+int scratch_for(hipStream_t s, char** out) {
+  int dev = -1;
+  hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "device of the stream");
+  if (dev < 0) return fail(MUON_ERR_HIP, "no device for the stream");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the scratch array");
+    if (!p || ((uintptr_t)p & 255)) return fail(MUON_ERR_HIP, "scratch array address %p is null or not 256-byte aligned", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = (char*)g_scratch_ptr[dev];
+  return MUON_OK;
+}
+
 }  // namespace
 
 // =============================================================================
@@ -695,6 +733,26 @@ int muon_ns_batched(const void* x, int32_t x_dtype, int64_t x_batch_stride, int6
   const size_t need = make_layout(make_geom(rows, cols, cfg->compute_dtype), chunk_of(n, cfg->max_batch)).total;
   if ((rc = check_workspace(workspace, workspace_bytes, need))) return rc;
   return ns_run(&q, 1, *cfg, (char*)workspace, (hipStream_t)stream);
+}
+
+int muon_ns_batched_noalloc(const void* x, int32_t x_dtype, int64_t x_batch_stride, int64_t x_row_stride,
+                            void* y, int32_t y_dtype, int64_t y_batch_stride, int64_t y_row_stride,
+                            int64_t n, int64_t rows, int64_t cols, const muon_ns_config* cfg, void* stream) {
+  const muon_ns_problem q{x, x_dtype, x_batch_stride, x_row_stride, y, y_dtype, y_batch_stride, y_row_stride,
+                          n, rows, cols};
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if ((rc = check_ns_problem(q))) return rc;
+  if (ns_empty(q)) return ok();
+  const size_t need = make_layout(make_geom(rows, cols, cfg->compute_dtype), chunk_of(n, cfg->max_batch)).total;
+  if (need > MUON_NS_NOALLOC_WORKSPACE_BYTES)
+    return fail(MUON_ERR_WORKSPACE,
+                "this problem needs %zu bytes of workspace, above the %zu-byte scratch array of "
+                "muon_ns_batched_noalloc; set cfg->max_batch lower or call muon_ns_batched with a workspace",
+                need, (size_t)MUON_NS_NOALLOC_WORKSPACE_BYTES);
+  char* ws = nullptr;
+  if ((rc = scratch_for((hipStream_t)stream, &ws))) return rc;
+  return ns_run(&q, 1, *cfg, ws, (hipStream_t)stream);
 }
 
 int muon_ns_groups_workspace_bytes(const muon_ns_problem* probs, int64_t nprob, const muon_ns_config* cfg,

@@ -150,6 +150,25 @@ def test_ns_batched_argument_errors(over, code):
     assert m.lib().muon_last_error()
 
 
+def test_ns_batched_noalloc_refuses_before_enqueue():
+    # Argument errors and a workspace beyond the scratch array are reported
+    # before the device is touched.
+    L = m.lib()
+    cfg = m.ns_config()
+
+    def call(x=FAKE, y=FAKE, n=1, rows=64, cols=64, c=cfg):
+        return L.muon_ns_batched_noalloc(ctypes.c_void_p(x), 1, rows * cols, cols, ctypes.c_void_p(y), 1, rows * cols,
+                                         cols, n, rows, cols, ctypes.byref(c) if c is not None else None, None)
+    assert call(x=0) == -1
+    assert call(c=None) == -1
+    assert call(y=FAKE + 64) == -1
+    assert call(n=0) == 0
+    assert m.ns_workspace_bytes(1, 4096, 14336, cfg) > m.NOALLOC_WORKSPACE_BYTES
+    assert call(rows=4096, cols=14336, y=FAKE + (1 << 30)) == -3
+    assert b"scratch" in L.muon_last_error()
+    assert m.NOALLOC_WORKSPACE_BYTES == 256 << 20
+
+
 def test_ns_batched_unsupported_compute_dtype():
     c = m.ns_config()
     c.compute_dtype = 5
