@@ -14,7 +14,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmuon_mi355x.so")
-SOURCES = ["gemm_bf16.hip", "gemm_f32.hip", "elementwise.hip", "poly_small.hip", "muon_host.hip"]
+SOURCES = ["gemm_bf16.hip", "gemm_f32.hip", "elementwise.hip", "poly_small.hip", "update_gram128.hip",
+           "muon_host.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-mcode-object-version=5", "-O3", "-std=c++17", "-fPIC",
@@ -24,9 +25,15 @@ FLAGS = [
 ]
 
 
+# Per-source flags.  The fused update/Gram kernel keeps two sets of MFMA
+# accumulators live; with the MFMA operands and results in ordinary VGPRs the
+# compiler does not shuttle one set between register files every sub-tile.
+EXTRA = {"update_gram128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "not a recognized feature for this target"
     err = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)

@@ -45,6 +45,44 @@ __device__ __forceinline__ void store_elem(void* base, int64_t idx, float v, boo
   else ((float*)base)[idx] = v;
 }
 
+// s_waitcnt with only a vector-memory count (expcnt and lgkmcnt left open).
+// On gfx950 the count covers vector-memory loads and stores alike, and they
+// complete in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Buffer descriptor of a byte range as four words (base address, size),
+// made explicitly wave-uniform, for the assembly loads below.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, int64_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)(uint32_t)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// One 16-byte-per-lane HBM -> LDS load issued as assembly: lane l's 16 bytes
+// from base + voff + soff land at LDS byte address lds + 16 l.  The compiler
+// does not see it as an LDS write, so it does not make later LDS reads wait
+// for every load in flight (it would before each transpose read); a kernel
+// using it orders these loads itself with explicit vmcnt waits and barriers.
+// The LDS address reaches the instruction through M0, passed as an input
+// operand bound to that register: the compiler writes M0 itself and knows
+// it is read here, so nothing the compiler keeps in M0 is overwritten.
+__device__ __forceinline__ void lds_dma16_asm(i32x4 rsrc, uint32_t lds, int voff, int soff) {
+  asm volatile("buffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "{m0}"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc),
+                 "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "memory");
+}
+
 // Launch a kernel taking one parameter block by value, 256 threads per
 // workgroup; returns the launch's own status.
 template <typename P>

@@ -42,13 +42,6 @@ constexpr int KS = 64;        // K per slice: one 128-byte line of each operand 
 constexpr int NSLOT = 5;      // LDS ring of operand slots (one operand's rows of one slice each)
 constexpr int ROWB = KS * 2;  // bytes per LDS row
 
-// s_waitcnt with only a vector-memory count (expcnt and lgkmcnt left open).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
 // Workgroup -> (problem, batch, tile row, tile col).
 //
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup w runs on
@@ -121,34 +114,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
   const int n = __builtin_amdgcn_readfirstlane((int)bytes);
   return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, n, 0x00020000);
-}
-
-// The same descriptor as four words, for the assembly loads below.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4 rsrc_words(const void* base, int64_t bytes) {
-  const uint64_t a = (uint64_t)base;
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
-  r[2] = __builtin_amdgcn_readfirstlane((int)(uint32_t)bytes);
-  r[3] = 0x00020000;
-  return r;
-}
-
-// One 16-byte-per-lane HBM -> LDS load issued as assembly: lane l's 16 bytes
-// from base + voff + soff land at LDS byte address lds + 16 l.  The compiler
-// does not see it as an LDS write, so it does not make later LDS reads wait
-// for every load in flight (it would before each transpose read); the kernel
-// orders these loads itself with explicit vmcnt waits and barriers.
-// The LDS address reaches the instruction through M0, passed as an input
-// operand bound to that register: the compiler writes M0 itself and knows
-// it is read here, so nothing the compiler keeps in M0 is overwritten.
-__device__ __forceinline__ void lds_dma16_asm(i32x4 rsrc, uint32_t lds, int voff, int soff) {
-  asm volatile("buffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "{m0}"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc),
-                 "s"(__builtin_amdgcn_readfirstlane(soff))
-               : "memory");
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));

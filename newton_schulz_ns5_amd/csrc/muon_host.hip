@@ -284,8 +284,10 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
     std::vector<GemmParams> gram, poly, upd;
     struct Sum { SplitSumParams p; int nb; double bytes; };
     struct Fused { Poly128Params p; int nb; double flop, bytes; };
+    struct UpdGram { UpdGram128Params p; int nb; double flop, bytes; };
     std::vector<Sum> sums;
     std::vector<Fused> fused;
+    std::vector<UpdGram> updgram;
     for (size_t k = 0; k < jobs.size(); ++k) {
       const NsJob& J = jobs[k];
       const Geom& g = J.g;
@@ -308,6 +310,10 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
         p.batch = (int)J.nb;
         p.flop = B * m * m * n; p.bytes = B * (m * n + m * m) * 2;
         const int ks = gram_ksplit(g);
+        // A 128-row matrix's Gram after the first iteration was computed by
+        // the previous iteration's update (update_gram128): its chunk
+        // products are already in the workspace.
+        const bool prev_fused = ks > 1 && g.mp == 128 && !first;
         if (ks > 1 && g.mp == 128) {
           // fp32 product of each K chunk, summed by the fused kernel that also
           // computes B (A is not stored)
@@ -332,7 +338,7 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
           p.ksplit = ks;
           p.bytes += B * (ks - 1) * m * m * 4;
         }
-        gram.push_back(p);
+        if (!prev_fused) gram.push_back(p);
       }
       {  // B = c A A + b A; A is stored exactly symmetric, so the b A term is
          // A^T restricted to each tile and is added inside the products
@@ -373,7 +379,22 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
           p.Mreal = (int)g.mp; p.Nreal = (int)g.np;
         }
         p.flop = B * 2 * m * m * n; p.bytes = B * (m * m + 2 * m * n) * 2;
-        upd.push_back(p);
+        const int ks = gram_ksplit(g);
+        if (ks > 1 && g.mp == 128 && !last) {
+          // Fused with the next iteration's Gram: X' to the other X buffer
+          // and the chunk products of X' X'^T to the split-K buffer.
+          UpdGram128Params u{};
+          u.B = Bm; u.b_bs = sa;
+          u.X = X[c]; u.x_bs = sx;
+          u.Y = X[c ^ 1]; u.y_bs = sx;
+          u.part = (float*)(ws + J.L.part);
+          u.np = (int)g.np; u.ksplit = ks;
+          u.alpha = 1.f; u.beta = cf.a;
+          u.rs = p.rs; u.alpha_pow = 1; u.beta_pow = 1;
+          updgram.push_back({u, (int)J.nb, B * 3 * m * m * n, B * ((m * m + 2 * m * n) * 2 + ks * m * m * 4)});
+        } else {
+          upd.push_back(p);
+        }
       }
     }
     hipError_t e;
@@ -395,6 +416,18 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
     }
     if ((e = launch_phase(poly, true, false, MUON_K_POLY, s)) != hipSuccess) return e;
     if ((e = launch_phase(upd, false, true, MUON_K_UPDATE, s)) != hipSuccess) return e;
+    for (size_t i0 = 0; i0 < updgram.size(); i0 += kMaxUpdGram128) {
+      UpdGram128Group ug{};
+      double flop = 0, bytes = 0;
+      for (size_t i = i0; i < updgram.size() && i < i0 + kMaxUpdGram128; ++i) {
+        ug.prob[ug.nprob] = updgram[i].p;
+        ug.start[ug.nprob + 1] = ug.start[ug.nprob] + updgram[i].nb * updgram[i].p.ksplit;
+        ++ug.nprob;
+        flop += updgram[i].flop;
+        bytes += updgram[i].bytes;
+      }
+      if ((e = run(MUON_K_UPDATE, flop, bytes, s, [&]() { return launch_updgram128(ug, s); })) != hipSuccess) return e;
+    }
     for (auto& c : cur) c ^= 1;
   }
   return hipSuccess;

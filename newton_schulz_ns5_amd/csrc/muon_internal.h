@@ -144,6 +144,30 @@ struct Poly128Group {
   int32_t nprob;
 };
 hipError_t launch_poly128(const Poly128Group& g, hipStream_t s);
+// ---- update fused with the next Gram's chunk products, 128-row matrices -----
+// Y[b] = alpha_b B[b] X[b] + beta_b X[b] (bf16, [128][np] row-major; alpha_b
+// = alpha rs[b]^alpha_pow, beta_b = beta rs[b]^beta_pow, rs may be null) and,
+// when part is not null, part[b * ksplit + c] = Y_c Y_c^T (fp32 [128][128],
+// exactly symmetric) over the columns of chunk c, whose edges are those of the
+// split-K Gram (128 * floor(c * (np / 128) / ksplit)).  B is exactly symmetric.
+struct UpdGram128Params {
+  const void* B; int64_t b_bs;       // [128][128] bf16, row stride 128
+  const void* X; int64_t x_bs;       // [128][np] bf16, row stride np
+  void* Y; int64_t y_bs;             // [128][np] bf16, row stride np
+  float* part;                       // [nb * ksplit][128][128] fp32, or null
+  int32_t np, ksplit;                // np a multiple of 128; 1 <= ksplit <= np / 128
+  float alpha, beta;
+  const float* rs; int32_t alpha_pow, beta_pow;
+};
+// Up to kMaxUpdGram128 such problems in one launch; problem i owns workgroups
+// start[i] .. start[i + 1] - 1 (nb_i * ksplit_i, one per matrix and chunk).
+constexpr int kMaxUpdGram128 = 8;
+struct UpdGram128Group {
+  UpdGram128Params prob[kMaxUpdGram128];
+  int32_t start[kMaxUpdGram128 + 1];
+  int32_t nprob;
+};
+hipError_t launch_updgram128(const UpdGram128Group& g, hipStream_t s);
 hipError_t launch_rowstat(const RowStatParams& p, int nb, hipStream_t s);
 hipError_t launch_rho(const RhoParams& p, int nb, hipStream_t s);
 hipError_t launch_apply(const ApplyParams& p, int nb, hipStream_t s);
