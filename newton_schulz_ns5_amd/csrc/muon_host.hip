@@ -209,10 +209,11 @@ struct FinalOut {
   int64_t ldc, sC;
 };
 
-// One fp32-compute GEMM launch (64 x 64 tiles).
+// One fp32-compute GEMM launch.
 hipError_t gemm_f32(GemmParams& p, bool nn, bool syrk, int cls, double flop, double bytes, hipStream_t s) {
-  p.tiles_m = p.M / 64;
-  p.tiles_n = p.N / 64;
+  const int t = gemm_f32_tile();
+  p.tiles_m = p.M / t;
+  p.tiles_n = p.N / t;
   p.tiles_per_batch = syrk ? p.tiles_m * (p.tiles_m + 1) / 2 : p.tiles_m * p.tiles_n;
   return run(cls, flop, bytes, s, [&]() { return launch_gemm_f32(p, nn, syrk, s); });
 }

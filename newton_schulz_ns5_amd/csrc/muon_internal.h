@@ -132,6 +132,7 @@ struct ApplyParams {
 // bf16: symmetric NT products (syrk) or NN products (nn), exactly one of the two.
 hipError_t launch_gemm_bf16(const GemmGroup& g, bool syrk, bool nn, int tile, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmParams& p, bool nn, bool syrk, hipStream_t s);
+int gemm_f32_tile();    // output tile edge of the fp32 GEMM (divides kPadF32)
 hipError_t launch_prep(const PrepParams& p, int nb, hipStream_t s);
 hipError_t launch_norm(const NormParams& p, int nb, hipStream_t s);
 hipError_t launch_split_sum(const SplitSumParams& p, int nb, hipStream_t s);
