@@ -236,7 +236,19 @@ def event_time(fn, steps, warmup):
     return evs[0].elapsed_time(evs[-1]) / steps, per
 
 
-def timed_steps(step_fn, steps, warmup):
+def calibration_pass(mib, dev):
+    """Known HBM traffic for calibrating the counters: a fill writes exactly
+    `mib` MiB, a sum over the same buffer reads them once."""
+    import torch
+    cal = torch.empty(mib << 19, dtype=torch.int16, device=dev)
+    torch.cuda.synchronize()
+    cal.fill_(1)
+    total = cal.sum()
+    torch.cuda.synchronize()
+    del cal, total
+
+
+def timed_steps(step_fn, steps, warmup, eager_only=False):
     """Time `steps` steps replayed from a HIP graph and `steps` steps launched
     from the host, then run `steps` more with the library's per-launch events
     on.  These steps are dozens of launches of a few microseconds each, so
@@ -245,9 +257,12 @@ def timed_steps(step_fn, steps, warmup):
     (graph, eager) and the per-class launch totals of the third run."""
     import torch
     import newton_schulz_ns5_amd as ns
-    ms_eager, _ = event_time(step_fn, steps, warmup)
-    replay = capture(step_fn)
-    ms, per = event_time(replay, steps, warmup)
+    ms_eager, per_eager = event_time(step_fn, steps, warmup)
+    if eager_only:
+        ms, per = ms_eager, per_eager
+    else:
+        replay = capture(step_fn)
+        ms, per = event_time(replay, steps, warmup)
     ns.profile_reset()
     ns.profile_enable(True)
     # A spin kernel of ~0.1 s keeps the GPU busy while the host enqueues the
@@ -408,7 +423,9 @@ def side_workload(args, dev):
             return (done / dt) * f1 / fw * nm, (f"float64 numpy oracle, {done} Muon/NorMuon steps of one 256 x 1152 "
                                                 f"matrix in {dt:.1f} s, scaled by dense NS FLOPs to the workload")
 
-    ms, ms_eager, per, prof = timed_steps(step_fn, args.steps, args.warmup)
+    if args.copy_calibration_mib > 0:
+        calibration_pass(args.copy_calibration_mib, dev)
+    ms, ms_eager, per, prof = timed_steps(step_fn, args.steps, args.warmup, args.eager_only)
     nmat = sum(n for n, _, _ in shapes)
     fl_L = sum(n * ns_flops(r, c)[0] for n, r, c in shapes)
     fl_E = sum(n * ns_flops(r, c)[1] for n, r, c in shapes)
@@ -426,7 +443,8 @@ def side_workload(args, dev):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": compute, "data": "synthetic",
         "config": dict({"workload": workload, "matrices": nmat, "ns_iterations": 5,
-                        "launch": "HIP graph replay of one step",
+                        "launch": ("host-launched steps (--eager-only)" if args.eager_only
+                                   else "HIP graph replay of one step"),
                         "ms_per_step_host_launched": round(ms_eager, 4),
                         "step_ms": step_stats(per),
                         "ns_compute": ("bf16 storage, fp32 accumulate (MFMA)" if compute == "bf16"
@@ -473,6 +491,8 @@ def main():
                     help="Llama-3-8B layers per step (1: the layer workload; 32: the whole model)")
     ap.add_argument("--print-source-digest", action="store_true",
                     help="print the digest of the HIP sources that profiles/traffic.json is keyed on, and exit")
+    ap.add_argument("--eager-only", action="store_true",
+                    help="side workloads: time host-launched steps only (no HIP graph), e.g. for counter passes")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the steps, fill and then sum a buffer of this many MiB (known bytes written "
                          "and read, for calibrating HBM traffic counters)")
@@ -540,14 +560,7 @@ def main():
             raise RuntimeError(f"muon_step_groups failed: {rc} {L.muon_last_error()}")
 
     if args.copy_calibration_mib > 0:
-        # Known traffic for counter calibration: a fill writes exactly this many
-        # MiB, a sum over the same buffer reads them once.
-        cal = torch.empty(args.copy_calibration_mib << 19, dtype=torch.int16, device=dev)
-        torch.cuda.synchronize()
-        cal.fill_(1)
-        total = cal.sum()
-        torch.cuda.synchronize()
-        del cal, total
+        calibration_pass(args.copy_calibration_mib, dev)
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
