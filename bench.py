@@ -437,7 +437,13 @@ def side_workload(args, dev):
     gbps = d["bytes"] / sec / 1e9
     peak = PEAK_BF16_TFLOPS if compute == "bf16" else PEAK_F32_TFLOPS
     hbm = d["flop"] / max(d["bytes"], 1) < peak / 8.0
-    kname = "gemm_nt_bf16_kernel" if compute == "bf16" else "gemm_f32_kernel"
+    if compute == "f32":
+        kname = "gemm_f32_kernel"
+    elif args.workload == "heads" and dom == "update":
+        kname = ("updgram128_kernel: the update fused with the next iteration's Gram, iterations 1-4; "
+                 "gemm_nt_bf16_kernel<128, false, true>: the last iteration")
+    else:
+        kname = "gemm_nt_bf16_kernel"
     out = {
         "metric": METRIC, "value": round(nmat / (ms * 1e-3), 3), "unit": "orth/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
