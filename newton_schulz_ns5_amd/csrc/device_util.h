@@ -83,12 +83,12 @@ __device__ __forceinline__ void lds_dma16_asm(i32x4 rsrc, uint32_t lds, int voff
                : "memory");
 }
 
-// Launch a kernel taking one parameter block by value, 256 threads per
-// workgroup; returns the launch's own status.
+// Launch a kernel taking one parameter block by value, `threads` (256 unless
+// given) threads per workgroup; returns the launch's own status.
 template <typename P>
-inline hipError_t launch_kernel(void (*kernel)(const P), dim3 grid, const P& p, hipStream_t s) {
+inline hipError_t launch_kernel(void (*kernel)(const P), dim3 grid, const P& p, hipStream_t s, int threads = 256) {
   void* args[] = {const_cast<P*>(&p)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, dim3(256), args, 0, s);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, dim3(threads), args, 0, s);
 }
 
 }  // namespace muon

@@ -277,6 +277,31 @@ Coeffs coeffs_of(const muon_ns_config& cfg, int it) {
 // bf16 mode: Gram and poly are symmetric NT products, the update is NN and
 // reads X row-major.  X ping-pongs between two buffers; the last update
 // writes the output in parameter orientation instead.
+// A problem of the fused 128-row kernel with its batch and modelled cost.
+struct UpdGram { UpdGram128Params p; int nb; double flop, bytes; };
+
+// Launches of the fused 128-row kernel over `v`, kMaxUpdGram128 problems at a
+// time: the update (with the next Gram when the problems have `part`), or the
+// Gram only (`gram_only`).
+hipError_t launch_updgram_groups(const std::vector<UpdGram>& v, int kclass, bool gram_only, hipStream_t s) {
+  for (size_t i0 = 0; i0 < v.size(); i0 += kMaxUpdGram128) {
+    UpdGram128Group ug{};
+    double flop = 0, bytes = 0;
+    for (size_t i = i0; i < v.size() && i < i0 + kMaxUpdGram128; ++i) {
+      ug.prob[ug.nprob] = v[i].p;
+      ug.start[ug.nprob + 1] = ug.start[ug.nprob] + v[i].nb * v[i].p.ksplit;
+      ++ug.nprob;
+      flop += v[i].flop;
+      bytes += v[i].bytes;
+    }
+    const hipError_t e = run(kclass, flop, bytes, s, [&]() {
+      return gram_only ? launch_gram128(ug, s) : launch_updgram128(ug, s);
+    });
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_config& cfg, hipStream_t s) {
   std::vector<int> cur(jobs.size(), 0);
   for (int it = 0; it < cfg.steps; ++it) {
@@ -285,10 +310,9 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
     std::vector<GemmParams> gram, poly, upd;
     struct Sum { SplitSumParams p; int nb; double bytes; };
     struct Fused { Poly128Params p; int nb; double flop, bytes; };
-    struct UpdGram { UpdGram128Params p; int nb; double flop, bytes; };
     std::vector<Sum> sums;
     std::vector<Fused> fused;
-    std::vector<UpdGram> updgram;
+    std::vector<UpdGram> updgram, gram128;
     for (size_t k = 0; k < jobs.size(); ++k) {
       const NsJob& J = jobs[k];
       const Geom& g = J.g;
@@ -321,6 +345,11 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
           Poly128Params q{};
           q.part = (const float*)(ws + J.L.part); q.ksplit = ks;
           q.rs = p.rs;
+          if (first) {  // the norm is finalized here (norm_finalize skipped it)
+            q.rs = nullptr;
+            q.nsum = (const float*)(ws + J.L.partial); q.ntiles = J.L.tiles;
+            q.eps = cfg.eps; q.rs_out = (float*)(ws + J.L.rs);
+          }
           q.b = cf.b; q.c = cf.c;
           q.B = Bm; q.ldb = g.mp; q.b_bs = sa;
           fused.push_back({q, (int)J.nb, B * m * m * m, B * (ks * m * m * 4 + m * m * 2)});
@@ -339,7 +368,17 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
           p.ksplit = ks;
           p.bytes += B * (ks - 1) * m * m * 4;
         }
-        if (!prev_fused) gram.push_back(p);
+        if (ks > 1 && g.mp == 128 && first) {
+          // The first Gram of a 128-row matrix: chunk products straight from
+          // X by the Gram-only variant of the fused kernel (same chunks).
+          UpdGram128Params u{};
+          u.X = X[c]; u.x_bs = sx;
+          u.part = (float*)(ws + J.L.part);
+          u.np = (int)g.np; u.ksplit = ks;
+          gram128.push_back({u, (int)J.nb, p.flop, B * (m * n * 2 + ks * m * m * 4)});
+        } else if (!prev_fused) {
+          gram.push_back(p);
+        }
       }
       {  // B = c A A + b A; A is stored exactly symmetric, so the b A term is
          // A^T restricted to each tile and is added inside the products
@@ -400,6 +439,7 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
     }
     hipError_t e;
     if ((e = launch_phase(gram, true, false, MUON_K_GRAM, s)) != hipSuccess) return e;
+    if ((e = launch_updgram_groups(gram128, MUON_K_GRAM, true, s)) != hipSuccess) return e;
     for (const Sum& u : sums)
       if ((e = run(MUON_K_GRAM, 0, u.bytes, s, [&]() { return launch_split_sum(u.p, u.nb, s); })) != hipSuccess)
         return e;
@@ -417,18 +457,7 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
     }
     if ((e = launch_phase(poly, true, false, MUON_K_POLY, s)) != hipSuccess) return e;
     if ((e = launch_phase(upd, false, true, MUON_K_UPDATE, s)) != hipSuccess) return e;
-    for (size_t i0 = 0; i0 < updgram.size(); i0 += kMaxUpdGram128) {
-      UpdGram128Group ug{};
-      double flop = 0, bytes = 0;
-      for (size_t i = i0; i < updgram.size() && i < i0 + kMaxUpdGram128; ++i) {
-        ug.prob[ug.nprob] = updgram[i].p;
-        ug.start[ug.nprob + 1] = ug.start[ug.nprob] + updgram[i].nb * updgram[i].p.ksplit;
-        ++ug.nprob;
-        flop += updgram[i].flop;
-        bytes += updgram[i].bytes;
-      }
-      if ((e = run(MUON_K_UPDATE, flop, bytes, s, [&]() { return launch_updgram128(ug, s); })) != hipSuccess) return e;
-    }
+    if ((e = launch_updgram_groups(updgram, MUON_K_UPDATE, false, s)) != hipSuccess) return e;
     for (auto& c : cur) c ^= 1;
   }
   return hipSuccess;
@@ -510,6 +539,9 @@ hipError_t ns_iterations(const std::vector<NsJob>& jobs, const muon_ns_config& c
 }
 
 hipError_t norm_finalize(const Geom& g, int64_t nb, float eps, char* ws, const Layout& L, hipStream_t s) {
+  // A 128-row matrix with a split Gram has its norm finalized by the first
+  // iteration's sum-and-polynomial kernel, which is the first to need it.
+  if (g.mp == 128 && gram_ksplit(g) > 1) return hipSuccess;
   NormParams np{};
   np.partial = (const float*)(ws + L.partial);
   np.tiles = L.tiles;

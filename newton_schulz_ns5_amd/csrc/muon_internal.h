@@ -94,11 +94,16 @@ struct SplitSumParams {
 // B[b] = bf16(c A A + b A) with A = bf16(rs[b]^2 * sum_s part[b][s]) (rs may
 // be null: factor 1); one workgroup per matrix.
 constexpr int kMaxKsplit = 16;   // K chunks of a split Gram, at most
+// With nsum set (the first iteration), the workgroup of matrix b first
+// computes rs[b] itself from the matrix's ntiles Frobenius-norm partials,
+// exactly as the norm finalize does, uses it and stores it to rs_out[b] for
+// the iteration's update; rs is then unused.
 struct Poly128Params {
   const float* part; int32_t ksplit;
   const float* rs;
   float b, c;
   void* B; int64_t ldb; int64_t b_bs;
+  const float* nsum; int32_t ntiles; float eps; float* rs_out;
 };
 
 // ---- NorMuon statistics ---------------------------------------------------
@@ -169,6 +174,9 @@ struct UpdGram128Group {
   int32_t nprob;
 };
 hipError_t launch_updgram128(const UpdGram128Group& g, hipStream_t s);
+// The chunk products of X X^T alone (the first iteration's Gram), chunked as
+// above; only X, x_bs, part, np and ksplit are used.
+hipError_t launch_gram128(const UpdGram128Group& g, hipStream_t s);
 hipError_t launch_rowstat(const RowStatParams& p, int nb, hipStream_t s);
 hipError_t launch_rho(const RhoParams& p, int nb, hipStream_t s);
 hipError_t launch_apply(const ApplyParams& p, int nb, hipStream_t s);

@@ -24,8 +24,11 @@
 //      (fp32) and finally stores it exactly symmetric (the upper triangle and
 //      its mirror, straight from the accumulators) as chunk c of the split-K
 //      product the next iteration's sum-and-polynomial kernel reads.
-// Every LDS address a lane uses is fixed up front, so the loop issues its
-// LDS accesses with immediate offsets.
+// The same kernel without steps 2-3 computes the first iteration's chunk
+// products from X itself, and without step 4 an update alone.
+// Eight waves (two per SIMD) share each sub-tile's products, so one wave's
+// MFMAs run while the other waits on LDS.  Every LDS address a lane uses is
+// fixed up front, so the loop issues its LDS accesses with immediate offsets.
 // The chunk edges are the split-K Gram's, multiples of 128 that depend on the
 // matrix shape only, and every sub-tile is computed by the same instruction
 // sequence, so a matrix's result does not depend on its batch.
@@ -59,12 +62,18 @@ static_assert(LDS_BYTES <= 160 * 1024, "LDS of one workgroup");
 //  - X sub-tile: row k (a K index of the update) at XROWB k, its eight
 //    32-byte blocks (16 columns each) XOR-swizzled by 2 (k mod 4), so a
 //    transpose read of 32 lanes covers every bank once.
-template <bool GRAM>
-__global__ __launch_bounds__(256, 1) void updgram128_kernel(const UpdGram128Group grp) {
+// MODE: kUpdGram (update, then the next Gram's chunk products), kUpdOnly
+// (update only) or kGramOnly (the chunk products of X itself: the first
+// iteration's Gram; B, Y, alpha and beta are unused).
+enum { kUpdGram = 0, kUpdOnly = 1, kGramOnly = 2 };
+
+template <int MODE>
+__global__ __launch_bounds__(512, 1) void updgram128_kernel(const UpdGram128Group grp) {
+  constexpr bool UPD = MODE != kGramOnly, GRAM = MODE != kUpdOnly;
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wa = wave >> 1, wb = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7, two per SIMD
+  const int wa = wave >> 1, wb = wave & 1;                     // wa 0..3: a 32-wide block row
 
   int pi = 0;
   while (pi + 1 < grp.nprob && (int)blockIdx.x >= grp.start[pi + 1]) ++pi;
@@ -95,26 +104,41 @@ __global__ __launch_bounds__(256, 1) void updgram128_kernel(const UpdGram128Grou
   const float alpha = p.alpha * (p.alpha_pow == 2 ? rsb * rsb : (p.alpha_pow == 1 ? rsb : 1.f));
   const float beta = p.beta * (p.beta_pow == 1 ? rsb : 1.f);
 
-  // B: instruction q (0..7) of a wave fills rows 8 g .. 8 g + 7 (g = 4 wave +
-  // q % 4) of slice q / 4; lane l lands at row 8 g + l / 8, chunk l % 8 and
+  // B: instruction q (0..3) of a wave fills rows 8 g .. 8 g + 7 (g = 2 wave +
+  // q % 2) of slice q / 2; lane l lands at row 8 g + l / 8, chunk l % 8 and
   // therefore fetches the chunk (l % 8) ^ ((row / 2) % 8) of that row.
+  if constexpr (UPD) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int s = q >> 2, g = wave * 4 + (q & 3);
-    const int voff = (lane >> 3) * (M * 2) + ((lane & 7) ^ ((4 * g + (lane >> 4)) & 7)) * 16;
-    lds_dma16_asm(brw, Bs + (uint32_t)(s * NT_SLICE + 8 * g * 128), voff, 8 * g * (M * 2) + s * 128);
+    for (int q = 0; q < 4; ++q) {
+      const int s = q >> 1, g = wave * 2 + (q & 1);
+      const int voff = (lane >> 3) * (M * 2) + ((lane & 7) ^ ((4 * g + (lane >> 4)) & 7)) * 16;
+      lds_dma16_asm(brw, Bs + (uint32_t)(s * NT_SLICE + 8 * g * 128), voff, 8 * g * (M * 2) + s * 128);
+    }
   }
-  // X sub-tile jj: instruction q (0..7) of a wave fills rows 32 wave + 4 q ..
-  // + 3; lane l lands at row 32 wave + 4 q + l / 16, 16-byte chunk l % 16,
-  // fetching the chunk whose 32-byte block is swizzled by 2 (row % 4) =
-  // 2 (l / 16).
-  const int xvoff = (lane >> 4) * ldx * 2 + (2 * (((lane & 15) >> 1) ^ (2 * (lane >> 4))) + (lane & 1)) * 16;
+  // X sub-tile jj, update modes: instruction q (0..3) of a wave fills rows
+  // 16 wave + 4 q .. + 3; lane l lands at row 16 wave + 4 q + l / 16, 16-byte
+  // chunk l % 16, fetching the chunk whose 32-byte block is swizzled by
+  // 2 (row % 4) = 2 (l / 16).
+  // Gram only: the sub-tile goes into the NT layout (it is the Gram's operand
+  // as it stands), filled as B is: instruction q fills rows 8 g .. 8 g + 7
+  // (g = 2 wave + q % 2) of slice q / 2.
+  const int xvoff = UPD ? (lane >> 4) * ldx * 2 + (2 * (((lane & 15) >> 1) ^ (2 * (lane >> 4))) + (lane & 1)) * 16
+                        : (lane >> 3) * ldx * 2;
   auto dma_x = [&](int jj, int buf) {
     const uint32_t dst = Xs + (uint32_t)(buf * X_BYTES);
+    if constexpr (UPD) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int row = 32 * wave + 4 * q;
-      lds_dma16_asm(xrw, dst + (uint32_t)(row * XROWB), xvoff, row * ldx * 2 + jj * SUB * 2);
+      for (int q = 0; q < 4; ++q) {
+        const int row = 16 * wave + 4 * q;
+        lds_dma16_asm(xrw, dst + (uint32_t)(row * XROWB), xvoff, row * ldx * 2 + jj * SUB * 2);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int s = q >> 1, g = wave * 2 + (q & 1);
+        const int voff = xvoff + ((lane & 7) ^ ((4 * g + (lane >> 4)) & 7)) * 16;
+        lds_dma16_asm(xrw, dst + (uint32_t)(s * NT_SLICE + 8 * g * 128), voff, 8 * g * ldx * 2 + s * 128 + jj * SUB * 2);
+      }
     }
   };
 
@@ -132,18 +156,17 @@ __global__ __launch_bounds__(256, 1) void updgram128_kernel(const UpdGram128Grou
     typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
     return __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(uintptr_t)(base + ntl[kk & 3] + (kk >> 2) * NT_SLICE));
   };
-  // X^T fragment: columns n0 + l % 32 of an X sub-tile (n0 = 64 wa + 32 i),
+  // X^T fragment: columns n0 + l % 32 of an X sub-tile (n0 = 32 wa),
   // K rows 16 kk + 8 (l / 32) .. + 7, from two transpose reads.  Within each
   // 16-lane group lane l supplies row 8 (l / 32) + (l % 16) / 4 (+ 16 kk, + 4
   // for the second read) and columns 4 (l % 4) .. + 3 of the 16-column half
   // (l / 16) % 2; that row's 32-byte blocks are swizzled by 2 ((l % 16) / 4).
-  uint32_t xtl[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int blk = ((4 * wa + 2 * i + ((lane >> 4) & 1)) ^ (2 * ((lane & 15) >> 2)));
-    xtl[i] = (uint32_t)((8 * (lane >> 5) + ((lane & 15) >> 2)) * XROWB + blk * 32 + (lane & 3) * 8);
+  uint32_t xtl;
+  {
+    const int blk = ((2 * wa + ((lane >> 4) & 1)) ^ (2 * ((lane & 15) >> 2)));
+    xtl = (uint32_t)((8 * (lane >> 5) + ((lane & 15) >> 2)) * XROWB + blk * 32 + (lane & 3) * 8);
   }
-  auto xt_frag = [&](uint32_t xbase, int kk) {  // xbase: X buffer + xtl[i]
+  auto xt_frag = [&](uint32_t xbase, int kk) {  // xbase: X buffer + xtl
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(xbase + 16 * kk * XROWB));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(xbase + 16 * kk * XROWB + 4 * XROWB));
@@ -152,12 +175,13 @@ __global__ __launch_bounds__(256, 1) void updgram128_kernel(const UpdGram128Grou
   // Epilogue writes: X'(m, n .. n + 3) with m = 64 wb + 32 j + l % 32 and n =
   // 64 wa + 8 c + 4 (l / 32), c = 4 i + q, lands in slice wa of Y at row m,
   // chunk c ^ sw, byte 8 (l / 32) of the chunk.
-  uint32_t ywl[8];
+  uint32_t ywl[4];
 #pragma unroll
-  for (int c = 0; c < 8; ++c)
-    ywl[c] = Ys + (uint32_t)(wa * NT_SLICE + (64 * wb + (lane & 31)) * 128 + ((c ^ sw) << 4) + 8 * (lane >> 5));
-  // X' rows to HBM: thread -> 16-byte chunk tid % 16 of rows tid / 16 + 16 u;
-  // row (tid / 16) + 16 u has the swizzle (tid / 32) % 8 whatever u.
+  for (int q = 0; q < 4; ++q)
+    ywl[q] = Ys + (uint32_t)((wa >> 1) * NT_SLICE + (64 * wb + (lane & 31)) * 128 + (((4 * (wa & 1) + q) ^ sw) << 4) +
+                             8 * (lane >> 5));
+  // X' rows to HBM: thread -> 16-byte chunk tid % 16 of rows tid / 16 + 32 u;
+  // row (tid / 16) + 32 u has the swizzle (tid / 32) % 8 whatever u.
   const uint32_t yrd = Ys + (uint32_t)(((tid >> 3) & 1) * NT_SLICE + (tid >> 4) * 128 +
                                        (((tid & 7) ^ ((tid >> 5) & 7)) << 4));
   const int yvoff = ((tid >> 4) * ldx + (tid & 15) * 8) * 2;
@@ -187,131 +211,118 @@ __global__ __launch_bounds__(256, 1) void updgram128_kernel(const UpdGram128Grou
     }
   }
 
-  f32x16 accg[2][2];
+  f32x16 accg[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) accg[i][j][r] = 0.f;
+    for (int r = 0; r < 16; ++r) accg[j][r] = 0.f;
 
   // Pipeline.  Per wave, vector-memory operations are issued in this order:
-  // B (8), X_0 (8), X_1 (8 when nsub > 1), then per sub-tile jj: X_{jj+2}
-  // (8 when jj + 2 < nsub) and the 8 stores of X'_jj.  Sub-tile jj's loads
-  // have landed once at most the operations issued after them are pending.
+  // B (4, update modes), X_0 (4), X_1 (4 when nsub > 1), then per sub-tile
+  // jj: X_{jj+2} (4 when jj + 2 < nsub) and the 4 stores of X'_jj (update
+  // modes).  Sub-tile jj's loads have landed once at most the operations
+  // issued after them are pending.
   dma_x(0, 0);
   if (nsub > 1) dma_x(1, 1);
 #pragma unroll 1
   for (int jj = 0; jj < nsub; ++jj) {
     const int buf = jj % NXB;
-    if (jj == 0) {
-      if (nsub > 1) wait_vmcnt<8>(); else wait_vmcnt<0>();
-    } else if (jj == 1) {
-      if (nsub > 2) wait_vmcnt<16>(); else wait_vmcnt<8>();
+    if constexpr (UPD) {
+      if (jj == 0) {
+        if (nsub > 1) wait_vmcnt<4>(); else wait_vmcnt<0>();
+      } else if (jj == 1) {
+        if (nsub > 2) wait_vmcnt<8>(); else wait_vmcnt<4>();
+      } else {
+        if (jj + 1 < nsub) wait_vmcnt<12>(); else wait_vmcnt<8>();
+      }
     } else {
-      if (jj + 1 < nsub) wait_vmcnt<24>(); else wait_vmcnt<16>();
+      if (jj + 1 < nsub) wait_vmcnt<4>(); else wait_vmcnt<0>();
     }
     __syncthreads();  // X_jj (and B) visible; every wave is done with sub-tile jj - 1
     if (jj + 2 < nsub) dma_x(jj + 2, (jj + 2) % NXB);
     const uint32_t xb = Xs + (uint32_t)(buf * X_BYTES);
-    const uint32_t xa0 = xb + xtl[0], xa1 = xb + xtl[1];
+    // The Gram's operand: the X' sub-tile, or (Gram only) the X sub-tile.
+    const uint32_t gop = UPD ? Ys : xb;
 
-    // X'^T block (i, j) of wave (wa, wb): columns 64 wa + 32 i .. of X' (its
-    // rows here), rows 64 wb + 32 j .. of X' (its columns here).
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
+    if constexpr (UPD) {
+      const uint32_t xa0 = xb + xtl;
+      // X'^T block j of wave (wa, wb): columns 32 wa .. of X' (its rows here),
+      // rows 64 wb + 32 j .. of X' (its columns here).
+      f32x16 acc[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+        for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      bf16x8 xa[2], bq[2];
-      xa[0] = xt_frag(xa0, kk);
-      xa[1] = xt_frag(xa1, kk);
+      for (int kk = 0; kk < 8; ++kk) {
+        const bf16x8 xa = xt_frag(xa0, kk);
+        bf16x8 bq[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bq[j] = nt_frag(Bs + (uint32_t)((64 * wb + 32 * j) * 128), kk);
+        for (int j = 0; j < 2; ++j) bq[j] = nt_frag(Bs + (uint32_t)((64 * wb + 32 * j) * 128), kk);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], bq[j], acc[i][j], 0, 0, 0);
-      if ((kk >> 2) == wb) {  // K step 4 wb + 2 j + h meets E's diagonal for block column j
-        const int j = (kk >> 1) & 1, h = kk & 1;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], eh[h], acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], el[h], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, bq[j], acc[j], 0, 0, 0);
+        if ((kk >> 2) == wb) {  // K step 4 wb + 2 j + h meets E's diagonal for block column j
+          const int j = (kk >> 1) & 1, h = kk & 1;
+          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, eh[h], acc[j], 0, 0, 0);
+          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, el[h], acc[j], 0, 0, 0);
         }
       }
-    }
-    // Accumulator register 4 q + e of block (i, j) holds X'(m, n + e) with m =
-    // 64 wb + 32 j + l % 32 and n = 64 wa + 32 i + 8 q + 4 (l / 32): four
-    // consecutive columns per lane and q, rounded to bf16 into Y.
-    if (alpha != 1.f) {  // first iteration: alpha = 1 / (||U|| + eps)
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
+      if (alpha != 1.f) {  // first iteration: alpha = 1 / (||U|| + eps)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] *= alpha;
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
+          for (int r = 0; r < 16; ++r) acc[j][r] *= alpha;
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           u32x2 w;
-          w[0] = pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-          w[1] = pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          w[0] = pack_bf2(acc[j][4 * q], acc[j][4 * q + 1]);
+          w[1] = pack_bf2(acc[j][4 * q + 2], acc[j][4 * q + 3]);
           typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
-          *(lds_u32x2*)(uintptr_t)(ywl[4 * i + q] + 32 * j * 128) = w;
+          *(lds_u32x2*)(uintptr_t)(ywl[q] + 32 * j * 128) = w;
         }
-    __syncthreads();  // the X' sub-tile is complete in LDS
-    {
-      typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-      u32x4 yv[8];
+      __syncthreads();  // the X' sub-tile is complete in LDS
+      {
+        typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+        u32x4 yv[4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) yv[u] = *(const lds_u32x4*)(uintptr_t)(yrd + 2048 * u);
+        for (int u = 0; u < 4; ++u) yv[u] = *(const lds_u32x4*)(uintptr_t)(yrd + 4096 * u);
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        __builtin_amdgcn_raw_buffer_store_b128(yv[u], yrs, yvoff,
-                                               __builtin_amdgcn_readfirstlane(16 * u * ldx * 2 + jj * SUB * 2), 0);
+        for (int u = 0; u < 4; ++u)
+          __builtin_amdgcn_raw_buffer_store_b128(yv[u], yrs, yvoff,
+                                                 __builtin_amdgcn_readfirstlane(32 * u * ldx * 2 + jj * SUB * 2), 0);
+      }
     }
+    // Gram block j of wave (wa, wb): rows 32 wa .., columns 64 wb + 32 j ...
     if constexpr (GRAM) {
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        bf16x8 ya[2], yq[2];
+        const bf16x8 ya = nt_frag(gop + (uint32_t)((32 * wa) * 128), kk);
+        bf16x8 yq[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) ya[i] = nt_frag(Ys + (uint32_t)((64 * wa + 32 * i) * 128), kk);
+        for (int j = 0; j < 2; ++j) yq[j] = nt_frag(gop + (uint32_t)((64 * wb + 32 * j) * 128), kk);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) yq[j] = nt_frag(Ys + (uint32_t)((64 * wb + 32 * j) * 128), kk);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            accg[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ya[i], yq[j], accg[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j) accg[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ya, yq[j], accg[j], 0, 0, 0);
       }
     }
   }
   if constexpr (!GRAM) return;
 
   // The chunk's Gram product, stored exactly symmetric from the accumulators:
-  // register 4 q + e of block (i, j) holds G(R + e, C) with R = 64 wa + 32 i +
-  // 8 q + 4 (l / 32) and C = 64 wb + 32 j + l % 32.  Only values on or above
-  // the diagonal are used: G(R + e, C) itself when R + e <= C, and as its
-  // mirror G(C, R + e) when R + e < C (four consecutive columns of row C).
-  // Block (i, j) lies wholly above the diagonal when its first row block
-  // index 2 wa + i is below 2 wb + j, on it when equal, else below (skipped).
+  // register 4 q + e of block j holds G(R + e, C) with R = 32 wa + 8 q + 4 (l /
+  // 32) and C = 64 wb + 32 j + l % 32.  Only values on or above the diagonal
+  // are used: G(R + e, C) itself when R + e <= C, and as its mirror G(C, R + e)
+  // when R + e < C (four consecutive columns of row C).  Block j lies wholly
+  // above the diagonal when its block row wa is below its block column
+  // 2 wb + j, on it when equal, else below (skipped).
   float* const out = p.part + ((int64_t)b * ks + ch) * M * M;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int bi = 2 * wa + i, bj = 2 * wb + j;
+      const int bi = wa, bj = 2 * wb + j;
       if (bi > bj) continue;
-      const f32x16& a = accg[i][j];
+      const f32x16& a = accg[j];
       const int C = 32 * bj + (lane & 31);
       if (bi < bj) {
 #pragma unroll
@@ -355,8 +366,21 @@ hipError_t launch_updgram128(const UpdGram128Group& g, hipStream_t s) {
   const bool gram = g.prob[0].part != nullptr;
   for (int i = 1; i < g.nprob; ++i)
     if ((g.prob[i].part != nullptr) != gram) return hipErrorInvalidValue;
-  return gram ? launch_kernel(updgram128_kernel<true>, dim3(grid), g, s)
-              : launch_kernel(updgram128_kernel<false>, dim3(grid), g, s);
+  return gram ? launch_kernel(updgram128_kernel<kUpdGram>, dim3(grid), g, s, 512)
+              : launch_kernel(updgram128_kernel<kUpdOnly>, dim3(grid), g, s, 512);
+}
+
+hipError_t launch_gram128(const UpdGram128Group& g, hipStream_t s) {
+  if (g.nprob < 1 || g.nprob > kMaxUpdGram128 || g.start[0] != 0) return hipErrorInvalidValue;
+  for (int i = 0; i < g.nprob; ++i) {
+    const UpdGram128Params& p = g.prob[i];
+    if (p.np <= 0 || p.np % SUB != 0 || p.ksplit < 1 || p.ksplit > p.np / SUB || !p.X || !p.part)
+      return hipErrorInvalidValue;
+    if (g.start[i + 1] < g.start[i] || (g.start[i + 1] - g.start[i]) % p.ksplit != 0) return hipErrorInvalidValue;
+  }
+  const int grid = g.start[g.nprob];
+  if (grid <= 0) return hipSuccess;
+  return launch_kernel(updgram128_kernel<kGramOnly>, dim3(grid), g, s, 512);
 }
 
 }  // namespace muon
