@@ -95,7 +95,8 @@ __device__ __forceinline__ void store8v(void* row, int valid, bool bf, bool vec,
 //   mode 0: U = x (muon_ns_batched input)
 //   mode 1: M <- mu M + G;  U = G + mu M  (or U = M without Nesterov)
 // Writes U (rounded to the X dtype) at its oriented position, zeros in the
-// padding, and the tile's sum of U^2 (from the fp32 U) to partial[].
+// padding, and the tile's sum of U^2 (from the fp32 U) to partial[]; with
+// no_x (a bf16 input the iterations read in place) the partials only.
 // Thread -> rows tid / 8 and tid / 8 + 32 of the tile, 8 consecutive columns
 // each: eight lanes cover one 64-element row segment, so every wave access
 // is whole 128-byte lines (bf16).  The tile is staged in LDS for the
@@ -154,16 +155,18 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams p) {
       T[r][c0 + e] = u[e];
     }
   }
-  __syncthreads();
-  // Oriented write: X[oi0 + orow][oj0 + c0 .. +8].
+  if (!p.no_x) {
+    __syncthreads();
+    // Oriented write: X[oi0 + orow][oj0 + c0 .. +8].
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int orow = (tid >> 3) + 32 * h;
-    float v[8];
+    for (int h = 0; h < 2; ++h) {
+      const int orow = (tid >> 3) + 32 * h;
+      float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = p.tall ? T[c0 + e][orow] : T[orow][c0 + e];
-    const int64_t xoff = (int64_t)bz * p.X_bs + (int64_t)(oi0 + orow) * p.np + oj0 + c0;
-    store8v((uint8_t*)p.X + xoff * (p.x_bf16 ? 2 : 4), 8, p.x_bf16, true, v);
+      for (int e = 0; e < 8; ++e) v[e] = p.tall ? T[c0 + e][orow] : T[orow][c0 + e];
+      const int64_t xoff = (int64_t)bz * p.X_bs + (int64_t)(oi0 + orow) * p.np + oj0 + c0;
+      store8v((uint8_t*)p.X + xoff * (p.x_bf16 ? 2 : 4), 8, p.x_bf16, true, v);
+    }
   }
   const float tot = block_sum(s, red);
   if (tid == 0) {

@@ -226,6 +226,10 @@ struct NsJob {
   char* ws;
   Layout L;
   FinalOut out;
+  // The caller's bf16 input, read in place by the first iteration instead of
+  // a copy in X0 (null: X0 holds the input), and its batch stride.
+  const void* x0 = nullptr;
+  int64_t x0_bs = 0;
 };
 
 // Launch one phase (Gram, poly or update) of several jobs: problems with the
@@ -324,10 +328,15 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
       const float* rs = (const float*)(ws + J.L.rs);
       const int64_t sx = g.mp * g.np, sa = g.mp * g.mp;
       const int c = cur[k];
+      // The iterate this iteration reads: the caller's input itself on the
+      // first iteration when it is read in place.
+      const bool direct = first && J.x0;
+      void* const Xin = direct ? const_cast<void*>(J.x0) : X[c];
+      const int64_t sxin = direct ? J.x0_bs : sx;
       {  // A = X X^T (times rs^2 on the first iteration, which folds in the normalization)
         GemmParams p{};
-        p.P = X[c]; p.ldp = g.np; p.sP = sx;
-        p.Q = X[c]; p.ldq = g.np; p.sQ = sx;
+        p.P = Xin; p.ldp = g.np; p.sP = sxin;
+        p.Q = Xin; p.ldq = g.np; p.sQ = sxin;
         p.C = A; p.ldc = g.mp; p.sC = sa; p.c_dtype = MUON_BF16;
         p.M = p.N = (int)g.mp; p.K = (int)g.np; p.Mreal = p.Nreal = (int)g.mp;
         p.alpha = 1.f;
@@ -372,7 +381,7 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
           // The first Gram of a 128-row matrix: chunk products straight from
           // X by the Gram-only variant of the fused kernel (same chunks).
           UpdGram128Params u{};
-          u.X = X[c]; u.x_bs = sx;
+          u.X = Xin; u.x_bs = sxin;
           u.part = (float*)(ws + J.L.part);
           u.np = (int)g.np; u.ksplit = ks;
           gram128.push_back({u, (int)J.nb, p.flop, B * (m * n * 2 + ks * m * m * 4)});
@@ -402,7 +411,7 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
          // products
         GemmParams p{};
         p.P = Bm; p.ldp = g.mp; p.sP = sa;
-        p.Q = X[c]; p.ldq = g.np; p.sQ = sx;
+        p.Q = Xin; p.ldq = g.np; p.sQ = sxin;
         p.dq = 1;
         p.M = (int)g.mp; p.N = (int)g.np; p.K = (int)g.mp;
         p.alpha = 1.f; p.beta = cf.a;
@@ -425,7 +434,7 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
           // and the chunk products of X' X'^T to the split-K buffer.
           UpdGram128Params u{};
           u.B = Bm; u.b_bs = sa;
-          u.X = X[c]; u.x_bs = sx;
+          u.X = Xin; u.x_bs = sxin;
           u.Y = X[c ^ 1]; u.y_bs = sx;
           u.part = (float*)(ws + J.L.part);
           u.np = (int)g.np; u.ksplit = ks;
@@ -666,12 +675,25 @@ hipError_t ns_run_passes(const muon_ns_problem* q, int64_t nq, const muon_ns_con
       pp.x_bs = p.x_batch_stride; pp.x_rs = p.x_row_stride;
       pp.X = v.ws + v.L.X0; pp.X_bs = v.g.mp * v.g.np;
       pp.partial = (float*)(v.ws + v.L.partial);
+      // A bf16 input already laid out as the iterate (not transposed, no
+      // padding, rows np apart, 16-byte aligned) and not overwritten by the
+      // output is read in place by the first iteration: the load kernel then
+      // computes the norm partials only.
+      const bool direct = v.g.bf && p.x_dtype == MUON_BF16 && !v.g.tall && v.g.mp == p.rows && v.g.np == p.cols &&
+                          p.x_row_stride == p.cols && (p.x_batch_stride % 8) == 0 && ((uintptr_t)p.x & 15) == 0 &&
+                          p.y != p.x;
+      pp.no_x = direct ? 1 : 0;
       hipError_t e = run(MUON_K_PREP, 0, (double)nb * p.rows * p.cols * (xe + (v.g.bf ? 2 : 4)), s,
                          [&]() { return launch_prep(pp, (int)nb, s); });
       if (e != hipSuccess) return e;
       if ((e = norm_finalize(v.g, nb, cfg.eps, v.ws, v.L, s)) != hipSuccess) return e;
       FinalOut out{(char*)p.y + c0 * p.y_batch_stride * ye, p.y_dtype, p.y_row_stride, p.y_batch_stride};
-      jobs.push_back(NsJob{v.g, nb, v.ws, v.L, out});
+      NsJob job{v.g, nb, v.ws, v.L, out};
+      if (direct) {
+        job.x0 = pp.x;
+        job.x0_bs = p.x_batch_stride;
+      }
+      jobs.push_back(job);
     }
     hipError_t e = ns_iterations(jobs, cfg, s);
     if (e != hipSuccess) return e;

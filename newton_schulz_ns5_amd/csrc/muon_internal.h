@@ -73,6 +73,7 @@ struct PrepParams {
   void* mom[kMaxParams];                       // mode 1
   void* X; int64_t X_bs;                       // oriented, padded output
   float* partial;                              // [b][tiles]
+  int32_t no_x;                                // mode 0: partials only, X not written
 };
 
 struct NormParams {

@@ -175,6 +175,33 @@ def test_strided_row_views():
     assert torch.equal(out, ref)
 
 
+@pytest.mark.parametrize("shape", [(3, 128, 4096), (1, 128, 1024), (2, 256, 1024), (2, 384, 768)])
+@pytest.mark.parametrize("steps", [5, 1])
+def test_input_read_in_place_matches_copied_input(shape, steps):
+    # A contiguous, aligned bf16 input that is not transposed or padded is read
+    # in place by the first iteration; a row-padded view, a misaligned copy and
+    # the in-place call (y == x) take the copy into the workspace.  All four
+    # give the same bits.
+    torch = torch_cuda()
+    n, rows, cols = shape
+    x = to_dev(synth.gaussian(shape, (9, 12, rows, cols, steps), "bf16"), "bf16")
+    direct = ns.ns_batched(x, steps=steps)
+    wide = torch.zeros((n, rows, cols + 64), dtype=x.dtype, device=x.device)
+    wide[:, :, :cols] = x
+    padded = ns.ns_batched(wide[:, :, :cols], steps=steps)
+    flat = torch.zeros(x.numel() + 4, dtype=x.dtype, device=x.device)
+    shifted = flat[4:].view(shape)          # 8 bytes past a 16-byte boundary
+    shifted.copy_(x)
+    mis = ns.ns_batched(shifted, steps=steps)
+    inplace = x.clone()
+    ns.ns_batched(inplace, inplace, steps=steps)
+    torch.cuda.synchronize()
+    assert torch.equal(direct, padded)
+    assert torch.equal(direct, mis)
+    assert torch.equal(direct, inplace)
+    assert torch.equal(x, to_dev(synth.gaussian(shape, (9, 12, rows, cols, steps), "bf16"), "bf16"))  # input intact
+
+
 # ---- per-iteration coefficient schedules ------------------------------------
 SCHEDULE = [oracle.QUINTIC] * 4 + [(15 / 8, -10 / 8, 3 / 8)]   # four quintic steps, then the classical polynomial
 
