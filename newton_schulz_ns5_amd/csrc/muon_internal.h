@@ -155,8 +155,10 @@ hipError_t launch_poly128(const Poly128Group& g, hipStream_t s);
 // Y[b] = alpha_b B[b] X[b] + beta_b X[b] (bf16, [128][np] row-major; alpha_b
 // = alpha rs[b]^alpha_pow, beta_b = beta rs[b]^beta_pow, rs may be null) and,
 // when part is not null, part[b * ksplit + c] = Y_c Y_c^T (fp32 [128][128],
-// exactly symmetric) over the columns of chunk c, whose edges are those of the
-// split-K Gram (128 * floor(c * (np / 128) / ksplit)).  B is exactly symmetric.
+// its 32 x 32 blocks on and above the diagonal only, the diagonal blocks
+// exactly symmetric; the blocks below are not written) over the columns of
+// chunk c, whose edges are those of the split-K Gram (128 * floor(c * (np /
+// 128) / ksplit)).  B is exactly symmetric.
 struct UpdGram128Params {
   const void* B; int64_t b_bs;       // [128][128] bf16, row stride 128
   const void* X; int64_t x_bs;       // [128][np] bf16, row stride np

@@ -11,10 +11,11 @@
 //      prep kernel's partials;
 //   1. sums the fp32 chunk products of the split-K Gram in chunk order,
 //      scales by rs^2 (first iteration) and rounds to bf16 once: A exactly
-//      as the separate sum would store it, but into LDS only.  The chunk
-//      products are exactly symmetric, so only their 32 x 32 blocks on or
-//      above the diagonal are read (10 of 16) and each is written to LDS
-//      twice, as itself and as its mirror;
+//      as the separate sum would store it, but into LDS only.  A is
+//      symmetric and the chunk products hold their 32 x 32 blocks on and
+//      above the diagonal only (10 of 16, the diagonal ones exactly
+//      symmetric), so those are read and each is written to LDS twice, as
+//      itself and as its mirror;
 //   2. computes A A with v_mfma_f32_32x32x16_bf16 (A is symmetric, so both
 //      operands are rows of A), each wave two 32 x 32 blocks;
 //   3. writes B = bf16(c (A A) + b A) through LDS with 16-byte stores.

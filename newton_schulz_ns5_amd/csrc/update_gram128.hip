@@ -21,9 +21,10 @@
 //      layout the Gram's operands are read in -- from where it goes to HBM
 //      with 16-byte stores;
 //   4. accumulates the chunk's Gram product X'_c X'_c^T over its sub-tiles
-//      (fp32) and finally stores it exactly symmetric (the upper triangle and
-//      its mirror, straight from the accumulators) as chunk c of the split-K
-//      product the next iteration's sum-and-polynomial kernel reads.
+//      (fp32) and finally stores its 32 x 32 blocks on and above the
+//      diagonal (the diagonal ones exactly symmetric), straight from the
+//      accumulators, as chunk c of the split-K product the next iteration's
+//      sum-and-polynomial kernel reads.
 // The same kernel without steps 2-3 computes the first iteration's chunk
 // products from X itself, and without step 4 an update alone.
 // Eight waves (two per SIMD) share each sub-tile's products, so one wave's
@@ -310,13 +311,13 @@ __global__ __launch_bounds__(512, 1) void updgram128_kernel(const UpdGram128Grou
   }
   if constexpr (!GRAM) return;
 
-  // The chunk's Gram product, stored exactly symmetric from the accumulators:
-  // register 4 q + e of block j holds G(R + e, C) with R = 32 wa + 8 q + 4 (l /
-  // 32) and C = 64 wb + 32 j + l % 32.  Only values on or above the diagonal
-  // are used: G(R + e, C) itself when R + e <= C, and as its mirror G(C, R + e)
-  // when R + e < C (four consecutive columns of row C).  Block j lies wholly
-  // above the diagonal when its block row wa is below its block column
-  // 2 wb + j, on it when equal, else below (skipped).
+  // The chunk's Gram product from the accumulators: register 4 q + e of
+  // block j holds G(R + e, C) with R = 32 wa + 8 q + 4 (l / 32) and C = 64 wb
+  // + 32 j + l % 32.  Its reader (the sum-and-polynomial kernel) takes the
+  // 32 x 32 blocks on and above the diagonal only, so those are stored: a
+  // block above the diagonal (block row wa below block column 2 wb + j) as
+  // it is, a diagonal block exactly symmetric (G(R + e, C) when R + e <= C,
+  // and as its mirror G(C, R + e) when R + e < C); blocks below are skipped.
   float* const out = p.part + ((int64_t)b * ks + ch) * M * M;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -328,13 +329,8 @@ __global__ __launch_bounds__(512, 1) void updgram128_kernel(const UpdGram128Grou
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int R = 32 * bi + 8 * q + 4 * (lane >> 5);
-          f32x4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[e] = a[4 * q + e];
-            out[(R + e) * M + C] = a[4 * q + e];
-          }
-          *(f32x4*)(out + C * M + R) = v;
+          for (int e = 0; e < 4; ++e) out[(R + e) * M + C] = a[4 * q + e];
         }
       } else {
 #pragma unroll
