@@ -184,7 +184,17 @@ __global__ __launch_bounds__(256) void norm_kernel(const NormParams p) {
   const int b = blockIdx.x;
   const float* src = p.partial + (int64_t)b * p.tiles;
   float s = 0.f;
-  for (int i = threadIdx.x; i < p.tiles; i += 256) s += src[i];
+  int i = threadIdx.x;
+  // Eight loads in flight per thread (a matrix has up to tens of thousands of
+  // partials); they are still added one by one in index order.
+  for (; i + 7 * 256 < p.tiles; i += 8 * 256) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = src[i + 256 * k];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += v[k];
+  }
+  for (; i < p.tiles; i += 256) s += src[i];
   const float tot = block_sum(s, red);
   if (threadIdx.x == 0) p.rs[b] = __builtin_isfinite(tot) ? 1.f / (sqrtf(tot) + p.eps) : __builtin_nanf("");
 }
