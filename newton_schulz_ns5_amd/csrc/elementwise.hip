@@ -101,11 +101,19 @@ __device__ __forceinline__ void store8v(void* row, int valid, bool bf, bool vec,
 // each: eight lanes cover one 64-element row segment, so every wave access
 // is whole 128-byte lines (bf16).  The tile is staged in LDS for the
 // transposed write of a tall matrix.
-__global__ __launch_bounds__(256) void prep_kernel(const PrepParams p) {
+// One launch covers the problems of a PrepGroup: the grid's z index picks the
+// problem and its matrix, and a problem smaller than the grid's x/y extent
+// leaves the rest of the grid idle.
+__global__ __launch_bounds__(256) void prep_kernel(const PrepGroup grp) {
   __shared__ float T[64][65];
   __shared__ float red[4];
+  int pi = 0;
+  while (pi + 1 < grp.nprob && (int)blockIdx.z >= grp.zstart[pi + 1]) ++pi;
+  const PrepParams& p = grp.prob[pi];
+  const int tiles_x = p.np / 64, tiles_y = p.mp / 64;
+  if ((int)blockIdx.x >= tiles_x || (int)blockIdx.y >= tiles_y) return;
   const int tid = threadIdx.x;
-  const int bz = blockIdx.z;
+  const int bz = (int)blockIdx.z - grp.zstart[pi];
   const int oi0 = blockIdx.y * 64, oj0 = blockIdx.x * 64;
   const int pr0 = p.tall ? oj0 : oi0, pc0 = p.tall ? oi0 : oj0;
   const int c0 = (tid & 7) * 8;
@@ -169,19 +177,19 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams p) {
     }
   }
   const float tot = block_sum(s, red);
-  if (tid == 0) {
-    const int tiles = gridDim.x * gridDim.y;
-    p.partial[(int64_t)bz * tiles + blockIdx.y * gridDim.x + blockIdx.x] = tot;
-  }
+  if (tid == 0) p.partial[(int64_t)bz * (tiles_x * tiles_y) + blockIdx.y * tiles_x + blockIdx.x] = tot;
 }
 
 // rs[b] = 1 / (sqrt(sum of the matrix's tile partials) + eps).  A sum that
 // is not finite (an input whose squared Frobenius norm exceeds the fp32
 // range, or a NaN in it) gives rs = NaN, so the output is NaN rather than a
 // silently zero matrix.
-__global__ __launch_bounds__(256) void norm_kernel(const NormParams p) {
+__global__ __launch_bounds__(256) void norm_kernel(const NormGroup grp) {
   __shared__ float red[4];
-  const int b = blockIdx.x;
+  int pi = 0;
+  while (pi + 1 < grp.nprob && (int)blockIdx.x >= grp.start[pi + 1]) ++pi;
+  const NormParams& p = grp.prob[pi];
+  const int b = (int)blockIdx.x - grp.start[pi];
   const float* src = p.partial + (int64_t)b * p.tiles;
   float s = 0.f;
   int i = threadIdx.x;
@@ -420,14 +428,46 @@ __global__ __launch_bounds__(256) void apply_kernel(const ApplyParams p) {
 
 }  // namespace
 
+hipError_t launch_prep_group(const PrepGroup& g, hipStream_t s) {
+  if (g.nprob < 1 || g.nprob > kMaxPrep || g.zstart[0] != 0) return hipErrorInvalidValue;
+  int gx = 0, gy = 0;
+  for (int i = 0; i < g.nprob; ++i) {
+    const PrepParams& p = g.prob[i];
+    if (g.zstart[i + 1] < g.zstart[i] || p.np % kPrepTile || p.mp % kPrepTile) return hipErrorInvalidValue;
+    gx = p.np / kPrepTile > gx ? p.np / kPrepTile : gx;
+    gy = p.mp / kPrepTile > gy ? p.mp / kPrepTile : gy;
+  }
+  const int gz = g.zstart[g.nprob];
+  if (gz <= 0 || gx <= 0 || gy <= 0) return hipSuccess;
+  if (gz > 65535 || gy > 65535) return hipErrorInvalidValue;
+  return launch_kernel(prep_kernel, dim3(gx, gy, gz), g, s);
+}
+
 hipError_t launch_prep(const PrepParams& p, int nb, hipStream_t s) {
   if (nb <= 0) return hipSuccess;
-  return launch_kernel(prep_kernel, dim3(p.np / kPrepTile, p.mp / kPrepTile, nb), p, s);
+  PrepGroup g{};
+  g.prob[0] = p;
+  g.zstart[1] = nb;
+  g.nprob = 1;
+  return launch_prep_group(g, s);
+}
+
+hipError_t launch_norm_group(const NormGroup& g, hipStream_t s) {
+  if (g.nprob < 1 || g.nprob > kMaxNorm || g.start[0] != 0) return hipErrorInvalidValue;
+  for (int i = 0; i < g.nprob; ++i)
+    if (g.start[i + 1] < g.start[i] || g.prob[i].tiles < 1) return hipErrorInvalidValue;
+  const int grid = g.start[g.nprob];
+  if (grid <= 0) return hipSuccess;
+  return launch_kernel(norm_kernel, dim3(grid), g, s);
 }
 
 hipError_t launch_norm(const NormParams& p, int nb, hipStream_t s) {
   if (nb <= 0) return hipSuccess;
-  return launch_kernel(norm_kernel, dim3(nb), p, s);
+  NormGroup g{};
+  g.prob[0] = p;
+  g.start[1] = nb;
+  g.nprob = 1;
+  return launch_norm_group(g, s);
 }
 
 hipError_t launch_split_sum(const SplitSumParams& p, int nb, hipStream_t s) {

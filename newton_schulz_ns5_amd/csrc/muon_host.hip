@@ -86,6 +86,10 @@ int gram_ksplit(const Geom& g) {
   return s < 2 ? 1 : (s > kMaxKsplit ? kMaxKsplit : (int)s);
 }
 
+// The 128-row path with a split Gram (fused update/Gram kernels; the norm
+// is finalized by the first iteration's sum-and-polynomial kernel).
+bool path128(const Geom& g) { return g.mp == 128 && gram_ksplit(g) > 1; }
+
 // Workspace of `nb` NS problems.
 struct Layout {
   size_t X0, X1, A, B, partial, rs, part, total;
@@ -347,8 +351,8 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
         // A 128-row matrix's Gram after the first iteration was computed by
         // the previous iteration's update (update_gram128): its chunk
         // products are already in the workspace.
-        const bool prev_fused = ks > 1 && g.mp == 128 && !first;
-        if (ks > 1 && g.mp == 128) {
+        const bool prev_fused = path128(g) && !first;
+        if (path128(g)) {
           // fp32 product of each K chunk, summed by the fused kernel that also
           // computes B (A is not stored)
           Poly128Params q{};
@@ -377,7 +381,7 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
           p.ksplit = ks;
           p.bytes += B * (ks - 1) * m * m * 4;
         }
-        if (ks > 1 && g.mp == 128 && first) {
+        if (path128(g) && first) {
           // The first Gram of a 128-row matrix: chunk products straight from
           // X by the Gram-only variant of the fused kernel (same chunks).
           UpdGram128Params u{};
@@ -404,7 +408,7 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
         p.alpha = cf.c; p.beta = cf.b;
         p.batch = (int)J.nb;
         p.flop = B * m * m * m; p.bytes = B * 2 * m * m * 2;
-        if (!(gram_ksplit(g) > 1 && g.mp == 128)) poly.push_back(p);
+        if (!path128(g)) poly.push_back(p);
       }
       {  // X' = B X + a X (times rs on the first iteration): NN with Q = X,
          // whose transposed tile is the D tile, so a X is added inside the
@@ -429,7 +433,7 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
         }
         p.flop = B * 2 * m * m * n; p.bytes = B * (m * m + 2 * m * n) * 2;
         const int ks = gram_ksplit(g);
-        if (ks > 1 && g.mp == 128 && !last) {
+        if (path128(g) && !last) {
           // Fused with the next iteration's Gram: X' to the other X buffer
           // and the chunk products of X' X'^T to the split-K buffer.
           UpdGram128Params u{};
@@ -547,15 +551,21 @@ hipError_t ns_iterations(const std::vector<NsJob>& jobs, const muon_ns_config& c
   return hipSuccess;
 }
 
-hipError_t norm_finalize(const Geom& g, int64_t nb, float eps, char* ws, const Layout& L, hipStream_t s) {
-  // A 128-row matrix with a split Gram has its norm finalized by the first
-  // iteration's sum-and-polynomial kernel, which is the first to need it.
-  if (g.mp == 128 && gram_ksplit(g) > 1) return hipSuccess;
+// The norm finalize of the matrices of one workspace region.
+NormParams norm_params(const Layout& L, float eps, char* ws) {
   NormParams np{};
   np.partial = (const float*)(ws + L.partial);
   np.tiles = L.tiles;
   np.eps = eps;
   np.rs = (float*)(ws + L.rs);
+  return np;
+}
+
+hipError_t norm_finalize(const Geom& g, int64_t nb, float eps, char* ws, const Layout& L, hipStream_t s) {
+  // A 128-row matrix with a split Gram has its norm finalized by the first
+  // iteration's sum-and-polynomial kernel, which is the first to need it.
+  if (path128(g)) return hipSuccess;
+  const NormParams np = norm_params(L, eps, ws);
   return run(MUON_K_NORM, 0, (double)nb * L.tiles * 4, s, [&]() { return launch_norm(np, (int)nb, s); });
 }
 
@@ -657,6 +667,9 @@ hipError_t ns_run_passes(const muon_ns_problem* q, int64_t nq, const muon_ns_con
   }
   for (int64_t k = 0; k < passes; ++k) {
     std::vector<NsJob> jobs;
+    struct Prep { PrepParams pp; int nb; double bytes; };
+    std::vector<Prep> preps;
+    std::vector<std::pair<NormParams, int>> norms;
     for (const Live& v : live) {
       const muon_ns_problem& p = *v.q;
       const int64_t c0 = k * v.chunk;
@@ -683,10 +696,8 @@ hipError_t ns_run_passes(const muon_ns_problem* q, int64_t nq, const muon_ns_con
                           p.x_row_stride == p.cols && (p.x_batch_stride % 8) == 0 && ((uintptr_t)p.x & 15) == 0 &&
                           p.y != p.x;
       pp.no_x = direct ? 1 : 0;
-      hipError_t e = run(MUON_K_PREP, 0, (double)nb * p.rows * p.cols * (xe + (v.g.bf ? 2 : 4)), s,
-                         [&]() { return launch_prep(pp, (int)nb, s); });
-      if (e != hipSuccess) return e;
-      if ((e = norm_finalize(v.g, nb, cfg.eps, v.ws, v.L, s)) != hipSuccess) return e;
+      preps.push_back({pp, (int)nb, (double)nb * p.rows * p.cols * (xe + (direct ? 0 : (v.g.bf ? 2 : 4)))});
+      if (!path128(v.g)) norms.push_back({norm_params(v.L, cfg.eps, v.ws), (int)nb});
       FinalOut out{(char*)p.y + c0 * p.y_batch_stride * ye, p.y_dtype, p.y_row_stride, p.y_batch_stride};
       NsJob job{v.g, nb, v.ws, v.L, out};
       if (direct) {
@@ -694,6 +705,34 @@ hipError_t ns_run_passes(const muon_ns_problem* q, int64_t nq, const muon_ns_con
         job.x0_bs = p.x_batch_stride;
       }
       jobs.push_back(job);
+    }
+    // The load kernel and the norm finalize for every problem of the pass,
+    // several problems per launch.
+    for (size_t i0 = 0; i0 < preps.size();) {
+      PrepGroup g{};
+      double bytes = 0;
+      size_t i = i0;
+      for (; i < preps.size() && g.nprob < kMaxPrep && g.zstart[g.nprob] + preps[i].nb <= 65535; ++i) {
+        g.prob[g.nprob] = preps[i].pp;
+        g.zstart[g.nprob + 1] = g.zstart[g.nprob] + preps[i].nb;
+        ++g.nprob;
+        bytes += preps[i].bytes;
+      }
+      const hipError_t e = run(MUON_K_PREP, 0, bytes, s, [&]() { return launch_prep_group(g, s); });
+      if (e != hipSuccess) return e;
+      i0 = i;
+    }
+    for (size_t i0 = 0; i0 < norms.size(); i0 += kMaxNorm) {
+      NormGroup g{};
+      double bytes = 0;
+      for (size_t i = i0; i < norms.size() && i < i0 + kMaxNorm; ++i) {
+        g.prob[g.nprob] = norms[i].first;
+        g.start[g.nprob + 1] = g.start[g.nprob] + norms[i].second;
+        ++g.nprob;
+        bytes += (double)norms[i].second * norms[i].first.tiles * 4;
+      }
+      const hipError_t e = run(MUON_K_NORM, 0, bytes, s, [&]() { return launch_norm_group(g, s); });
+      if (e != hipSuccess) return e;
     }
     hipError_t e = ns_iterations(jobs, cfg, s);
     if (e != hipSuccess) return e;

@@ -141,6 +141,26 @@ hipError_t launch_gemm_f32(const GemmParams& p, bool nn, bool syrk, hipStream_t 
 int gemm_f32_tile();    // output tile edge of the fp32 GEMM (divides kPadF32)
 hipError_t launch_prep(const PrepParams& p, int nb, hipStream_t s);
 hipError_t launch_norm(const NormParams& p, int nb, hipStream_t s);
+// Several problems in one launch of the load kernel (problem i: grid z
+// indices zstart[i] .. zstart[i + 1] - 1, one per matrix; at most 65535 in
+// all) or of the norm finalize (problem i: workgroups start[i] ..
+// start[i + 1] - 1).  A PrepParams carries two pointer tables, so a launch
+// holds at most four.
+constexpr int kMaxPrep = 4;
+struct PrepGroup {
+  PrepParams prob[kMaxPrep];
+  int32_t zstart[kMaxPrep + 1];
+  int32_t nprob;
+};
+static_assert(sizeof(PrepGroup) <= 4096, "kernel argument block of one launch");
+hipError_t launch_prep_group(const PrepGroup& g, hipStream_t s);
+constexpr int kMaxNorm = 8;
+struct NormGroup {
+  NormParams prob[kMaxNorm];
+  int32_t start[kMaxNorm + 1];
+  int32_t nprob;
+};
+hipError_t launch_norm_group(const NormGroup& g, hipStream_t s);
 hipError_t launch_split_sum(const SplitSumParams& p, int nb, hipStream_t s);
 // Up to kMaxPoly128 such problems in one launch; problem i owns workgroups
 // start[i] .. start[i + 1] - 1, one per matrix.

@@ -155,9 +155,12 @@ def test_transpose_orientation_consistent():
     assert rel_fro(to_f64(a), to_f64(b)) < 1e-5
 
 
-def test_max_batch_chunking_bitwise():
+@pytest.mark.parametrize("shape", [(5, 128, 384), (5, 128, 4096)])
+def test_max_batch_chunking_bitwise(shape):
+    # Passes of at most two matrices (the input read in place pass by pass;
+    # the second shape takes the split-Gram 128-row path) equal one pass.
     torch = torch_cuda()
-    x = to_dev(synth.gaussian((5, 128, 384), (9, 8, 8, 1, 0), "bf16"), "bf16")
+    x = to_dev(synth.gaussian(shape, (9, 8, 8, 1, shape[2]), "bf16"), "bf16")
     a = ns.ns_batched(x)
     b = ns.ns_batched(x, max_batch=2)
     torch.cuda.synchronize()
