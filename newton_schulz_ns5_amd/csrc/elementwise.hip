@@ -443,15 +443,6 @@ hipError_t launch_prep_group(const PrepGroup& g, hipStream_t s) {
   return launch_kernel(prep_kernel, dim3(gx, gy, gz), g, s);
 }
 
-hipError_t launch_prep(const PrepParams& p, int nb, hipStream_t s) {
-  if (nb <= 0) return hipSuccess;
-  PrepGroup g{};
-  g.prob[0] = p;
-  g.zstart[1] = nb;
-  g.nprob = 1;
-  return launch_prep_group(g, s);
-}
-
 hipError_t launch_norm_group(const NormGroup& g, hipStream_t s) {
   if (g.nprob < 1 || g.nprob > kMaxNorm || g.start[0] != 0) return hipErrorInvalidValue;
   for (int i = 0; i < g.nprob; ++i)
@@ -461,14 +452,6 @@ hipError_t launch_norm_group(const NormGroup& g, hipStream_t s) {
   return launch_kernel(norm_kernel, dim3(grid), g, s);
 }
 
-hipError_t launch_norm(const NormParams& p, int nb, hipStream_t s) {
-  if (nb <= 0) return hipSuccess;
-  NormGroup g{};
-  g.prob[0] = p;
-  g.start[1] = nb;
-  g.nprob = 1;
-  return launch_norm_group(g, s);
-}
 
 hipError_t launch_split_sum(const SplitSumParams& p, int nb, hipStream_t s) {
   // mp is a multiple of 128, so mp^2 / 8 is a whole number of 256-thread blocks.

@@ -358,7 +358,7 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
           Poly128Params q{};
           q.part = (const float*)(ws + J.L.part); q.ksplit = ks;
           q.rs = p.rs;
-          if (first) {  // the norm is finalized here (norm_finalize skipped it)
+          if (first) {  // the norm is finalized here (path128: no norm launch)
             q.rs = nullptr;
             q.nsum = (const float*)(ws + J.L.partial); q.ntiles = J.L.tiles;
             q.eps = cfg.eps; q.rs_out = (float*)(ws + J.L.rs);
@@ -561,12 +561,42 @@ NormParams norm_params(const Layout& L, float eps, char* ws) {
   return np;
 }
 
-hipError_t norm_finalize(const Geom& g, int64_t nb, float eps, char* ws, const Layout& L, hipStream_t s) {
-  // A 128-row matrix with a split Gram has its norm finalized by the first
-  // iteration's sum-and-polynomial kernel, which is the first to need it.
-  if (path128(g)) return hipSuccess;
-  const NormParams np = norm_params(L, eps, ws);
-  return run(MUON_K_NORM, 0, (double)nb * L.tiles * 4, s, [&]() { return launch_norm(np, (int)nb, s); });
+// Load-kernel and norm-finalize work of one pass, gathered over every group
+// and launched a few problems at a time.
+struct StageLaunches {
+  struct Prep { PrepParams pp; int nb; double bytes; };
+  std::vector<Prep> preps;
+  std::vector<std::pair<NormParams, int>> norms;
+};
+
+hipError_t launch_stage(const StageLaunches& st, hipStream_t s) {
+  for (size_t i0 = 0; i0 < st.preps.size();) {
+    PrepGroup g{};
+    double bytes = 0;
+    size_t i = i0;
+    for (; i < st.preps.size() && g.nprob < kMaxPrep && g.zstart[g.nprob] + st.preps[i].nb <= 65535; ++i) {
+      g.prob[g.nprob] = st.preps[i].pp;
+      g.zstart[g.nprob + 1] = g.zstart[g.nprob] + st.preps[i].nb;
+      ++g.nprob;
+      bytes += st.preps[i].bytes;
+    }
+    const hipError_t e = run(MUON_K_PREP, 0, bytes, s, [&]() { return launch_prep_group(g, s); });
+    if (e != hipSuccess) return e;
+    i0 = i;
+  }
+  for (size_t i0 = 0; i0 < st.norms.size(); i0 += kMaxNorm) {
+    NormGroup g{};
+    double bytes = 0;
+    for (size_t i = i0; i < st.norms.size() && i < i0 + kMaxNorm; ++i) {
+      g.prob[g.nprob] = st.norms[i].first;
+      g.start[g.nprob + 1] = g.start[g.nprob] + st.norms[i].second;
+      ++g.nprob;
+      bytes += (double)st.norms[i].second * st.norms[i].first.tiles * 4;
+    }
+    const hipError_t e = run(MUON_K_NORM, 0, bytes, s, [&]() { return launch_norm_group(g, s); });
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // Matrices (or parameters) processed per pass; the grid's z extent bounds it.
@@ -667,9 +697,7 @@ hipError_t ns_run_passes(const muon_ns_problem* q, int64_t nq, const muon_ns_con
   }
   for (int64_t k = 0; k < passes; ++k) {
     std::vector<NsJob> jobs;
-    struct Prep { PrepParams pp; int nb; double bytes; };
-    std::vector<Prep> preps;
-    std::vector<std::pair<NormParams, int>> norms;
+    StageLaunches st;
     for (const Live& v : live) {
       const muon_ns_problem& p = *v.q;
       const int64_t c0 = k * v.chunk;
@@ -696,8 +724,8 @@ hipError_t ns_run_passes(const muon_ns_problem* q, int64_t nq, const muon_ns_con
                           p.x_row_stride == p.cols && (p.x_batch_stride % 8) == 0 && ((uintptr_t)p.x & 15) == 0 &&
                           p.y != p.x;
       pp.no_x = direct ? 1 : 0;
-      preps.push_back({pp, (int)nb, (double)nb * p.rows * p.cols * (xe + (direct ? 0 : (v.g.bf ? 2 : 4)))});
-      if (!path128(v.g)) norms.push_back({norm_params(v.L, cfg.eps, v.ws), (int)nb});
+      st.preps.push_back({pp, (int)nb, (double)nb * p.rows * p.cols * (xe + (direct ? 0 : (v.g.bf ? 2 : 4)))});
+      if (!path128(v.g)) st.norms.push_back({norm_params(v.L, cfg.eps, v.ws), (int)nb});
       FinalOut out{(char*)p.y + c0 * p.y_batch_stride * ye, p.y_dtype, p.y_row_stride, p.y_batch_stride};
       NsJob job{v.g, nb, v.ws, v.L, out};
       if (direct) {
@@ -708,33 +736,9 @@ hipError_t ns_run_passes(const muon_ns_problem* q, int64_t nq, const muon_ns_con
     }
     // The load kernel and the norm finalize for every problem of the pass,
     // several problems per launch.
-    for (size_t i0 = 0; i0 < preps.size();) {
-      PrepGroup g{};
-      double bytes = 0;
-      size_t i = i0;
-      for (; i < preps.size() && g.nprob < kMaxPrep && g.zstart[g.nprob] + preps[i].nb <= 65535; ++i) {
-        g.prob[g.nprob] = preps[i].pp;
-        g.zstart[g.nprob + 1] = g.zstart[g.nprob] + preps[i].nb;
-        ++g.nprob;
-        bytes += preps[i].bytes;
-      }
-      const hipError_t e = run(MUON_K_PREP, 0, bytes, s, [&]() { return launch_prep_group(g, s); });
-      if (e != hipSuccess) return e;
-      i0 = i;
-    }
-    for (size_t i0 = 0; i0 < norms.size(); i0 += kMaxNorm) {
-      NormGroup g{};
-      double bytes = 0;
-      for (size_t i = i0; i < norms.size() && i < i0 + kMaxNorm; ++i) {
-        g.prob[g.nprob] = norms[i].first;
-        g.start[g.nprob + 1] = g.start[g.nprob] + norms[i].second;
-        ++g.nprob;
-        bytes += (double)norms[i].second * norms[i].first.tiles * 4;
-      }
-      const hipError_t e = run(MUON_K_NORM, 0, bytes, s, [&]() { return launch_norm_group(g, s); });
-      if (e != hipSuccess) return e;
-    }
-    hipError_t e = ns_iterations(jobs, cfg, s);
+    hipError_t e = launch_stage(st, s);
+    if (e != hipSuccess) return e;
+    e = ns_iterations(jobs, cfg, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -1110,11 +1114,10 @@ int check_groups(const muon_group* groups, int64_t ng, const muon_hparams* hp) {
 // Momentum (+ orientation and norm partials) and the norm finalize of one pass
 // of one group: one Newton-Schulz job per row block, appended to `jobs`;
 // *obuf receives where the pass's O [np_][rows][cols] is assembled.
-int stage_group(const GroupPlan& P, const muon_hparams* hp, char* ws, int64_t c0, int64_t np_, hipStream_t s,
+int stage_group(const GroupPlan& P, const muon_hparams* hp, char* ws, int64_t c0, int64_t np_, StageLaunches& st,
                 std::vector<NsJob>& jobs, void** obuf) {
   const muon_group* g = P.g;
   const double ges = (double)esize(g->grad_dtype), mes = (double)esize(g->mom_dtype);
-  hipError_t e;
   for (const Block& B : P.blocks) {
     const Geom& ge = B.ge;
     const Layout& L = B.L;
@@ -1139,11 +1142,9 @@ int stage_group(const GroupPlan& P, const muon_hparams* hp, char* ws, int64_t c0
       pp.X = bws + L.X0 + (size_t)(s0 * B.H) * ge.mp * ge.np * (size_t)oes;
       pp.X_bs = ge.mp * ge.np;
       pp.partial = (float*)(bws + L.partial) + s0 * B.H * L.tiles;
-      e = run(MUON_K_PREP, 0, (double)k * B.h * g->cols * (ges + 2 * mes + oes), s,
-              [&]() { return launch_prep(pp, (int)(k * B.H), s); });
-      if (e != hipSuccess) return hip_fail(e, "momentum kernel");
+      st.preps.push_back({pp, (int)(k * B.H), (double)k * B.h * g->cols * (ges + 2 * mes + oes)});
     }
-    if ((e = norm_finalize(ge, np_ * B.H, hp->ns.eps, bws, L, s)) != hipSuccess) return hip_fail(e, "norm kernel");
+    if (!path128(ge)) st.norms.push_back({norm_params(L, hp->ns.eps, bws), (int)(np_ * B.H)});
     // The last update writes O in parameter orientation ([n][rows][cols],
     // contiguous): a whole group into the X buffer its last iteration does not
     // read, row blocks into the group's O buffer at their row offset.
@@ -1264,14 +1265,17 @@ int muon_step_groups(const muon_group* groups, int64_t ngroups, const muon_hpara
   for (int64_t c = 0; c < passes; ++c) {
     std::vector<NsJob> jobs;
     std::vector<std::pair<const GroupPlan*, void*>> who;
+    StageLaunches st;
     for (const GroupPlan& P : plans) {
       if (!P.live || c * P.pc >= P.g->n) continue;
       const int64_t c0 = c * P.pc, np_ = std::min<int64_t>(P.pc, P.g->n - c0);
       void* obuf = nullptr;
-      if ((rc = stage_group(P, hp, (char*)workspace + P.offset, c0, np_, s, jobs, &obuf))) return rc;
+      if ((rc = stage_group(P, hp, (char*)workspace + P.offset, c0, np_, st, jobs, &obuf))) return rc;
       who.emplace_back(&P, obuf);
     }
-    hipError_t e = ns_iterations(jobs, hp->ns, s);
+    hipError_t e = launch_stage(st, s);
+    if (e != hipSuccess) return hip_fail(e, "momentum or norm kernel");
+    e = ns_iterations(jobs, hp->ns, s);
     if (e != hipSuccess) return hip_fail(e, "Newton-Schulz kernels");
     for (const auto& [pp, obuf] : who) {
       const GroupPlan& P = *pp;

@@ -139,13 +139,11 @@ struct ApplyParams {
 hipError_t launch_gemm_bf16(const GemmGroup& g, bool syrk, bool nn, int tile, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmParams& p, bool nn, bool syrk, hipStream_t s);
 int gemm_f32_tile();    // output tile edge of the fp32 GEMM (divides kPadF32)
-hipError_t launch_prep(const PrepParams& p, int nb, hipStream_t s);
-hipError_t launch_norm(const NormParams& p, int nb, hipStream_t s);
-// Several problems in one launch of the load kernel (problem i: grid z
-// indices zstart[i] .. zstart[i + 1] - 1, one per matrix; at most 65535 in
-// all) or of the norm finalize (problem i: workgroups start[i] ..
-// start[i + 1] - 1).  A PrepParams carries two pointer tables, so a launch
-// holds at most four.
+// The load kernel and the norm finalize take several problems per launch:
+// load-kernel problem i owns grid z indices zstart[i] .. zstart[i + 1] - 1,
+// one per matrix (at most 65535 in all), norm problem i owns workgroups
+// start[i] .. start[i + 1] - 1.  A PrepParams carries two pointer tables, so a
+// load launch holds at most four problems.
 constexpr int kMaxPrep = 4;
 struct PrepGroup {
   PrepParams prob[kMaxPrep];
