@@ -221,24 +221,18 @@ __global__ __launch_bounds__(512, 1) void updgram128_kernel(const UpdGram128Grou
   // Pipeline.  Per wave, vector-memory operations are issued in this order:
   // B (4, update modes), X_0 (4), X_1 (4 when nsub > 1), then per sub-tile
   // jj: X_{jj+2} (4 when jj + 2 < nsub) and the 4 stores of X'_jj (update
-  // modes).  Sub-tile jj's loads have landed once at most the operations
-  // issued after them are pending.
+  // modes).  The loads complete in issue order, but a store may complete
+  // before loads issued ahead of it, so the count a wait allows covers the
+  // loads issued after X_jj only (X_{jj+1}): with X_jj pending, those four
+  // are pending too and the count cannot drop that low, whatever the stores
+  // do.  (Counting the stores issued after X_jj as well lets the wait return
+  // with X_jj still in flight once they complete early.)
   dma_x(0, 0);
   if (nsub > 1) dma_x(1, 1);
 #pragma unroll 1
   for (int jj = 0; jj < nsub; ++jj) {
     const int buf = jj % NXB;
-    if constexpr (UPD) {
-      if (jj == 0) {
-        if (nsub > 1) wait_vmcnt<4>(); else wait_vmcnt<0>();
-      } else if (jj == 1) {
-        if (nsub > 2) wait_vmcnt<8>(); else wait_vmcnt<4>();
-      } else {
-        if (jj + 1 < nsub) wait_vmcnt<12>(); else wait_vmcnt<8>();
-      }
-    } else {
-      if (jj + 1 < nsub) wait_vmcnt<4>(); else wait_vmcnt<0>();
-    }
+    if (jj + 1 < nsub) wait_vmcnt<4>(); else wait_vmcnt<0>();
     __syncthreads();  // X_jj (and B) visible; every wave is done with sub-tile jj - 1
     if (jj + 2 < nsub) dma_x(jj + 2, (jj + 2) % NXB);
     const uint32_t xb = Xs + (uint32_t)(buf * X_BYTES);
