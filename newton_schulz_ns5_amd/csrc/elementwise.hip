@@ -233,9 +233,12 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const SplitSumParams p) 
 
 // NorMuon row statistics: one wave64 per row.  Lane l sums the squares of
 // elements 512 t + 8 l + e (t = 0, 1, ...; e = 0..7) in that order.
-__global__ __launch_bounds__(256) void rowstat_kernel(const RowStatParams p) {
+__global__ __launch_bounds__(256) void rowstat_kernel(const RowStatGroup grp) {
+  int pi = 0;
+  while (pi + 1 < grp.nprob && (int)blockIdx.y >= grp.start[pi + 1]) ++pi;
+  const RowStatParams& p = grp.prob[pi];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int b = blockIdx.y;
+  const int b = (int)blockIdx.y - grp.start[pi];
   const int r = blockIdx.x * 4 + wave;
   if (r >= p.rows) return;
   const bool bf = p.o_dtype == MUON_BF16;
@@ -308,13 +311,33 @@ __global__ __launch_bounds__(256) void rowstat_kernel(const RowStatParams p) {
 
 // rho[b] = ||O||_F / ||diag(d) O||_F = sqrt(sum ms / sum d^2 ms); 0 when the
 // normalized matrix is zero.
-__global__ __launch_bounds__(256) void rho_kernel(const RhoParams p) {
+__global__ __launch_bounds__(256) void rho_kernel(const RhoGroup grp) {
   __shared__ float red[4];
-  const int b = blockIdx.x;
+  int pi = 0;
+  while (pi + 1 < grp.nprob && (int)blockIdx.x >= grp.start[pi + 1]) ++pi;
+  const RhoParams& p = grp.prob[pi];
+  const int b = (int)blockIdx.x - grp.start[pi];
+  const float* ms = p.ms + (int64_t)b * p.rows;
+  const float* qq = p.q + (int64_t)b * p.rows;
   float a = 0.f, q = 0.f;
-  for (int i = threadIdx.x; i < p.rows; i += 256) {
-    a += p.ms[(int64_t)b * p.rows + i];
-    q += p.q[(int64_t)b * p.rows + i];
+  int i = threadIdx.x;
+  // Four rows of each in flight per thread, added one by one in row order.
+  for (; i + 3 * 256 < p.rows; i += 4 * 256) {
+    float va[4], vq[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      va[k] = ms[i + 256 * k];
+      vq[k] = qq[i + 256 * k];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      a += va[k];
+      q += vq[k];
+    }
+  }
+  for (; i < p.rows; i += 256) {
+    a += ms[i];
+    q += qq[i];
   }
   const float sa = block_sum(a, red);
   __syncthreads();
@@ -324,9 +347,12 @@ __global__ __launch_bounds__(256) void rho_kernel(const RhoParams p) {
 
 // One wave64 per row.  mode 0: W <- decay W - coef_r O (fp32 fused
 // multiply-add, one rounding) and the optional bf16 copy; mode 1: O <- coef_r O.
-__global__ __launch_bounds__(256) void apply_kernel(const ApplyParams p) {
+__global__ __launch_bounds__(256) void apply_kernel(const ApplyGroup grp) {
+  int pi = 0;
+  while (pi + 1 < grp.nprob && (int)blockIdx.y >= grp.start[pi + 1]) ++pi;
+  const ApplyParams& p = grp.prob[pi];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int b = blockIdx.y;
+  const int b = (int)blockIdx.y - grp.start[pi];
   const int r = blockIdx.x * 4 + wave;
   if (r >= p.rows) return;
   const bool bf = p.o_dtype == MUON_BF16;
@@ -460,19 +486,69 @@ hipError_t launch_split_sum(const SplitSumParams& p, int nb, hipStream_t s) {
   return launch_kernel(split_sum_kernel, dim3((unsigned)((int64_t)p.mp * p.mp / 8 / 256), nb), p, s);
 }
 
+// Grids of the grouped NorMuon / update launches: problem i owns grid y (or,
+// for rho, x) indices start[i] .. start[i + 1] - 1, one per matrix (at most
+// 65535 in all for y); the row extent is the largest problem's.
+template <typename G>
+static bool group_ok(const G& g, int kmax) {
+  if (g.nprob < 1 || g.nprob > kmax || g.start[0] != 0) return false;
+  for (int i = 0; i < g.nprob; ++i)
+    if (g.start[i + 1] < g.start[i]) return false;
+  return true;
+}
+
+hipError_t launch_rowstat_group(const RowStatGroup& g, hipStream_t s) {
+  if (!group_ok(g, kMaxRowStat)) return hipErrorInvalidValue;
+  int rows = 0;
+  for (int i = 0; i < g.nprob; ++i) rows = g.prob[i].rows > rows ? g.prob[i].rows : rows;
+  const int nb = g.start[g.nprob];
+  if (nb <= 0 || rows <= 0) return hipSuccess;
+  if (nb > 65535) return hipErrorInvalidValue;
+  return launch_kernel(rowstat_kernel, dim3((rows + 3) / 4, nb), g, s);
+}
+
+hipError_t launch_rho_group(const RhoGroup& g, hipStream_t s) {
+  if (!group_ok(g, kMaxRho)) return hipErrorInvalidValue;
+  const int nb = g.start[g.nprob];
+  if (nb <= 0) return hipSuccess;
+  return launch_kernel(rho_kernel, dim3(nb), g, s);
+}
+
+hipError_t launch_apply_group(const ApplyGroup& g, hipStream_t s) {
+  if (!group_ok(g, kMaxApply)) return hipErrorInvalidValue;
+  int rows = 0;
+  for (int i = 0; i < g.nprob; ++i) rows = g.prob[i].rows > rows ? g.prob[i].rows : rows;
+  const int nb = g.start[g.nprob];
+  if (nb <= 0 || rows <= 0) return hipSuccess;
+  if (nb > 65535) return hipErrorInvalidValue;
+  return launch_kernel(apply_kernel, dim3((rows + 3) / 4, nb), g, s);
+}
+
 hipError_t launch_rowstat(const RowStatParams& p, int nb, hipStream_t s) {
   if (nb <= 0 || p.rows <= 0) return hipSuccess;
-  return launch_kernel(rowstat_kernel, dim3((p.rows + 3) / 4, nb), p, s);
+  RowStatGroup g{};
+  g.prob[0] = p;
+  g.start[1] = nb;
+  g.nprob = 1;
+  return launch_rowstat_group(g, s);
 }
 
 hipError_t launch_rho(const RhoParams& p, int nb, hipStream_t s) {
   if (nb <= 0) return hipSuccess;
-  return launch_kernel(rho_kernel, dim3(nb), p, s);
+  RhoGroup g{};
+  g.prob[0] = p;
+  g.start[1] = nb;
+  g.nprob = 1;
+  return launch_rho_group(g, s);
 }
 
 hipError_t launch_apply(const ApplyParams& p, int nb, hipStream_t s) {
   if (nb <= 0 || p.rows <= 0) return hipSuccess;
-  return launch_kernel(apply_kernel, dim3((p.rows + 3) / 4, nb), p, s);
+  ApplyGroup g{};
+  g.prob[0] = p;
+  g.start[1] = nb;
+  g.nprob = 1;
+  return launch_apply_group(g, s);
 }
 
 }  // namespace muon

@@ -1163,9 +1163,50 @@ int stage_group(const GroupPlan& P, const muon_hparams* hp, char* ws, int64_t c0
   return MUON_OK;
 }
 
-// NorMuon (when on) and the weight update of one pass of one group.
-int finish_group(const GroupPlan& P, const muon_hparams* hp, char* ws, int64_t c0, int64_t np_, void* obuf,
-                 hipStream_t s) {
+// NorMuon and weight-update work of one pass, gathered over every group and
+// launched a few problems at a time (row statistics of every group, then
+// their rho, then the updates).
+struct FinishLaunches {
+  struct RS { RowStatParams p; int nb; double bytes; };
+  struct RH { RhoParams p; int nb; double bytes; };
+  struct AP { ApplyParams p; int nb; double bytes; };
+  std::vector<RS> rowstats;
+  std::vector<RH> rhos;
+  std::vector<AP> applies;
+};
+
+// Launches of one grouped kernel over `v`, at most `kmax` problems and 65535
+// matrices per launch.
+template <typename Group, typename Item, typename Launch>
+hipError_t launch_grouped(const std::vector<Item>& v, int kmax, int cls, hipStream_t s, Launch&& launch) {
+  for (size_t i0 = 0; i0 < v.size();) {
+    Group g{};
+    double bytes = 0;
+    size_t i = i0;
+    for (; i < v.size() && g.nprob < kmax && g.start[g.nprob] + v[i].nb <= 65535; ++i) {
+      g.prob[g.nprob] = v[i].p;
+      g.start[g.nprob + 1] = g.start[g.nprob] + v[i].nb;
+      ++g.nprob;
+      bytes += v[i].bytes;
+    }
+    const hipError_t e = run(cls, 0, bytes, s, [&]() { return launch(g, s); });
+    if (e != hipSuccess) return e;
+    i0 = i;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_finish(const FinishLaunches& f, hipStream_t s) {
+  hipError_t e = launch_grouped<RowStatGroup>(f.rowstats, kMaxRowStat, MUON_K_ROWSTAT, s, launch_rowstat_group);
+  if (e != hipSuccess) return e;
+  if ((e = launch_grouped<RhoGroup>(f.rhos, kMaxRho, MUON_K_RHO, s, launch_rho_group)) != hipSuccess) return e;
+  return launch_grouped<ApplyGroup>(f.applies, kMaxApply, MUON_K_APPLY, s, launch_apply_group);
+}
+
+// NorMuon (when on) and the weight update of one pass of one group, appended
+// to `f`.
+void finish_group(const GroupPlan& P, const muon_hparams* hp, char* ws, int64_t c0, int64_t np_, void* obuf,
+                  FinishLaunches& f) {
   const muon_group* g = P.g;
   const bool nm = hp->normuon != 0;
   const int32_t odt = hp->ns.compute_dtype == MUON_BF16 ? MUON_BF16 : MUON_F32;
@@ -1175,7 +1216,6 @@ int finish_group(const GroupPlan& P, const muon_hparams* hp, char* ws, int64_t c
   const double ratio = (double)fan_out / (double)fan_in;
   const float lr_eff = (float)((double)hp->lr * std::sqrt(ratio > 1.0 ? ratio : 1.0) * (double)hp->extra_scale);
   const float decay = (float)(1.0 - (double)hp->lr * (double)hp->weight_decay);
-  hipError_t e;
   if (nm) {
     for (int64_t s0 = 0; s0 < np_; s0 += kMaxParams) {
       const int64_t k = (np_ - s0) < kMaxParams ? (np_ - s0) : kMaxParams;
@@ -1188,12 +1228,10 @@ int finish_group(const GroupPlan& P, const muon_hparams* hp, char* ws, int64_t c
       r2.ms = (float*)(ws + P.nm_ms) + s0 * g->rows;
       r2.q = (float*)(ws + P.nm_q) + s0 * g->rows;
       for (int64_t i = 0; i < k; ++i) r2.v_tab[i] = g->var[c0 + s0 + i];
-      e = run(MUON_K_ROWSTAT, 0, (double)k * (P.pelems * oes + g->rows * 8), s, [&]() { return launch_rowstat(r2, (int)k, s); });
-      if (e != hipSuccess) return hip_fail(e, "row statistics kernel");
+      f.rowstats.push_back({r2, (int)k, (double)k * (P.pelems * oes + g->rows * 8)});
     }
     RhoParams hpm{(float*)(ws + P.nm_ms), (float*)(ws + P.nm_q), (int)g->rows, (float*)(ws + P.nm_rho)};
-    e = run(MUON_K_RHO, 0, (double)np_ * g->rows * 8, s, [&]() { return launch_rho(hpm, (int)np_, s); });
-    if (e != hipSuccess) return hip_fail(e, "rho kernel");
+    f.rhos.push_back({hpm, (int)np_, (double)np_ * g->rows * 8});
   }
   for (int64_t s0 = 0; s0 < np_; s0 += kMaxParams) {
     const int64_t k = (np_ - s0) < kMaxParams ? (np_ - s0) : kMaxParams;
@@ -1211,10 +1249,8 @@ int finish_group(const GroupPlan& P, const muon_hparams* hp, char* ws, int64_t c
       ap.wm[i] = g->model_dtype == MUON_BF16 ? g->w_model[c0 + s0 + i] : nullptr;
     }
     const double wb = g->model_dtype == MUON_BF16 ? 10 : 8;
-    e = run(MUON_K_APPLY, 0, (double)k * P.pelems * (oes + wb), s, [&]() { return launch_apply(ap, (int)k, s); });
-    if (e != hipSuccess) return hip_fail(e, "update kernel");
+    f.applies.push_back({ap, (int)k, (double)k * P.pelems * (oes + wb)});
   }
-  return MUON_OK;
 }
 
 }  // namespace
@@ -1277,11 +1313,13 @@ int muon_step_groups(const muon_group* groups, int64_t ngroups, const muon_hpara
     if (e != hipSuccess) return hip_fail(e, "momentum or norm kernel");
     e = ns_iterations(jobs, hp->ns, s);
     if (e != hipSuccess) return hip_fail(e, "Newton-Schulz kernels");
+    FinishLaunches f;
     for (const auto& [pp, obuf] : who) {
       const GroupPlan& P = *pp;
       const int64_t c0 = c * P.pc, np_ = std::min<int64_t>(P.pc, P.g->n - c0);
-      if ((rc = finish_group(P, hp, (char*)workspace + P.offset, c0, np_, obuf, s))) return rc;
+      finish_group(P, hp, (char*)workspace + P.offset, c0, np_, obuf, f);
     }
+    if ((e = launch_finish(f, s)) != hipSuccess) return hip_fail(e, "NorMuon or update kernels");
   }
   return ok();
 }

@@ -201,6 +201,28 @@ hipError_t launch_gram128(const UpdGram128Group& g, hipStream_t s);
 hipError_t launch_rowstat(const RowStatParams& p, int nb, hipStream_t s);
 hipError_t launch_rho(const RhoParams& p, int nb, hipStream_t s);
 hipError_t launch_apply(const ApplyParams& p, int nb, hipStream_t s);
+// The same three for several problems per launch (the step's shape groups):
+// problem i owns matrices start[i] .. start[i + 1] - 1 of the launch.
+constexpr int kMaxRowStat = 4, kMaxRho = 8, kMaxApply = 4;
+struct RowStatGroup {
+  RowStatParams prob[kMaxRowStat];
+  int32_t start[kMaxRowStat + 1];
+  int32_t nprob;
+};
+struct RhoGroup {
+  RhoParams prob[kMaxRho];
+  int32_t start[kMaxRho + 1];
+  int32_t nprob;
+};
+struct ApplyGroup {
+  ApplyParams prob[kMaxApply];
+  int32_t start[kMaxApply + 1];
+  int32_t nprob;
+};
+static_assert(sizeof(RowStatGroup) <= 4096 && sizeof(ApplyGroup) <= 4096, "kernel argument block of one launch");
+hipError_t launch_rowstat_group(const RowStatGroup& g, hipStream_t s);
+hipError_t launch_rho_group(const RhoGroup& g, hipStream_t s);
+hipError_t launch_apply_group(const ApplyGroup& g, hipStream_t s);
 
 // Tile edge the bf16 GEMM uses for an M x N output (depends on shape only).
 // An output of at most 512 rows has at most 2 tile rows of 256 (a symmetric
