@@ -248,12 +248,15 @@ def test_group_size_invariance_bitwise():
 
 
 def test_grouped_step_equals_per_group_bitwise():
-    # muon_step_groups over four shape groups (a wide, a tall, a per-head and
-    # a ragged one, each a different GEMM tile edge or orientation) gives every
-    # parameter exactly the result of its own group's muon_step_group call,
-    # over two steps, with NorMuon and the bf16 model copy.
+    # muon_step_groups over six shape groups (a wide, a tall, a per-head, a
+    # ragged, a 128-row split-Gram and a small one, each a different GEMM tile
+    # edge or orientation; more problems than one launch of the load, row
+    # statistics and update kernels holds) gives every parameter exactly the
+    # result of its own group's muon_step_group call, over two steps, with
+    # NorMuon and the bf16 model copy.
     torch = torch_cuda()
-    specs = [((256, 512), 2, 1), ((640, 256), 1, 1), ((512, 384), 2, 4), ((300, 130), 3, 1)]
+    specs = [((256, 512), 2, 1), ((640, 256), 1, 1), ((512, 384), 2, 4), ((300, 130), 3, 1), ((128, 4096), 2, 1),
+             ((96, 200), 5, 1)]
 
     def state(seed):
         out = []
