@@ -1112,8 +1112,9 @@ int check_groups(const muon_group* groups, int64_t ng, const muon_hparams* hp) {
 }
 
 // Momentum (+ orientation and norm partials) and the norm finalize of one pass
-// of one group: one Newton-Schulz job per row block, appended to `jobs`;
-// *obuf receives where the pass's O [np_][rows][cols] is assembled.
+// of one group, appended to `st` (launched once all groups are staged), and
+// one Newton-Schulz job per row block, appended to `jobs`; *obuf receives
+// where the pass's O [np_][rows][cols] is assembled.
 int stage_group(const GroupPlan& P, const muon_hparams* hp, char* ws, int64_t c0, int64_t np_, StageLaunches& st,
                 std::vector<NsJob>& jobs, void** obuf) {
   const muon_group* g = P.g;
