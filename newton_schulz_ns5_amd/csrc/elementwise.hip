@@ -135,15 +135,15 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepGroup grp) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) u[e] = valid > 0 ? tmp[e] : 0.f;
     } else {
-      const int pi = bz / p.heads, hd = bz - pi * p.heads;
+      const int par = bz / p.heads, hd = bz - par * p.heads;
       const bool mom_bf = p.mom_dtype == MUON_BF16;
       const int64_t off = (int64_t)(hd * p.rows + gr) * p.param_cols + gc;
       const int valid = gr < p.rows ? p.cols - gc : 0;
       const bool vec = (p.param_cols & 7) == 0;
       float g[8], m[8];
       if (valid > 0) {
-        load8((const uint8_t*)p.grad[pi] + off * (src_bf ? 2 : 4), valid, src_bf, vec, g);
-        load8((const uint8_t*)p.mom[pi] + off * (mom_bf ? 2 : 4), valid, mom_bf, vec, m);
+        load8((const uint8_t*)p.grad[par] + off * (src_bf ? 2 : 4), valid, src_bf, vec, g);
+        load8((const uint8_t*)p.mom[par] + off * (mom_bf ? 2 : 4), valid, mom_bf, vec, m);
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepGroup grp) {
           u[e] = 0.f;
         }
       }
-      if (valid > 0) store8v((uint8_t*)p.mom[pi] + off * (mom_bf ? 2 : 4), valid, mom_bf, vec, m);
+      if (valid > 0) store8v((uint8_t*)p.mom[par] + off * (mom_bf ? 2 : 4), valid, mom_bf, vec, m);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
