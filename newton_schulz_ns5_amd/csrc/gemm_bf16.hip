@@ -45,27 +45,53 @@ constexpr int ROWB = KS * 2;  // bytes per LDS row
 // Workgroup -> (problem, batch, tile row, tile col).
 //
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup w runs on
-// XCD w % 8).  Logical tiles are handed out in rounds of 8 x 32: in each round
-// XCD x takes the 32 consecutive logical tiles [x*32, x*32 + 32), so tiles
-// that share operand panels run together on one XCD's L2 while every XCD
-// moves through the problem list at the same pace.  Within a problem, tiles
-// are ordered in bands of 4 tile rows (a band's tile columns one after the
-// other, before the next band), so 32 consecutive tiles read about 12
-// operand panels; SYRK bands cover the upper triangle only.
+// XCD w % 8, as the k = w / 8-th of that XCD's queue), and each XCD's 32 CUs
+// drain their own queue.  The launch's tiles are numbered problem after
+// problem, longest K first.  Two orders:
+//  - rounds (default): the tile numbers are handed out in rounds of 8 x 32,
+//    XCD x taking the 32 consecutive tiles [x*32, x*32 + 32) of each round,
+//    so tiles that share operand panels run together on one XCD's L2 while
+//    every XCD moves through the problem list at the same pace;
+//  - balanced (g.balance): every XCD gets an equal share of every problem
+//    and works through the problems in order, so the last waves of all XCDs
+//    end together when long and short tiles mix (with rounds, the XCDs that
+//    draw the long tiles of the round where the long problems end finish
+//    far behind the others).  XCD x's share of a problem whose tiles are
+//    numbered c0 .. c1 - 1 is the number of i in [c0, c1) with i % 8 == x,
+//    so the shares add up to exactly the workgroups each XCD is sent.
+//    Within a problem the XCDs still move together in rounds of 8 x 32
+//    tiles; the tail after the last full round is cut into 8 contiguous
+//    pieces, one per XCD.
+// Within a problem, tiles are ordered in bands of 4 tile rows (a band's tile
+// columns one after the other, before the next band), so 32 consecutive
+// tiles read about 12 operand panels; SYRK bands cover the upper triangle
+// only.
 template <bool SYRK>
 __device__ __forceinline__ const GemmParams& decode_tile(const GemmGroup& g, int& b, int& tm, int& tn) {
   constexpr int CH = 32;
-  const int G = gridDim.x, wg = blockIdx.x;
-  const int full = (G / (8 * CH)) * (8 * CH);
-  int pid = wg;
-  if (wg < full) {
-    const int x = wg & 7, k = wg >> 3;
-    pid = (k / CH) * (8 * CH) + x * CH + (k % CH);
+  const int wg = blockIdx.x, x = wg & 7, k = wg >> 3;
+  int pi = 0, local;
+  if (!g.balance) {
+    const int G = gridDim.x;
+    const int full = (G / (8 * CH)) * (8 * CH);
+    const int pid = wg < full ? (k / CH) * (8 * CH) + x * CH + (k % CH) : wg;
+    while (pi + 1 < g.nprob && pid >= g.tile_start[pi + 1]) ++pi;
+    local = pid - g.tile_start[pi];
+  } else {
+    // Number of i in [0, n) with i % 8 == xx (n >= 0).
+    auto share = [](int n, int xx) { return (n + 7 - xx) >> 3; };
+    while (pi + 1 < g.nprob && k >= share(g.tile_start[pi + 1], x)) ++pi;
+    const int c0 = g.tile_start[pi], c1 = g.tile_start[pi + 1];
+    const int j = k - share(c0, x);  // position in XCD x's share of this problem
+    const int rounds = (c1 - c0) / (8 * CH);
+    if (j < rounds * CH) {
+      local = (j / CH) * (8 * CH) + x * CH + j % CH;
+    } else {
+      local = rounds * 8 * CH + (j - rounds * CH);
+      for (int xx = 0; xx < x; ++xx) local += share(c1, xx) - share(c0, xx) - rounds * CH;
+    }
   }
-  int pi = 0;
-  while (pi + 1 < g.nprob && pid >= g.tile_start[pi + 1]) ++pi;
   const GemmParams& p = g.prob[pi];
-  const int local = pid - g.tile_start[pi];
   b = local / p.tiles_per_batch;
   int t = local - b * p.tiles_per_batch;
   if constexpr (SYRK) {

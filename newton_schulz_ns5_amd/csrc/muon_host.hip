@@ -236,9 +236,52 @@ struct NsJob {
   int64_t x0_bs = 0;
 };
 
+// Estimated end of a launch's slowest XCD, in units of K: XCD x runs, in
+// problem order, its tiles of each problem p (which ones: the kernel's tile
+// order, rounds or balanced), each taking dur[p], on whichever of its 32 CUs
+// frees first.
+double xcd_makespan(const GemmGroup& g, const int* dur, bool balance) {
+  constexpr int CH = 32, NCU = 32;
+  const int G = g.tile_start[g.nprob];
+  const int full = (G / (8 * CH)) * (8 * CH);
+  // Tiles numbered below n that XCD x runs (n a problem boundary).
+  auto before = [&](int n, int x) -> int64_t {
+    if (balance) return (n + 7 - x) / 8;
+    if (n <= full) return (int64_t)(n / (8 * CH)) * CH + std::min(std::max(n % (8 * CH) - x * CH, 0), CH);
+    return (int64_t)(full / (8 * CH)) * CH + (n - full + 7 - x) / 8;
+  };
+  double worst = 0;
+  for (int x = 0; x < 8; ++x) {
+    double f[NCU] = {};  // CU free times, ascending
+    for (int p = 0; p < g.nprob; ++p) {
+      int64_t n = before(g.tile_start[p + 1], x) - before(g.tile_start[p], x);
+      const double d = dur[p];
+      while (n > 0) {
+        if (n >= NCU && f[NCU - 1] - f[0] <= d) {
+          // Every CU takes one tile of each batch of NCU (a CU that takes a
+          // tile frees after all the others).
+          const int64_t k = n / NCU;
+          for (double& v : f) v += (double)k * d;
+          n -= k * NCU;
+          continue;
+        }
+        double v = f[0] + d;
+        int i = 1;
+        for (; i < NCU && f[i] < v; ++i) f[i - 1] = f[i];
+        f[i - 1] = v;
+        --n;
+      }
+    }
+    worst = std::max(worst, f[NCU - 1]);
+  }
+  return worst;
+}
+
 // Launch one phase (Gram, poly or update) of several jobs: problems with the
 // same tile edge share a launch (at most kMaxProblems each), longest K first
-// so that the long tiles start in the first waves.
+// so that the long tiles start in the first waves.  Where K differs between
+// the problems of a launch, the balanced tile order is taken if it is
+// expected to end the launch at least 3 % sooner.
 hipError_t launch_phase(std::vector<GemmParams>& probs, bool syrk, bool nn, int cls, hipStream_t s) {
   for (int tile : {256, 128}) {
     std::vector<GemmParams*> sel;
@@ -263,6 +306,14 @@ hipError_t launch_phase(std::vector<GemmParams>& probs, bool syrk, bool nn, int 
       // Tile indices are 32-bit in the kernel (and a grid holds < 2^31 workgroups).
       if (tiles > INT32_MAX) return hipErrorInvalidValue;
       grp.tile_start[grp.nprob] = (int32_t)tiles;
+      grp.balance = 0;
+      int dur[kMaxProblems];
+      bool mixed = false;
+      for (int i = 0; i < grp.nprob; ++i) {
+        dur[i] = kwg(&grp.prob[i]);
+        mixed |= dur[i] != dur[0];
+      }
+      if (mixed && xcd_makespan(grp, dur, true) < 0.97 * xcd_makespan(grp, dur, false)) grp.balance = 1;
       double fl = 0, by = 0;  // algorithmic FLOPs and bytes of this launch
       for (int i = 0; i < grp.nprob; ++i) {
         fl += grp.prob[i].flop;

@@ -54,6 +54,7 @@ struct GemmGroup {
   GemmParams prob[kMaxProblems];
   int32_t nprob;
   int32_t tile_start[kMaxProblems + 1];
+  int32_t balance;  // 1: every XCD takes an equal share of every problem (else rounds of 8 x 32 tiles)
 };
 
 // ---- load / momentum / orientation / norm partials ------------------------
