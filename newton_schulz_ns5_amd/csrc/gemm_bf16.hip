@@ -522,34 +522,42 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
     const int j0 = tn * BT;
     // Almost every tile: all its rows and columns are stored, no D, aligned
     // rows.  Then both passes store alpha S (bf16, or fp32 for split-K
-    // partial products) with 16-byte stores; the transposed pass recomputes
-    // alpha S, so its values are bitwise those of the row pass.  On a SYRK diagonal tile the row pass stores
-    // the chunks on or above the diagonal (element stores where the diagonal
-    // crosses a chunk) and the transposed pass mirrors the strictly upper
-    // part, so the stored matrix is exactly symmetric.
+    // partial products) in whole 8-element chunks with 16-byte stores; the
+    // transposed pass recomputes alpha S, so its values are bitwise those of
+    // the row pass.  On a SYRK diagonal tile the row pass stores the chunks
+    // that reach the diagonal or above it and the transposed pass mirrors the
+    // chunks that reach below it.  Where the diagonal crosses a chunk, both
+    // passes store it, so the 8 x 8 diagonal blocks of the staged rows are
+    // first made symmetric in S (lower elements := their upper mirrors, all
+    // within one pass: 8-row chunks never straddle a quadrant band): then
+    // both passes store the same bits there, and the stored matrix is exactly
+    // symmetric.
     const bool fast = !Dg && i0 + BT <= Mlim && j0 + BT <= Nlim && (!Cg || cvec) && (!Tg || tvec);
-    // Store elements e0 .. e1 - 1 of v[0..7] at dst (bf16 or fp32); one or
-    // two 16-byte stores when all eight are stored.
-    auto put8 = [&](uint8_t* dst, const float (&v)[8], int e0, int e1) {
+    // Store v[0..7] at dst (bf16 or fp32) with one or two 16-byte stores.
+    auto put8 = [&](uint8_t* dst, const float (&v)[8]) {
       if (obf) {
         u32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = pack_bf2(v[2 * e], v[2 * e + 1]);
-        if (e0 <= 0 && e1 >= 8) {
-          *(u32x4*)dst = w;
-        } else {
-          for (int e = e0; e < e1; ++e) ((uint16_t*)dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-        }
-      } else if (e0 <= 0 && e1 >= 8) {
+        *(u32x4*)dst = w;
+      } else {
         f32x4 w0, w1;
 #pragma unroll
         for (int e = 0; e < 4; ++e) { w0[e] = v[e]; w1[e] = v[4 + e]; }
         *(f32x4*)dst = w0;
         *(f32x4*)(dst + 16) = w1;
-      } else {
-        for (int e = e0; e < e1; ++e) ((float*)dst)[e] = v[e];
       }
     };
+    if (fast && diag) {
+      // Diagonal block d (staged rows 8 d .. 8 d + 7, tile rows and columns
+      // trow(8 d) ..): element (r, c) with r > c takes (c, r).
+      for (int idx = tid; idx < R8 * 64; idx += 256) {
+        const int s0 = (idx >> 6) * 8, r = (idx >> 3) & 7, c = idx & 7;
+        const int t0 = trow(s0);
+        if (r > c) S[(s0 + r) * PITCH + t0 + c] = S[(s0 + c) * PITCH + t0 + r];
+      }
+      __syncthreads();
+    }
     if (fast) {
       if (Cg) {
         const int c8 = (tid % CPR) * 8, r0 = tid / CPR;
@@ -563,27 +571,22 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
           for (int e = 0; e < 4; ++e) { v[e] = alpha * s0[e]; v[4 + e] = alpha * s1[e]; }
           const int tr = trow(rr);
           uint8_t* const dst = Cg + ((int64_t)(i0 + tr) * ldc + j0 + c8) * esz;
-          const int lo = tr - c8;  // columns c8 + e with e >= lo are on or above the diagonal
-          if (!diag || lo <= 0) {
-            put8(dst, v, 0, 8);
-          } else if (lo < 8) {
-            put8(dst, v, lo, 8);
-          }
+          if (!diag || tr < c8 + 8) put8(dst, v);  // the chunk reaches the diagonal or above
         }
       }
       if (Tg) {
 #pragma unroll 2
         for (int idx = tid; idx < BT * R8; idx += 256) {
           const int jj = idx % BT, i8 = (idx / BT) * 8;
-          // mirrored rows i8 + e (tile rows trow(i8) + e) strictly below column jj
+          // mirrored to row jj, columns trow(i8) .. + 7: on a diagonal tile
+          // only where some of them are below the diagonal
           const int ti = trow(i8);
-          const int hi = diag ? jj - ti : 8;
-          if (hi <= 0) continue;
+          if (diag && jj <= ti) continue;
           float v[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = alpha * S[(i8 + e) * PITCH + jj];
           uint8_t* const dst = Tg + ((int64_t)(j0 + jj) * ldt + i0 + ti) * esz;
-          put8(dst, v, 0, hi < 8 ? hi : 8);
+          put8(dst, v);
         }
       }
     } else {
