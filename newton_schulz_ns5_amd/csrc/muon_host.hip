@@ -78,17 +78,29 @@ Geom make_geom(int64_t rows, int64_t cols, int32_t compute) {
 // chip over a long K = n; its Gram is then computed in chunks of about
 // max(4 m, 1024) columns (at most 16), whose fp32 products are summed
 // afterwards (shorter chunks would move more partial products than they save
-// in latency).  The count depends on the shape only, so a matrix's result
-// does not depend on its batch.
+// in latency).  A 128-row matrix takes chunks of about 683 columns (6 for
+// n = 4096): its chunks are also the workgroups of the fused update / Gram
+// kernel, and 40 heads of 4096 columns then fit one wave of workgroups over
+// the chip (8 chunks, 320 workgroups, would need two).  The count depends on
+// the shape only, so a matrix's result does not depend on its batch.
 int gram_ksplit(const Geom& g) {
   if (!g.bf || g.mp > 256) return 1;
-  const int64_t s = g.np / std::max<int64_t>(4 * g.mp, 1024);
+  const int64_t s = g.mp == 128 ? g.np * 3 / 2048 : g.np / std::max<int64_t>(4 * g.mp, 1024);
   return s < 2 ? 1 : (s > kMaxKsplit ? kMaxKsplit : (int)s);
 }
 
 // The 128-row path with a split Gram (fused update/Gram kernels; the norm
 // is finalized by the first iteration's sum-and-polynomial kernel).
 bool path128(const Geom& g) { return g.mp == 128 && gram_ksplit(g) > 1; }
+
+// Column chunks (workgroups per matrix) of the last update of a 128-row
+// matrix written straight to the output by the fused kernel.  No Gram
+// follows, so the chunking is free: every 128-column sub-tile is computed
+// the same way whatever chunk it is in.
+int last_chunks128(const Geom& g) {
+  const int kb = (int)(g.np / 128);
+  return std::max(1, std::min(kb, kb / 8));
+}
 
 // Workspace of `nb` NS problems.
 struct Layout {
@@ -371,7 +383,7 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
     struct Fused { Poly128Params p; int nb; double flop, bytes; };
     std::vector<Sum> sums;
     std::vector<Fused> fused;
-    std::vector<UpdGram> updgram, gram128;
+    std::vector<UpdGram> updgram, gram128, updonly;
     for (size_t k = 0; k < jobs.size(); ++k) {
       const NsJob& J = jobs[k];
       const Geom& g = J.g;
@@ -484,6 +496,13 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
         }
         p.flop = B * 2 * m * m * n; p.bytes = B * (m * m + 2 * m * n) * 2;
         const int ks = gram_ksplit(g);
+        // The last update of a 128-row matrix whose output is the bf16
+        // iterate's own layout (128 real rows, rows np apart, no padded
+        // columns, 16-byte aligned) is written by the fused kernel's
+        // update-only variant.
+        const bool out128 = path128(g) && last && J.out.dtype == MUON_BF16 && !g.tall && g.m == g.mp &&
+                            g.n == g.np && J.out.ldc == g.np && (J.out.sC % 8) == 0 &&
+                            ((uintptr_t)J.out.C & 15) == 0;
         if (path128(g) && !last) {
           // Fused with the next iteration's Gram: X' to the other X buffer
           // and the chunk products of X' X'^T to the split-K buffer.
@@ -496,6 +515,15 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
           u.alpha = 1.f; u.beta = cf.a;
           u.rs = p.rs; u.alpha_pow = 1; u.beta_pow = 1;
           updgram.push_back({u, (int)J.nb, B * 3 * m * m * n, B * ((m * m + 2 * m * n) * 2 + ks * m * m * 4)});
+        } else if (out128) {
+          UpdGram128Params u{};
+          u.B = Bm; u.b_bs = sa;
+          u.X = Xin; u.x_bs = sxin;
+          u.Y = J.out.C; u.y_bs = J.out.sC;
+          u.np = (int)g.np; u.ksplit = last_chunks128(g);
+          u.alpha = 1.f; u.beta = cf.a;
+          u.rs = p.rs; u.alpha_pow = 1; u.beta_pow = 1;
+          updonly.push_back({u, (int)J.nb, p.flop, p.bytes});
         } else {
           upd.push_back(p);
         }
@@ -522,6 +550,7 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
     if ((e = launch_phase(poly, true, false, MUON_K_POLY, s)) != hipSuccess) return e;
     if ((e = launch_phase(upd, false, true, MUON_K_UPDATE, s)) != hipSuccess) return e;
     if ((e = launch_updgram_groups(updgram, MUON_K_UPDATE, false, s)) != hipSuccess) return e;
+    if ((e = launch_updgram_groups(updonly, MUON_K_UPDATE, false, s)) != hipSuccess) return e;
     for (auto& c : cur) c ^= 1;
   }
   return hipSuccess;

@@ -279,6 +279,11 @@ def test_largest_long_side_parity():
     torch.cuda.synchronize()
     got = to_f64(out)
     del out
+    bad = ~np.isfinite(got)
+    if bad.any():  # name where the non-finite values are (rows: the long side)
+        r, c = np.nonzero(bad)
+        raise AssertionError(f"{bad.sum()} non-finite values in rows {r.min()}..{r.max()} "
+                             f"({len(np.unique(r // 128))} 128-row blocks), columns {c.min()}..{c.max()}")
     err = rel_fro(got, oracle.newton_schulz5(storage_f64(x, "bf16")))
     assert err <= TOL["bf16"], err
 
