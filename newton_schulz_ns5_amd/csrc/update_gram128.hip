@@ -28,7 +28,9 @@
 // The same kernel without steps 2-3 computes the first iteration's chunk
 // products from X itself, and without step 4 an update alone.
 // Eight waves (two per SIMD) share each sub-tile's products, so one wave's
-// MFMAs run while the other waits on LDS.  Every LDS address a lane uses is
+// MFMAs run while the other waits on LDS.  Waves 0-3 issue every HBM -> LDS
+// load and waves 4-7 every X' store, so no wave waits on a count that
+// mixes loads and stores.  Every LDS address a lane uses is
 // fixed up front, so the loop issues its LDS accesses with immediate offsets.
 // The chunk edges are the split-K Gram's, multiples of 128 that depend on the
 // matrix shape only, and every sub-tile is computed by the same instruction
@@ -105,38 +107,40 @@ __global__ __launch_bounds__(512, 1) void updgram128_kernel(const UpdGram128Grou
   const float alpha = p.alpha * (p.alpha_pow == 2 ? rsb * rsb : (p.alpha_pow == 1 ? rsb : 1.f));
   const float beta = p.beta * (p.beta_pow == 1 ? rsb : 1.f);
 
-  // B: instruction q (0..3) of a wave fills rows 8 g .. 8 g + 7 (g = 2 wave +
-  // q % 2) of slice q / 2; lane l lands at row 8 g + l / 8, chunk l % 8 and
-  // therefore fetches the chunk (l % 8) ^ ((row / 2) % 8) of that row.
-  if constexpr (UPD) {
+  // B (waves 0-3): instruction q (0..7) of a wave fills rows 8 g .. 8 g + 7
+  // (g = 4 wave + q % 4) of slice q / 4; lane l lands at row 8 g + l / 8,
+  // chunk l % 8 and therefore fetches the chunk (l % 8) ^ ((row / 2) % 8) of
+  // that row.
+  if (UPD && wave < 4) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int s = q >> 1, g = wave * 2 + (q & 1);
+    for (int q = 0; q < 8; ++q) {
+      const int s = q >> 2, g = wave * 4 + (q & 3);
       const int voff = (lane >> 3) * (M * 2) + ((lane & 7) ^ ((4 * g + (lane >> 4)) & 7)) * 16;
       lds_dma16_asm(brw, Bs + (uint32_t)(s * NT_SLICE + 8 * g * 128), voff, 8 * g * (M * 2) + s * 128);
     }
   }
-  // X sub-tile jj, update modes: instruction q (0..3) of a wave fills rows
-  // 16 wave + 4 q .. + 3; lane l lands at row 16 wave + 4 q + l / 16, 16-byte
-  // chunk l % 16, fetching the chunk whose 32-byte block is swizzled by
-  // 2 (row % 4) = 2 (l / 16).
+  // X sub-tile jj (waves 0-3), update modes: instruction q (0..7) of a wave
+  // fills rows 32 wave + 4 q .. + 3; lane l lands at row 32 wave + 4 q +
+  // l / 16, 16-byte chunk l % 16, fetching the chunk whose 32-byte block is
+  // swizzled by 2 (row % 4) = 2 (l / 16).
   // Gram only: the sub-tile goes into the NT layout (it is the Gram's operand
   // as it stands), filled as B is: instruction q fills rows 8 g .. 8 g + 7
-  // (g = 2 wave + q % 2) of slice q / 2.
+  // (g = 4 wave + q % 4) of slice q / 4.
   const int xvoff = UPD ? (lane >> 4) * ldx * 2 + (2 * (((lane & 15) >> 1) ^ (2 * (lane >> 4))) + (lane & 1)) * 16
                         : (lane >> 3) * ldx * 2;
   auto dma_x = [&](int jj, int buf) {
+    if (wave >= 4) return;
     const uint32_t dst = Xs + (uint32_t)(buf * X_BYTES);
     if constexpr (UPD) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = 16 * wave + 4 * q;
+      for (int q = 0; q < 8; ++q) {
+        const int row = 32 * wave + 4 * q;
         lds_dma16_asm(xrw, dst + (uint32_t)(row * XROWB), xvoff, row * ldx * 2 + jj * SUB * 2);
       }
     } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int s = q >> 1, g = wave * 2 + (q & 1);
+      for (int q = 0; q < 8; ++q) {
+        const int s = q >> 2, g = wave * 4 + (q & 3);
         const int voff = xvoff + ((lane & 7) ^ ((4 * g + (lane >> 4)) & 7)) * 16;
         lds_dma16_asm(xrw, dst + (uint32_t)(s * NT_SLICE + 8 * g * 128), voff, 8 * g * ldx * 2 + s * 128 + jj * SUB * 2);
       }
@@ -181,11 +185,13 @@ __global__ __launch_bounds__(512, 1) void updgram128_kernel(const UpdGram128Grou
   for (int q = 0; q < 4; ++q)
     ywl[q] = Ys + (uint32_t)((wa >> 1) * NT_SLICE + (64 * wb + (lane & 31)) * 128 + (((4 * (wa & 1) + q) ^ sw) << 4) +
                              8 * (lane >> 5));
-  // X' rows to HBM: thread -> 16-byte chunk tid % 16 of rows tid / 16 + 32 u;
-  // row (tid / 16) + 32 u has the swizzle (tid / 32) % 8 whatever u.
-  const uint32_t yrd = Ys + (uint32_t)(((tid >> 3) & 1) * NT_SLICE + (tid >> 4) * 128 +
-                                       (((tid & 7) ^ ((tid >> 5) & 7)) << 4));
-  const int yvoff = ((tid >> 4) * ldx + (tid & 15) * 8) * 2;
+  // X' rows to HBM (waves 4-7, t2 = tid - 256): thread -> 16-byte chunk
+  // t2 % 16 of rows t2 / 16 + 16 u (u = 0..7); row t2 / 16 + 16 u has the
+  // swizzle (t2 / 32) % 8 whatever u.
+  const int t2 = tid & 255;
+  const uint32_t yrd = Ys + (uint32_t)(((t2 >> 3) & 1) * NT_SLICE + (t2 >> 4) * 128 +
+                                       (((t2 & 7) ^ ((t2 >> 5) & 7)) << 4));
+  const int yvoff = ((t2 >> 4) * ldx + (t2 & 15) * 8) * 2;
 
   // beta X is added inside the products: X'^T = X^T (B + E) with E = (beta /
   // alpha) I, entered as two bf16 terms (hi + lo, within 2^-16 of the
@@ -218,21 +224,22 @@ __global__ __launch_bounds__(512, 1) void updgram128_kernel(const UpdGram128Grou
 #pragma unroll
     for (int r = 0; r < 16; ++r) accg[j][r] = 0.f;
 
-  // Pipeline.  Per wave, vector-memory operations are issued in this order:
-  // B (4, update modes), X_0 (4), X_1 (4 when nsub > 1), then per sub-tile
-  // jj: X_{jj+2} (4 when jj + 2 < nsub) and the 4 stores of X'_jj (update
-  // modes).  The loads complete in issue order, but a store may complete
-  // before loads issued ahead of it, so the count a wait allows covers the
-  // loads issued after X_jj only (X_{jj+1}): with X_jj pending, those four
-  // are pending too and the count cannot drop that low, whatever the stores
-  // do.  (Counting the stores issued after X_jj as well lets the wait return
-  // with X_jj still in flight once they complete early.)
+  // Pipeline.  Waves 0-3 issue only loads, in this order: B (8, update
+  // modes), X_0 (8), X_1 (8 when nsub > 1), then per sub-tile jj X_{jj+2} (8
+  // when jj + 2 < nsub).  Loads complete in issue order, so waiting until at
+  // most the 8 loads of X_{jj+1} are pending means X_jj has landed; the
+  // barrier after it publishes X_jj to every wave.  Waves 4-7 issue only the
+  // X' stores and never wait on them: a store may complete before loads
+  // issued ahead of it, so a count that mixed the two could return with a
+  // load still in flight.
   dma_x(0, 0);
   if (nsub > 1) dma_x(1, 1);
 #pragma unroll 1
   for (int jj = 0; jj < nsub; ++jj) {
     const int buf = jj % NXB;
-    if (jj + 1 < nsub) wait_vmcnt<4>(); else wait_vmcnt<0>();
+    if (wave < 4) {
+      if (jj + 1 < nsub) wait_vmcnt<8>(); else wait_vmcnt<0>();
+    }
     __syncthreads();  // X_jj (and B) visible; every wave is done with sub-tile jj - 1
     if (jj + 2 < nsub) dma_x(jj + 2, (jj + 2) % NXB);
     const uint32_t xb = Xs + (uint32_t)(buf * X_BYTES);
@@ -279,15 +286,15 @@ __global__ __launch_bounds__(512, 1) void updgram128_kernel(const UpdGram128Grou
           *(lds_u32x2*)(uintptr_t)(ywl[q] + 32 * j * 128) = w;
         }
       __syncthreads();  // the X' sub-tile is complete in LDS
-      {
+      if (wave >= 4) {
         typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-        u32x4 yv[4];
+        u32x4 yv[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) yv[u] = *(const lds_u32x4*)(uintptr_t)(yrd + 4096 * u);
+        for (int u = 0; u < 8; ++u) yv[u] = *(const lds_u32x4*)(uintptr_t)(yrd + 2048 * u);
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 8; ++u)
           __builtin_amdgcn_raw_buffer_store_b128(yv[u], yrs, yvoff,
-                                                 __builtin_amdgcn_readfirstlane(32 * u * ldx * 2 + jj * SUB * 2), 0);
+                                                 __builtin_amdgcn_readfirstlane(16 * u * ldx * 2 + jj * SUB * 2), 0);
       }
     }
     // Gram block j of wave (wa, wb): rows 32 wa .., columns 64 wb + 32 j ...
