@@ -13,10 +13,12 @@
 // is added inside the products.  NN fragments come from the LDS transpose
 // read (ds_read_b64_tr_b16), so the iterate is only ever stored row-major.
 //
-// Work decomposition: one workgroup of 256 threads (four wave64s, 2 x 2) per
-// BT x BT output tile (BT = 256 or 128); each wave owns a (BT/2)^2 sub-tile of
-// 32x32 blocks computed with v_mfma_f32_32x32x16_bf16 (fp32 accumulation in
-// AGPRs).  K advances 64 at a time: each operand row contributes one 128-byte
+// Work decomposition: one workgroup per BT x BT output tile: at BT = 256
+// eight wave64s (2 x 4, two per SIMD, so one wave's MFMAs run while the other
+// waits on a load, a fragment read or the barrier), each owning a 128 x 64
+// sub-tile; at BT = 128 four (2 x 2, two workgroups per CU), each owning
+// 64 x 64.  Sub-tiles are 32x32 blocks computed with
+// v_mfma_f32_32x32x16_bf16 (fp32 accumulation).  K advances 64 at a time: each operand row contributes one 128-byte
 // line per slice, brought by direct HBM -> LDS buffer loads
 // (buffer_load_dwordx4 ... lds) into a ring of five operand slots (160 KiB
 // for BT = 256), about one and a half slices ahead of the multiply.  One
@@ -147,16 +149,22 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 
 // NN: Q is stored [K][N] (N contiguous) instead of [N][K]; its fragments are
 // read with the LDS transpose read (ds_read_b64_tr_b16).
-template <int BT, bool SYRK, bool NN>
-__global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup grp) {
+template <int BT, bool SYRK, bool NN, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_nt_bf16_kernel(const GemmGroup grp) {
   static_assert(!(SYRK && NN), "SYRK products are NT");
-  constexpr int WT = BT / 2;          // wave tile edge
-  constexpr int F = WT / 32;          // 32x32 MFMA blocks per wave tile edge
+  static_assert(NW == 4 || NW == 8, "2 x 2 or 2 x 4 waves");
+  constexpr int NTH = NW * 64;        // threads per workgroup
+  constexpr int WT = BT / 2;          // wave tile rows (two rows of waves)
+  constexpr int WC = BT / (NW / 2);   // wave tile columns
+  constexpr int F = WT / 32;          // 32x32 MFMA block rows per wave tile
+  constexpr int FN = WC / 32;         // 32x32 MFMA block columns per wave tile
+  constexpr int MPS = F / 2;          // MFMAs per slot of a quarter
+  constexpr int NSL = F * FN / MPS;   // slots per quarter
   constexpr int OPB = BT * ROWB;      // bytes of one slot
-  constexpr int RPW = BT / 4;         // operand rows each wave loads per slice
+  constexpr int RPW = BT / NW;        // operand rows each wave loads per slice
   constexpr int DPW = RPW / 8;        // DMA instructions per wave per operand slice (8 rows each)
   constexpr int DQ = DPW / 2;         // DMA instructions per quarter step
-  static_assert(DQ <= F, "one DMA instruction per even slot at most");
+  static_assert(2 * DQ <= NSL && F + FN <= 2 * NSL, "one DMA instruction per even slot, two fragment reads per slot");
   constexpr int RH = BT / 2;          // epilogue: tile rows staged per pass
   constexpr int EPI = RH * (BT + 4) * 4;  // epilogue staging bytes
   constexpr int LDS_BYTES = (NSLOT * OPB > EPI) ? NSLOT * OPB : EPI;
@@ -164,7 +172,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / (NW / 2), wn = wave % (NW / 2);
 
   int b, tm, tn;
   const GemmParams& p = decode_tile<SYRK>(grp, b, tm, tn);
@@ -205,11 +213,13 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   //
   // NN Q slot: 64 K rows of the tile's BT columns, QROWB bytes each, with the
   // 32-byte blocks of a row XOR-swizzled by 2 (row % 4) (see the transpose
-  // reads).  Wave w fills rows 16 w .. 16 w + 15, QRPI rows per instruction;
-  // lane l lands at row l / QCH, chunk l % QCH.
+  // reads).  Wave w fills rows QW w .. QW w + QW - 1 (QW = 64 / NW), QRPI rows
+  // per instruction; lane l lands at row l / QCH, chunk l % QCH.
   constexpr int QROWB = NN ? BT * 2 : ROWB;
   constexpr int QCH = QROWB / 16;      // 16-byte chunks per Q slot row
   constexpr int QRPI = 1024 / QROWB;   // Q slot rows per DMA instruction
+  constexpr int QW = KS / NW;          // Q slot rows per wave (NN)
+  static_assert(!NN || QW == DPW * QRPI, "the NN Q rows of a slice take DPW instructions per wave");
   const int prow = wave * RPW + (lane >> 3);
   int pvo[2], qvo[2];
 #pragma unroll
@@ -245,8 +255,8 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
       if (op == 0) {
         lds_dma16_asm(prw, sl + (wave * RPW + 8 * j) * ROWB, pvo[j & 1], 8 * j * ldp * 2 + k0b);
       } else {
-        const uint32_t krow = (uint32_t)tc * KS + wave * 16 + j * QRPI;
-        lds_dma16_asm(qrw, sl + (wave * 16 + j * QRPI) * QROWB, qvo[j & 1], (int)(krow * (uint32_t)ldq * 2u));
+        const uint32_t krow = (uint32_t)tc * KS + wave * QW + j * QRPI;
+        lds_dma16_asm(qrw, sl + (wave * QW + j * QRPI) * QROWB, qvo[j & 1], (int)(krow * (uint32_t)ldq * 2u));
       }
     } else {
       uint8_t* const dst = slot(t, op) + (wave * RPW + 8 * j) * ROWB;
@@ -263,7 +273,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   // 2 ks + l / 32 of quarter ks.  Blocks start at multiples of 32 rows, so a
   // row's swizzle is ((l % 32) / 2) % 8.
   const int prd = (wm * WT + (lane & 31)) * ROWB;
-  const int qrd = (wn * WT + (lane & 31)) * ROWB;
+  const int qrd = (wn * WC + (lane & 31)) * ROWB;
   // NN: lane l of 16-lane group g = l / 16 supplies row 8 (g / 2) + (l % 16) / 4
   // (+ 16 ks + 4 r) and the four columns 4 (l % 4) .. + 3 of the 16-column half
   // g % 2 of a 32-column block; the transpose read then hands lane l column
@@ -271,10 +281,10 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   // Lanes 0..31 cover four rows and all eight 32-byte blocks of a 256-byte
   // span under the 2 (row % 4) swizzle: no bank is read twice.
   const int trow = (8 * (lane >> 5) + ((lane & 15) >> 2)) * QROWB;
-  int tcol[F];
+  int tcol[FN];
 #pragma unroll
-  for (int f = 0; f < F; ++f)
-    tcol[f] = ((((wn * WT + 32 * f) >> 4) + ((lane >> 4) & 1)) ^ (2 * ((lane & 15) >> 2))) * 32 + (lane & 3) * 8;
+  for (int f = 0; f < FN; ++f)
+    tcol[f] = ((((wn * WC + 32 * f) >> 4) + ((lane >> 4) & 1)) ^ (2 * ((lane & 15) >> 2))) * 32 + (lane & 3) * 8;
   auto trq = [&](int t, int ks, int f) {
     const uint8_t* base = slot(t, 1) + 16 * ks * QROWB + trow + tcol[f];
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -282,20 +292,20 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)MUON_LDS(base + 4 * QROWB));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  // Fragment u (0 .. 2F-1) of quarter ks of slice t, in the order the MFMAs
-  // first need them: a[0], q[0 .. F-1], a[1 .. F-1].
-  auto frag = [&](int t, int ks, int u, bf16x8 (&a)[F], bf16x8 (&q)[F]) {
+  // Fragment u (0 .. F+FN-1) of quarter ks of slice t, in the order the MFMAs
+  // first need them: a[0], q[0 .. FN-1], a[1 .. F-1].
+  auto frag = [&](int t, int ks, int u, bf16x8 (&a)[F], bf16x8 (&q)[FN]) {
     const int so = ((2 * ks + (lane >> 5)) ^ (((lane & 31) >> 1) & 7)) * 16;
     if (u == 0)
       a[0] = __builtin_bit_cast(bf16x8, *(const u32x4*)(slot(t, 0) + prd + so));
-    else if (u <= F) {
+    else if (u <= FN) {
       if constexpr (NN)
         q[u - 1] = trq(t, ks, u - 1);
       else
         q[u - 1] = __builtin_bit_cast(bf16x8, *(const u32x4*)(slot(t, same_pq ? 0 : 1) + qrd + (u - 1) * 32 * ROWB + so));
     }
     else
-      a[u - F] = __builtin_bit_cast(bf16x8, *(const u32x4*)(slot(t, 0) + prd + (u - F) * 32 * ROWB + so));
+      a[u - FN] = __builtin_bit_cast(bf16x8, *(const u32x4*)(slot(t, 0) + prd + (u - FN) * 32 * ROWB + so));
   };
 
   const float rsb = p.rs ? p.rs[bm] : 1.f;
@@ -328,24 +338,24 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
     }
   }
 
-  f32x16 acc[F][F];
+  f32x16 acc[F][FN];
 #pragma unroll
   for (int i = 0; i < F; ++i)
 #pragma unroll
-    for (int j = 0; j < F; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // One quarter of a slice (16 K): its F^2 MFMAs on (ac, qc), spread over 2F
-  // slots; the first F slots also read two fragments each of quarter rks of
-  // slice rt into (an, qn), and even slots issue DMA instructions
-  // j0 .. j0 + DQ - 1 of operand dop of slice dt.  Straight-line code, so the
+  // One quarter of a slice (16 K): its F x FN MFMAs on (ac, qc), MPS per
+  // slot over NSL slots; the first slots also read two fragments each (F + FN
+  // in all) of quarter rks of slice rt into (an, qn), and even slots issue DMA
+  // instructions j0 .. j0 + DQ - 1 of operand dop of slice dt.  Straight-line code, so the
   // compiler waits on exactly the fragment reads each MFMA needs, and the
   // loads never hold the MFMAs back in one burst.
-  auto diag_mfmas = [&](auto bi_c, auto h_c, const bf16x8 (&qc)[F]) {
+  auto diag_mfmas = [&](auto bi_c, auto h_c, const bf16x8 (&qc)[FN]) {
     constexpr int bi = decltype(bi_c)::value, h = decltype(h_c)::value;
 #pragma unroll
-    for (int j = 0; j < F; ++j) {
+    for (int j = 0; j < FN; ++j) {
       acc[bi][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(eh[h], qc[j], acc[bi][j], 0, 0, 0);
       acc[bi][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(el[h], qc[j], acc[bi][j], 0, 0, 0);
     }
@@ -353,19 +363,17 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   // SD >= 0: the slice multiplied is the SD-th of the tile's own rows, whose
   // K values 16 cq .. 16 cq + 15 are rows 16 (cq % 2) .. of block row
   // bi = 2 (SD % (F/2)) + cq / 2 of wave SD / (F/2); that wave adds E Q^T.
-  auto quarter = [&](auto cq_c, auto sd_c, int rt, int rks, bf16x8 (&an)[F], bf16x8 (&qn)[F],
-                     const bf16x8 (&ac)[F], const bf16x8 (&qc)[F], int dt, int dop, int j0) {
+  auto quarter = [&](auto cq_c, auto sd_c, int rt, int rks, bf16x8 (&an)[F], bf16x8 (&qn)[FN],
+                     const bf16x8 (&ac)[F], const bf16x8 (&qc)[FN], int dt, int dop, int j0) {
     constexpr int cq = decltype(cq_c)::value, SD = decltype(sd_c)::value;
 #pragma unroll
-    for (int u = 0; u < 2 * F; ++u) {
+    for (int u = 0; u < NSL; ++u) {
       if ((u & 1) == 0 && (u >> 1) < DQ && !(dop == 1 && same_pq)) dma(dt, dop, j0 + (u >> 1));
-      if (u < F) {
-        frag(rt, rks, 2 * u, an, qn);
-        frag(rt, rks, 2 * u + 1, an, qn);
-      }
+      if (2 * u < F + FN) frag(rt, rks, 2 * u, an, qn);
+      if (2 * u + 1 < F + FN) frag(rt, rks, 2 * u + 1, an, qn);
 #pragma unroll
-      for (int m = u * (F / 2); m < (u + 1) * (F / 2); ++m)
-        acc[m / F][m % F] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ac[m / F], qc[m % F], acc[m / F][m % F], 0, 0, 0);
+      for (int m = u * MPS; m < (u + 1) * MPS; ++m)
+        acc[m / FN][m % FN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ac[m / FN], qc[m % FN], acc[m / FN][m % FN], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (SD >= 0) {
@@ -391,7 +399,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   //   q1, q2 of step t:                P rows of slice t + 2
   // so at step t's barrier the loads issued after slice t + 1's are the DPW
   // of P(t + 2).
-  bf16x8 a0[F], q0[F], a1[F], q1[F];
+  bf16x8 a0[F], q0[FN], a1[F], q1[FN];
 #pragma unroll
   for (int j = 0; j < DPW; ++j) dma(0, 0, j);
 #pragma unroll
@@ -408,7 +416,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
     wait_vmcnt<DPW + DQ>();
   __builtin_amdgcn_s_barrier();
 #pragma unroll
-  for (int u = 0; u < 2 * F; ++u) frag(0, 0, u, a0, q0);
+  for (int u = 0; u < F + FN; ++u) frag(0, 0, u, a0, q0);
   __builtin_amdgcn_sched_barrier(0);
   auto step = [&](int t, auto sd_c) {
     quarter(Q0{}, sd_c, t, 1, a1, q1, a0, q0, t + 1, 1, DQ);
@@ -496,7 +504,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
   constexpr int PITCH = BT + 4;      // floats per staged row
   constexpr int HWT = WT / 2;        // rows of one wave's quadrant staged per pass
   constexpr int CPR = BT / 8;        // 8-column chunks per row
-  constexpr int RPI = 256 / CPR;     // rows per step of the row pass
+  constexpr int RPI = NTH / CPR;     // rows per step of the row pass
   constexpr int NIT = RH / RPI;      // steps of the row pass
   constexpr int R8 = RH / 8;         // 8-row chunks per pass (transposed pass)
   static_assert(RH * PITCH * 4 <= LDS_BYTES, "epilogue staging must fit");
@@ -508,11 +516,11 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
 #pragma unroll
     for (int ii = 0; ii < F / 2; ++ii)
 #pragma unroll
-      for (int j = 0; j < F; ++j)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = wm * HWT + ii * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          const int col = wn * WT + j * 32 + (lane & 31);
+          const int col = wn * WC + j * 32 + (lane & 31);
           S[row * PITCH + col] = acc[pass * (F / 2) + ii][j][r];
         }
     __syncthreads();
@@ -551,7 +559,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
     if (fast && diag) {
       // Diagonal block d (staged rows 8 d .. 8 d + 7, tile rows and columns
       // trow(8 d) ..): element (r, c) with r > c takes (c, r).
-      for (int idx = tid; idx < R8 * 64; idx += 256) {
+      for (int idx = tid; idx < R8 * 64; idx += NTH) {
         const int s0 = (idx >> 6) * 8, r = (idx >> 3) & 7, c = idx & 7;
         const int t0 = trow(s0);
         if (r > c) S[(s0 + r) * PITCH + t0 + c] = S[(s0 + c) * PITCH + t0 + r];
@@ -576,7 +584,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
       }
       if (Tg) {
 #pragma unroll 2
-        for (int idx = tid; idx < BT * R8; idx += 256) {
+        for (int idx = tid; idx < BT * R8; idx += NTH) {
           const int jj = idx % BT, i8 = (idx / BT) * 8;
           // mirrored to row jj, columns trow(i8) .. + 7: on a diagonal tile
           // only where some of them are below the diagonal
@@ -627,7 +635,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_kernel(const GemmGroup gr
       if (Tg) {
         __syncthreads();
 #pragma unroll 1
-        for (int idx = tid; idx < BT * R8; idx += 256) {
+        for (int idx = tid; idx < BT * R8; idx += NTH) {
           const int jj = idx % BT, i8 = (idx / BT) * 8;
           const int jt = j0 + jj, it8 = i0 + trow(i8);
           float v[8];
@@ -654,7 +662,8 @@ template <int BT, bool SYRK, bool NN>
 hipError_t launch_one(const GemmGroup& g, hipStream_t s) {
   const int64_t grid = g.tile_start[g.nprob];
   if (grid <= 0) return hipSuccess;
-  return launch_kernel(gemm_nt_bf16_kernel<BT, SYRK, NN>, dim3((unsigned)grid), g, s);
+  constexpr int NW = BT == 256 ? 8 : 4;
+  return launch_kernel(gemm_nt_bf16_kernel<BT, SYRK, NN, NW>, dim3((unsigned)grid), g, s, NW * 64);
 }
 
 }  // namespace
