@@ -440,8 +440,8 @@ def side_workload(args, dev):
     if compute == "f32":
         kname = "gemm_f32_kernel"
     elif args.workload == "heads" and dom == "update":
-        kname = ("updgram128_kernel: the update fused with the next iteration's Gram, iterations 1-4; "
-                 "gemm_nt_bf16_kernel<128, false, true>: the last iteration")
+        kname = ("updgram128_kernel: the update fused with the next iteration's Gram, iterations 1-4, "
+                 "and its update-only variant, the last iteration")
     else:
         kname = "gemm_nt_bf16_kernel"
     out = {
@@ -659,7 +659,7 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": f"update GEMM X' = B X + a X, all {nmat} matrices per launch (gemm_nt_bf16_kernel<256, false, true>)",
+            "kernel": f"update GEMM X' = B X + a X, all {nmat} matrices per launch (gemm_nt_bf16_kernel<256, false, true, 8>)",
             "achieved": round(upd_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
