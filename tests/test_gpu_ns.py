@@ -406,6 +406,25 @@ def test_ns_groups_more_problems_than_one_launch_holds():
     assert rel_fro(to_f64(grouped[9])[1], oracle.newton_schulz5(xin[1])) <= TOL["bf16"]
 
 
+def test_ns_groups_balanced_tile_order_bitwise():
+    # One Gram launch mixes 136 tiles with K = 16384, 136 with K = 4096 and the
+    # six of a 768-row matrix (K = 2048): the host then takes the balanced
+    # per-XCD tile order (every XCD an equal share of every problem; six tiles
+    # leave two XCDs without any).  Each matrix equals its own call (one problem
+    # per launch, round order) bit for bit, and the 768 x 2048 one matches the
+    # oracle.
+    torch = torch_cuda()
+    shapes = [(1, 4096, 16384), (1, 4096, 4096), (1, 768, 2048)]
+    xs = [to_dev(synth.gaussian(s, (34, i, 0, 1, 0), "bf16"), "bf16") for i, s in enumerate(shapes)]
+    grouped = ns.ns_groups(xs)
+    alone = [ns.ns_batched(x) for x in xs]
+    torch.cuda.synchronize()
+    for g, a in zip(grouped, alone):
+        assert torch.equal(g, a)
+    xin = storage_f64(synth.gaussian(shapes[2], (34, 2, 0, 1, 0), "bf16"), "bf16")
+    assert rel_fro(to_f64(grouped[2])[0], oracle.newton_schulz5(xin[0])) <= TOL["bf16"]
+
+
 # The Frobenius normalization is folded into the first iteration (its Gram
 # accumulates the unnormalized input in fp32, scaled by 1/(||U|| + eps)^2
 # afterwards), so parity is checked across input scales: 1e-12 and 1e-9 (the
