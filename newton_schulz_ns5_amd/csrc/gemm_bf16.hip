@@ -18,11 +18,11 @@
 // waits on a load, a fragment read or the barrier), each owning a 128 x 64
 // sub-tile; at BT = 128 four (2 x 2, two workgroups per CU), each owning
 // 64 x 64.  Sub-tiles are 32x32 blocks computed with
-// v_mfma_f32_32x32x16_bf16 (fp32 accumulation).  K advances 64 at a time: each operand row contributes one 128-byte
-// line per slice, brought by direct HBM -> LDS buffer loads
-// (buffer_load_dwordx4 ... lds) into a ring of five operand slots (160 KiB
-// for BT = 256), about one and a half slices ahead of the multiply.  One
-// barrier per slice.  The loads, the LDS fragment reads and the MFMAs are
+// v_mfma_f32_32x32x16_bf16 (fp32 accumulation).  K advances 64 at a time:
+// each operand row contributes one 128-byte line per slice, brought by direct
+// HBM -> LDS buffer loads (buffer_load_dwordx4 ... lds) into a ring of five
+// operand slots (160 KiB for BT = 256), about one and a half slices ahead of
+// the multiply.  One barrier per slice.  The loads, the LDS fragment reads and the MFMAs are
 // interleaved in fixed slots, so no burst of loads holds the MFMAs back.
 //
 // Every output tile is computed by the same instruction sequence whatever the
