@@ -421,9 +421,9 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
           Poly128Params q{};
           q.part = (const float*)(ws + J.L.part); q.ksplit = ks;
           q.rs = p.rs;
-          if (first) {  // the norm is finalized here (path128: no norm launch)
+          if (first) {  // the norm is finalized here from the first Gram's chunk sums of squares
             q.rs = nullptr;
-            q.nsum = (const float*)(ws + J.L.partial); q.ntiles = J.L.tiles;
+            q.nsum = (const float*)(ws + J.L.partial); q.ntiles = ks;
             q.eps = cfg.eps; q.rs_out = (float*)(ws + J.L.rs);
           }
           q.b = cf.b; q.c = cf.c;
@@ -446,10 +446,13 @@ hipError_t ns_iterations_bf16(const std::vector<NsJob>& jobs, const muon_ns_conf
         }
         if (path128(g) && first) {
           // The first Gram of a 128-row matrix: chunk products straight from
-          // X by the Gram-only variant of the fused kernel (same chunks).
+          // X by the Gram-only variant of the fused kernel (same chunks), with
+          // each chunk's sum of squares (the norm's partials: no load-kernel
+          // partials and no norm launch on this path).
           UpdGram128Params u{};
           u.X = Xin; u.x_bs = sxin;
           u.part = (float*)(ws + J.L.part);
+          u.nsq = (float*)(ws + J.L.partial);
           u.np = (int)g.np; u.ksplit = ks;
           gram128.push_back({u, (int)J.nb, p.flop, B * (m * n * 2 + ks * m * m * 4)});
         } else if (!prev_fused) {
@@ -804,7 +807,10 @@ hipError_t ns_run_passes(const muon_ns_problem* q, int64_t nq, const muon_ns_con
                           p.x_row_stride == p.cols && (p.x_batch_stride % 8) == 0 && ((uintptr_t)p.x & 15) == 0 &&
                           p.y != p.x;
       pp.no_x = direct ? 1 : 0;
-      st.preps.push_back({pp, (int)nb, (double)nb * p.rows * p.cols * (xe + (direct ? 0 : (v.g.bf ? 2 : 4)))});
+      // A 128-row matrix's norm comes from its first Gram (the fused kernel's
+      // chunk sums of squares), so an input read in place needs no load launch.
+      if (!(direct && path128(v.g)))
+        st.preps.push_back({pp, (int)nb, (double)nb * p.rows * p.cols * (xe + (direct ? 0 : (v.g.bf ? 2 : 4)))});
       if (!path128(v.g)) st.norms.push_back({norm_params(v.L, cfg.eps, v.ws), (int)nb});
       FinalOut out{(char*)p.y + c0 * p.y_batch_stride * ye, p.y_dtype, p.y_row_stride, p.y_batch_stride};
       NsJob job{v.g, nb, v.ws, v.L, out};

@@ -183,6 +183,7 @@ struct UpdGram128Params {
   const void* X; int64_t x_bs;       // [128][np] bf16, row stride np
   void* Y; int64_t y_bs;             // [128][np] bf16, row stride np
   float* part;                       // [nb * ksplit][128][128] fp32, or null
+  float* nsq;                        // Gram only: [nb][ksplit] sums of squares of X's chunks, or null
   int32_t np, ksplit;                // np a multiple of 128; 1 <= ksplit <= np / 128
   float alpha, beta;
   const float* rs; int32_t alpha_pow, beta_pow;
@@ -197,7 +198,8 @@ struct UpdGram128Group {
 };
 hipError_t launch_updgram128(const UpdGram128Group& g, hipStream_t s);
 // The chunk products of X X^T alone (the first iteration's Gram), chunked as
-// above; only X, x_bs, part, np and ksplit are used.
+// above, and (nsq) each chunk's sum of squares; only X, x_bs, part, nsq, np
+// and ksplit are used.
 hipError_t launch_gram128(const UpdGram128Group& g, hipStream_t s);
 hipError_t launch_rowstat(const RowStatParams& p, int nb, hipStream_t s);
 hipError_t launch_rho(const RhoParams& p, int nb, hipStream_t s);

@@ -26,7 +26,8 @@
 //      accumulators, as chunk c of the split-K product the next iteration's
 //      sum-and-polynomial kernel reads.
 // The same kernel without steps 2-3 computes the first iteration's chunk
-// products from X itself, and without step 4 an update alone.
+// products from X itself (and, when asked, the chunk's sum of squares, the
+// norm's partial), and without step 4 an update alone.
 // Eight waves (two per SIMD) share each sub-tile's products, so one wave's
 // MFMAs run while the other waits on LDS.  Waves 0-3 issue every HBM -> LDS
 // load and waves 4-7 every X' store, so no wave waits on a count that
@@ -223,6 +224,10 @@ __global__ __launch_bounds__(512, 1) void updgram128_kernel(const UpdGram128Grou
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r) accg[j][r] = 0.f;
+  // Gram only, with nsq: this thread's share of the chunk's sum of squares,
+  // the 16-byte pieces tid + 512 i (i = 0..3) of every sub-tile, added in
+  // sub-tile, piece and element order.
+  float sq = 0.f;
 
   // Pipeline.  Waves 0-3 issue only loads, in this order: B (8, update
   // modes), X_0 (8), X_1 (8 when nsub > 1), then per sub-tile jj X_{jj+2} (8
@@ -297,6 +302,21 @@ __global__ __launch_bounds__(512, 1) void updgram128_kernel(const UpdGram128Grou
                                                  __builtin_amdgcn_readfirstlane(16 * u * ldx * 2 + jj * SUB * 2), 0);
       }
     }
+    if constexpr (!UPD) {
+      if (p.nsq) {
+        typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4 w = *(const lds_u32x4*)(uintptr_t)(xb + (uint32_t)(16 * tid + 8192 * i));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float lo = __uint_as_float(w[e] << 16), hi = __uint_as_float(w[e] & 0xffff0000u);
+            sq += lo * lo;
+            sq += hi * hi;
+          }
+        }
+      }
+    }
     // Gram block j of wave (wa, wb): rows 32 wa .., columns 64 wb + 32 j ...
     if constexpr (GRAM) {
 #pragma unroll
@@ -311,6 +331,20 @@ __global__ __launch_bounds__(512, 1) void updgram128_kernel(const UpdGram128Grou
     }
   }
   if constexpr (!GRAM) return;
+  if constexpr (!UPD) {
+    if (p.nsq) {
+      // Wave sums into the (unused) X' area, then added in wave order.
+      typedef __attribute__((address_space(3))) float lds_f32;
+      sq = wave_sum(sq);
+      if (lane == 0) *(lds_f32*)(uintptr_t)(Ys + 4 * wave) = sq;
+      __syncthreads();
+      if (tid == 0) {
+        float t = 0.f;
+        for (int w = 0; w < 8; ++w) t += *(const lds_f32*)(uintptr_t)(Ys + 4 * w);
+        p.nsq[(int64_t)b * ks + ch] = t;
+      }
+    }
+  }
 
   // The chunk's Gram product from the accumulators: register 4 q + e of
   // block j holds G(R + e, C) with R = 32 wa + 8 q + 4 (l / 32) and C = 64 wb
