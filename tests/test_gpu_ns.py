@@ -429,10 +429,12 @@ def test_ns_groups_balanced_tile_order_bitwise():
 # accumulates the unnormalized input in fp32, scaled by 1/(||U|| + eps)^2
 # afterwards), so parity is checked across input scales: 1e-12 and 1e-9 (the
 # norm below and near eps), 1e12 and 1e16 (||U||_F ~ 4e18, just inside the
-# documented fp32 limit of 1.8e19).
+# documented fp32 limit of 1.8e19).  The 128-row shapes take the split-Gram
+# path whose norm comes from the first Gram's chunk sums of squares (the wide
+# one read in place, the tall one through the transposing load).
 @pytest.mark.parametrize("scale", [1e-12, 1e-9, 1e12, 1e16])
 @pytest.mark.parametrize("compute", ["bf16", "f32"])
-@pytest.mark.parametrize("shape", [(2, 300, 520), (1, 520, 300)])
+@pytest.mark.parametrize("shape", [(2, 300, 520), (1, 520, 300), (2, 128, 2048), (2, 2048, 128)])
 def test_input_scale_parity(scale, compute, shape):
     torch = torch_cuda()
     x = synth.gaussian(shape, (41, 0, 0, 1, 0), compute, std=scale)
@@ -444,11 +446,13 @@ def test_input_scale_parity(scale, compute, shape):
     assert max(errs) <= TOL[compute], (scale, errs)
 
 
-def test_input_beyond_fp32_norm_range_gives_nan():
+@pytest.mark.parametrize("shape", [(1, 256, 384), (1, 128, 2048)])
+def test_input_beyond_fp32_norm_range_gives_nan(shape):
     # ||U||_F above 1.8e19 overflows the fp32 sum of squares: the documented
-    # result is NaN, never a silently zero matrix.
+    # result is NaN, never a silently zero matrix (also where the norm comes
+    # from the first Gram's chunk sums of squares, the 128-row shape).
     torch = torch_cuda()
-    x = synth.gaussian((1, 256, 384), (41, 0, 1, 1, 0), "bf16", std=1e20)
+    x = synth.gaussian(shape, (41, 0, 1, 1, 0), "bf16", std=1e20)
     out = ns.ns_batched(to_dev(x, "bf16"))
     torch.cuda.synchronize()
     assert torch.isnan(out.float()).all()
