@@ -71,6 +71,51 @@ static_assert(LDS_BYTES <= 160 * 1024, "LDS of one workgroup");
 // iteration's Gram; B, Y, alpha and beta are unused).
 enum { kUpdGram = 0, kUpdOnly = 1, kGramOnly = 2 };
 
+// Workgroup -> (problem, matrix, chunk).  Workgroup w runs on XCD w % 8 as the
+// (w / 8)-th of that XCD's queue.  The launch's matrices are numbered problem
+// after problem, and matrix g is given to XCD g % 8 with all its chunks: the
+// chunk products a workgroup writes are read by the next launch's workgroups
+// of the same matrix on the same XCD, from its L2.  XCD x's queue holds its
+// matrices in order, each as its chunks in order; the grid is 8 times the
+// longest queue, and the workgroups past the end of a shorter queue return
+// at once (xcd_slot false).
+__device__ __forceinline__ bool xcd_slot(const UpdGram128Group& g, int& pi, int& b, int& ch) {
+  const int x = (int)blockIdx.x & 7;
+  int k = (int)blockIdx.x >> 3;
+  auto share = [x](int n) { return (n + 7 - x) >> 3; };  // g < n with g % 8 == x
+  int g0 = 0;
+  for (pi = 0; pi < g.nprob; ++pi) {
+    const int ks = g.prob[pi].ksplit;
+    const int nb = (g.start[pi + 1] - g.start[pi]) / ks;
+    const int cnt = share(g0 + nb) - share(g0);  // this problem's matrices on XCD x
+    if (k < cnt * ks) {
+      const int j = k / ks;
+      ch = k - j * ks;
+      b = ((x - g0) & 7) + 8 * j;  // the j-th matrix g >= g0 with g % 8 == x, minus g0
+      return true;
+    }
+    k -= cnt * ks;
+    g0 += nb;
+  }
+  return false;
+}
+
+// Grid of a launch: 8 x the longest XCD queue.
+int xcd_grid(const UpdGram128Group& g) {
+  int longest = 0;
+  for (int x = 0; x < 8; ++x) {
+    int q = 0, g0 = 0;
+    for (int i = 0; i < g.nprob; ++i) {
+      const int ks = g.prob[i].ksplit;
+      const int nb = (g.start[i + 1] - g.start[i]) / ks;
+      q += (((g0 + nb + 7 - x) >> 3) - ((g0 + 7 - x) >> 3)) * ks;
+      g0 += nb;
+    }
+    longest = q > longest ? q : longest;
+  }
+  return 8 * longest;
+}
+
 template <int MODE>
 __global__ __launch_bounds__(512, 1) void updgram128_kernel(const UpdGram128Group grp) {
   constexpr bool UPD = MODE != kGramOnly, GRAM = MODE != kUpdOnly;
@@ -79,12 +124,10 @@ __global__ __launch_bounds__(512, 1) void updgram128_kernel(const UpdGram128Grou
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7, two per SIMD
   const int wa = wave >> 1, wb = wave & 1;                     // wa 0..3: a 32-wide block row
 
-  int pi = 0;
-  while (pi + 1 < grp.nprob && (int)blockIdx.x >= grp.start[pi + 1]) ++pi;
+  int pi, b, ch;
+  if (!xcd_slot(grp, pi, b, ch)) return;  // a padding workgroup: no work
   const UpdGram128Params& p = grp.prob[pi];
-  const int local = (int)blockIdx.x - grp.start[pi];
   const int ks = p.ksplit;
-  const int b = local / ks, ch = local - b * ks;
   const int kb = p.np / SUB;
   const int j0 = (int)((int64_t)ch * kb / ks);
   const int nsub = (int)((int64_t)(ch + 1) * kb / ks) - j0;
@@ -390,8 +433,8 @@ hipError_t launch_updgram128(const UpdGram128Group& g, hipStream_t s) {
     if (p.np <= 0 || p.np % SUB != 0 || p.ksplit < 1 || p.ksplit > p.np / SUB) return hipErrorInvalidValue;
     if (g.start[i + 1] < g.start[i] || (g.start[i + 1] - g.start[i]) % p.ksplit != 0) return hipErrorInvalidValue;
   }
-  const int grid = g.start[g.nprob];
-  if (grid <= 0) return hipSuccess;
+  if (g.start[g.nprob] <= 0) return hipSuccess;
+  const int grid = xcd_grid(g);
   // One variant per launch: the Gram products are computed for every problem
   // or for none.
   const bool gram = g.prob[0].part != nullptr;
@@ -409,9 +452,8 @@ hipError_t launch_gram128(const UpdGram128Group& g, hipStream_t s) {
       return hipErrorInvalidValue;
     if (g.start[i + 1] < g.start[i] || (g.start[i + 1] - g.start[i]) % p.ksplit != 0) return hipErrorInvalidValue;
   }
-  const int grid = g.start[g.nprob];
-  if (grid <= 0) return hipSuccess;
-  return launch_kernel(updgram128_kernel<kGramOnly>, dim3(grid), g, s, 512);
+  if (g.start[g.nprob] <= 0) return hipSuccess;
+  return launch_kernel(updgram128_kernel<kGramOnly>, dim3(xcd_grid(g)), g, s, 512);
 }
 
 }  // namespace muon
