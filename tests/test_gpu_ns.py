@@ -241,8 +241,10 @@ CUBIC = (1.5, -0.5, 0.0)
 
 
 @pytest.mark.parametrize("compute", ["bf16", "f32"])
-@pytest.mark.parametrize("shape", [(2, 300, 520), (1, 256, 256), (1, 640, 384)])
+@pytest.mark.parametrize("shape", [(2, 300, 520), (1, 256, 256), (1, 640, 384), (1, 768, 1024)])
 def test_cubic_coefficients_parity(shape, compute):
+    # (1, 768, 1024) has 256-edge tiles (eight waves): its polynomial takes the
+    # explicit D through the generic epilogue.
     torch = torch_cuda()
     dt = "bf16" if compute == "bf16" else "f32"
     x = synth.gaussian(shape, (23, shape[1], shape[2], 1, 0), dt)
@@ -262,6 +264,22 @@ def test_schedule_mixing_zero_and_nonzero_c():
     torch.cuda.synchronize()
     got, xin = to_f64(out), storage_f64(x, "bf16")
     err = max(rel_fro(got[i], oracle.newton_schulz5(xin[i], steps=5, coeffs=sched)) for i in range(2))
+    assert err <= TOL["bf16"], err
+
+
+# ---- ragged 256-edge tiles ------------------------------------------------------
+@pytest.mark.parametrize("shape", [(1, 1000, 3000), (1, 3000, 1000), (2, 1000, 1000)])
+def test_ragged_256_edge_tiles_parity(shape):
+    # Padded to 1024 x 3072 (1024 x 1024): every product has 256-edge tiles
+    # (eight waves), and the last update's tiles along the real edges are
+    # ragged (the generic epilogue with element stores; the tall shape writes
+    # its transposed output there, the square one is stored as is).
+    torch = torch_cuda()
+    x = synth.gaussian(shape, (35, shape[1], shape[2], 1, 0), "bf16")
+    out = ns.ns_batched(to_dev(x, "bf16"))
+    torch.cuda.synchronize()
+    got, xin = to_f64(out), storage_f64(x, "bf16")
+    err = max(rel_fro(got[i], oracle.newton_schulz5(xin[i])) for i in range(shape[0]))
     assert err <= TOL["bf16"], err
 
 
