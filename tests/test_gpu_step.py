@@ -123,6 +123,15 @@ def test_per_head_step():
     run_steps((256, 384), 2, "bf16", "bf16", "bf16", steps=2, heads=4)
 
 
+def test_per_head_split_gram_step():
+    # Heads of 128 x 2048 (a 512 x 2048 parameter, heads=4): the 128-row path
+    # with a split Gram, where the norm of the momentum update comes from the
+    # first Gram's chunk sums of squares of its bf16 rounding, the fused
+    # update / Gram kernel and its update-only last iteration; NorMuon and the
+    # bf16 model copy on the whole parameter.
+    run_steps((512, 2048), 2, "bf16", "bf16", "bf16", steps=2, heads=4, normuon=True, model_copy=True)
+
+
 @pytest.mark.parametrize("normuon", [False, True])
 def test_split_qkv_step(normuon):
     # A fused [q; k; v] weight of 384 x 256 split into 256 + 64 + 64 rows (the
