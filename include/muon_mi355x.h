@@ -57,7 +57,9 @@
  *    matrices share the call and of its position in the batch.
  *  - Input range: the Frobenius normalization is folded into the first
  *    iteration, whose products accumulate the unnormalized input in fp32, and
- *    ||U||_F^2 is summed in fp32.  Any input with ||U||_F below 1.8e19 (its
+ *    ||U||_F^2 is summed in fp32 (for a matrix whose short side pads to 128
+ *    and whose Gram is split over column chunks, from U as rounded to bf16,
+ *    by the first Gram).  Any input with ||U||_F below 1.8e19 (its
  *    square within the fp32 range) is supported, down to the smallest normal
  *    values; above it the output is NaN (never a silent zero).  Entries so
  *    small that their squares fall below the fp32 normal range leave
