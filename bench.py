@@ -140,8 +140,9 @@ def step_stats(ms):
 
 
 def cpu_baseline(grads, weights, target_seconds=20.0):
-    """The oracle as it stands, on q, k and v of the layer (3 of 7 matrices),
-    scaled by dense float64 NS FLOPs to the whole layer."""
+    """The oracle as it stands, on the layer's matrices smallest first until about
+    target_seconds of CPU work (k, v, q, o, down, gate, ...), scaled by dense
+    float64 NS FLOPs to the whole layer."""
     import oracle
     import synth
     host = host_info()
@@ -151,7 +152,7 @@ def cpu_baseline(grads, weights, target_seconds=20.0):
         m, n = min(rows, cols), max(rows, cols)
         return 5 * (4 * m * m * n + 2 * m ** 3)
 
-    sample = ["k", "v", "q"]
+    sample = ["k", "v", "q", "o", "down", "gate", "up"]
     t0 = time.perf_counter()
     done = []
     for name in sample:
